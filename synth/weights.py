@@ -1,0 +1,136 @@
+"""Seeded synthetic weights and inputs.
+
+Random-init weights stand in for trained ones (the pages ship none): every matrix
+and embedding is drawn N(0, init_std); RMSNorm gains are 1; the router matrix is
+drawn N(0, d_model^-1/2) so that router logits have unit variance.  Each tensor
+has its own generator, seeded from (run seed, tensor name), so any tensor can be
+regenerated alone.  Values are drawn in fp32 and stored in the model's precision:
+fp32, bf16 (round-to-nearest-even, by torch's conversion), or for fp8 models
+OCP E4M3FN codes with one fp32 scale per output channel, scale = amax / 448.
+
+This module is plumbing shared by the oracle's tests and the HIP path's callers:
+it holds no step of the denoising method.  A tensor generated on one device and
+the same tensor generated on another are NOT the same draw; callers that compare
+the two paths generate once and copy.
+"""
+from __future__ import annotations
+
+import hashlib
+from typing import Dict, List
+
+import torch
+
+from .configs import ModelConfig, RunConfig
+
+E4M3_MAX = 448.0
+
+
+def tensor_seed(seed: int, name: str) -> int:
+    h = hashlib.blake2b(f"{seed}/{name}".encode(), digest_size=8).digest()
+    return int.from_bytes(h, "little") & 0x7FFF_FFFF_FFFF_FFFF
+
+
+def _gen(seed: int, name: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(tensor_seed(seed, name))
+    return g
+
+
+def normal(seed: int, name: str, shape, std: float, device="cpu") -> torch.Tensor:
+    g = _gen(seed, name, device)
+    x = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    return x.mul_(std)
+
+
+def quantize_e4m3_rows(w: torch.Tensor):
+    """Per-output-channel (last-dim rows) E4M3FN quantisation of fp32 weights.
+
+    Returns (codes uint8 with the same shape, scales fp32 of shape w.shape[:-1]).
+    scale = amax/448 (1 when a row is all zero); code = e4m3(w/scale), round to
+    nearest even, saturating at +-448.
+    """
+    amax = w.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = (w / s.unsqueeze(-1)).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), s.contiguous()
+
+
+def _store(out: Dict[str, torch.Tensor], name: str, w: torch.Tensor, dtype: str,
+           projection: bool):
+    if dtype == "f32":
+        out[name] = w.contiguous()
+    elif dtype == "bf16" or not projection:
+        out[name] = w.to(torch.bfloat16).contiguous()
+    elif dtype == "fp8":
+        q, s = quantize_e4m3_rows(w)
+        out[name + ".q"] = q.contiguous()
+        out[name + ".s"] = s
+    else:
+        raise ValueError(dtype)
+
+
+def projection_names(cfg: ModelConfig) -> List[str]:
+    names = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]
+    if cfg.ffn == "moe":
+        names += ["we_gate", "we_up", "we_down"]
+    return names
+
+
+def make_weights(cfg: ModelConfig, seed: int = 0, device="cpu",
+                 layers=None) -> Dict[str, torch.Tensor]:
+    """All weights of `cfg`, keyed '<name>' or '<layer>.<name>'.
+
+    `layers` restricts generation to a subset of layer indices (the others are
+    simply absent), for tests that check one layer at full size.
+    """
+    d, std = cfg.d_model, cfg.init_std
+    out: Dict[str, torch.Tensor] = {}
+    emb = normal(seed, "embed", (cfg.vocab, d), std, device)
+    out["embed"] = emb.contiguous() if cfg.dtype == "f32" else emb.to(torch.bfloat16).contiguous()
+    del emb
+    out["final_norm"] = torch.ones(d, dtype=torch.float32, device=device)
+    _store(out, "lm_head", normal(seed, "lm_head", (cfg.vocab, d), std, device),
+           cfg.dtype, projection=True)
+    for l in (range(cfg.n_layers) if layers is None else layers):
+        p = f"{l}."
+        out[p + "attn_norm"] = torch.ones(d, dtype=torch.float32, device=device)
+        out[p + "ffn_norm"] = torch.ones(d, dtype=torch.float32, device=device)
+        shapes = {
+            "wq": (cfg.q_dim, d), "wk": (cfg.kv_dim, d), "wv": (cfg.kv_dim, d),
+            "wo": (d, cfg.q_dim),
+            "w_gate": (cfg.d_ffn, d), "w_up": (cfg.d_ffn, d), "w_down": (d, cfg.d_ffn),
+        }
+        if cfg.ffn == "moe":
+            E, de = cfg.n_experts, cfg.d_expert
+            shapes.update({"we_gate": (E, de, d), "we_up": (E, de, d), "we_down": (E, d, de)})
+        for name, shape in shapes.items():
+            _store(out, p + name, normal(seed, p + name, shape, std, device), cfg.dtype,
+                   projection=True)
+        if cfg.ffn == "moe":
+            wr = normal(seed, p + "w_router", (cfg.n_experts, d), cfg.router_sigma, device)
+            out[p + "w_router"] = wr.contiguous() if cfg.dtype == "f32" else wr.to(torch.bfloat16).contiguous()
+    return out
+
+
+def prefix_lengths(run: RunConfig) -> List[int]:
+    lo, hi = run.prefix_len
+    if lo == hi:
+        return [lo] * run.n_requests
+    g = _gen(run.seed, "prefix_lengths", "cpu")
+    return torch.randint(lo, hi + 1, (run.n_requests,), generator=g).tolist()
+
+
+def prefix_ids(run: RunConfig, request: int, length: int, device="cpu") -> torch.Tensor:
+    """Uniform ids in [0, V-2]: a prompt never holds the [MASK] id (V-1)."""
+    g = _gen(run.seed, f"prefix_ids/{request}", device)
+    hi = run.model.vocab - 1   # exclusive bound -> ids 0..V-2
+    return torch.randint(0, hi, (length,), generator=g, device=device, dtype=torch.int64).to(torch.int32)
+
+
+def make_inputs(run: RunConfig, device="cpu") -> List[torch.Tensor]:
+    return [prefix_ids(run, r, n, device) for r, n in enumerate(prefix_lengths(run))]
+
+
+def to_float64_numpy(t: torch.Tensor):
+    """Exact float64 copy of a stored fp32 or bf16 tensor."""
+    return t.detach().to("cpu", torch.float64).numpy()
