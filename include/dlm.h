@@ -1,0 +1,262 @@
+/*
+ * dlm.h -- C ABI of the block-diffusion denoising library (libdlm.so, gfx950).
+ *
+ * The library runs the hot path of a block-diffusion language model:
+ *
+ *   1. dlm_prefill        causal forward over a prompt; writes every layer's
+ *                         post-RoPE K and V into the request's KV cache.
+ *   2. dlm_denoise_step   one bidirectional forward over the canvas (all
+ *                         canvas positions see each other and the whole
+ *                         cached prefix), the LM head, and per position the
+ *                         greedy prediction and its confidence.
+ *   3. dlm_commit         turns the most confident still-masked positions into
+ *                         their predicted tokens.
+ *   4. dlm_append_canvas  forward over the finished canvas with the denoising
+ *                         mask; its K/V become part of the cache (T += C).
+ *
+ * Where these come from ("What changes" = rahulsharmavishwakarma.github.io,
+ * "Diffusion LLMs: what changes when you stop generating one token at a time"):
+ *   - reverse process: start all-[MASK], predict masked positions, commit the
+ *     most confident ones, repeat until nothing is masked (What changes, sec. 2);
+ *   - bidirectional attention inside the block and several commits per pass
+ *     (What changes, sec. 2, properties 1 and 2);
+ *   - autoregressive across blocks, diffusion within a block, with KV caching
+ *     (What changes, sec. 4.1);
+ *   - a 256-token canvas, causal prefill, bidirectional denoising, finished
+ *     canvases appended to the KV cache, up to 48 steps (What changes,
+ *     sec. 4.2 "Block decoding" and "Few steps");
+ *   - committing only positions above a confidence threshold (What changes,
+ *     sec. 5, "Quality vs steps").
+ * The pages give no layer internals; the model is a pre-RMSNorm transformer
+ * with rotary embeddings, grouped-query attention, a SwiGLU FFN (dense, or a
+ * softmax-top-k mixture of SwiGLU experts plus an ungated shared expert) and an
+ * untied LM head.  [MASK] is excluded from the prediction; confidence is the
+ * maximum softmax probability over the remaining vocabulary; ties in the
+ * prediction go to the lower token id and ties in confidence rank to the lower
+ * position.
+ *
+ * Conventions for every entry point:
+ *   - Memory: the caller allocates and frees all device memory (weights, KV
+ *     caches, canvases, outputs, workspace).  Pointers marked "device" must be
+ *     device memory of the current HIP device; "host" pointers are read before
+ *     the call returns.  The library never frees caller memory.  It owns only
+ *     its host handle and one 4-byte device error word per model.
+ *   - Streams: all GPU work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No entry point synchronises except dlm_check_device_status
+ *     and dlm_timing_read.  One model handle serves one stream at a time.
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     on failure the call returns a negative dlm_status, enqueues nothing and
+ *     changes no state, and dlm_last_error() describes the failure.  Faults only
+ *     the device can see (a token id outside the vocabulary, a masked position
+ *     in a canvas being appended) set the model's device error word, which
+ *     dlm_check_device_status reports.  Nothing throws across the ABI.
+ *   - No entry point allocates device memory after dlm_create, and none issues
+ *     hipMemset, so a caller may capture dlm_denoise_step / dlm_commit into a
+ *     HIP graph.
+ *   - Host state: dlm_prefill and dlm_append_canvas advance dlm_seq.T on the
+ *     host when they return DLM_OK.
+ */
+#ifndef DLM_H
+#define DLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dlm_status;
+#define DLM_OK            0
+#define DLM_E_ARG        -1   /* null pointer, bad enum, bad count */
+#define DLM_E_SHAPE      -2   /* dimensions the kernels cannot take */
+#define DLM_E_DTYPE      -3   /* dtype / weight set mismatch */
+#define DLM_E_CAPACITY   -4   /* KV cache too small for the call */
+#define DLM_E_STATE      -5   /* call not valid in the current state */
+#define DLM_E_WORKSPACE  -6   /* workspace null or smaller than dlm_workspace_bytes */
+#define DLM_E_HIP        -7   /* a HIP runtime call failed */
+#define DLM_E_DEVICE     -8   /* the device error word is set */
+#define DLM_E_UNSUPPORTED -9  /* valid request this build does not implement */
+
+/* Bits of the device error word. */
+#define DLM_DEVERR_TOKEN_RANGE   1   /* an input id was < 0 or >= vocab */
+#define DLM_DEVERR_MASK_APPEND   2   /* dlm_append_canvas saw a [MASK] */
+
+#define DLM_MAX_SEQS 64              /* requests per denoise/commit/append call */
+
+typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_FP8 = 2 } dlm_dtype;
+typedef enum { DLM_FFN_DENSE = 0, DLM_FFN_MOE = 1 } dlm_ffn_kind;
+
+/* Model shape.  Constraints checked by dlm_create: head_dim in {32, 64, 128};
+ * n_q_heads a multiple of n_kv_heads; d_model, d_ffn, d_expert multiples of 32
+ * (f32) / 64 (bf16) / 128 (fp8) elements; top_k <= n_experts <= 256,
+ * top_k <= 16; 0 <= mask_id < vocab; canvas in [1, 1024]. */
+typedef struct {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t vocab;
+    int32_t mask_id;
+    int32_t ffn;        /* dlm_ffn_kind */
+    int32_t d_ffn;      /* dense FFN inner dim; for MoE the shared expert's inner dim */
+    int32_t n_experts;  /* MoE only */
+    int32_t top_k;      /* MoE only */
+    int32_t d_expert;   /* MoE only: inner dim of each expert */
+    int32_t dtype;      /* dlm_dtype: storage of weights and GEMM operands */
+    int32_t canvas;     /* C: tokens per canvas */
+    float   rms_eps;
+    float   rope_base;
+} dlm_config;
+
+/* Per-layer weights, all device pointers, row-major [out, in] (a GEMM computes
+ * y = x W^T).  Element type: fp32 for DLM_F32, bf16 for DLM_BF16, OCP E4M3FN
+ * codes (uint8) for DLM_FP8 projections.  "_s" pointers are the fp8 per-output-
+ * channel fp32 scales (W = code * s[out]); NULL for other dtypes.
+ *   wqkv   [(Hq + 2 Hkv) * dh, d]  rows: Q heads, then K heads, then V heads
+ *   wo     [d, Hq * dh]
+ *   w_gate, w_up [F, d]; w_down [d, F]     F = d_ffn (dense FFN or shared expert)
+ *   w_router [E, d]        bf16 (fp32 for DLM_F32) -- also for DLM_FP8 models
+ *   we_gate, we_up [E, De, d]; we_down [E, d, De]
+ *   attn_norm, ffn_norm [d] fp32 RMSNorm gains.                                  */
+typedef struct {
+    const float* attn_norm;
+    const float* ffn_norm;
+    const void*  wqkv;    const float* wqkv_s;
+    const void*  wo;      const float* wo_s;
+    const void*  w_gate;  const float* w_gate_s;
+    const void*  w_up;    const float* w_up_s;
+    const void*  w_down;  const float* w_down_s;
+    const void*  w_router;
+    const void*  we_gate; const float* we_gate_s;
+    const void*  we_up;   const float* we_up_s;
+    const void*  we_down; const float* we_down_s;
+} dlm_layer_weights;
+
+/* embed [V, d]: fp32 (DLM_F32) or bf16.  lm_head [V, d] untied, projection
+ * dtype.  final_norm [d] fp32.  layers: HOST array of n_layers entries, copied
+ * by dlm_create (the device tensors it points to must outlive the model). */
+typedef struct {
+    const void*  embed;
+    const float* final_norm;
+    const void*  lm_head;  const float* lm_head_s;
+    const dlm_layer_weights* layers;
+} dlm_weights;
+
+/* One request.  Host struct of non-owning device pointers.
+ *   kv: KV cache, [n_layers][2 (K, V)][n_kv_heads][capacity][head_dim],
+ *       bf16 (fp32 for DLM_F32 models); slot t holds the post-RoPE key and the
+ *       value of absolute position t.
+ *   capacity: tokens the cache holds.
+ *   T: tokens cached so far (prefix plus appended canvases).
+ *   canvas: device int32[C], the block being denoised ([MASK] = mask_id).
+ *   page_table / page_size: reserved for a paged cache; must be NULL / 0. */
+typedef struct {
+    void*          kv;
+    int32_t        capacity;
+    int32_t        T;
+    int32_t*       canvas;
+    const int32_t* page_table;
+    int32_t        page_size;
+} dlm_seq;
+
+/* Commit rule (What changes, sec. 2 and sec. 5).
+ *   DLM_COMMIT_TOPK: at step s commit the k_per_step[s] most confident masked
+ *     positions (all of them if fewer remain).
+ *   DLM_COMMIT_THRESHOLD: commit every masked position with confidence >=
+ *     threshold; if there is none, the single most confident one; at step
+ *     n_steps - 1, every masked position.
+ * k_per_step: HOST array of n_steps entries (TOPK only). */
+typedef enum { DLM_COMMIT_TOPK = 0, DLM_COMMIT_THRESHOLD = 1 } dlm_commit_kind;
+typedef struct {
+    int32_t        kind;
+    int32_t        n_steps;
+    const int32_t* k_per_step;
+    float          threshold;
+} dlm_commit_rule;
+
+typedef struct dlm_model dlm_model;
+
+/* Creates a model handle over caller-owned device weights on the current HIP
+ * device.  Validates the config and that every pointer the config needs is
+ * non-NULL.  Allocates the 4-byte device error word (zeroed).  */
+dlm_status dlm_create(const dlm_config* cfg, const dlm_weights* weights, dlm_model** out);
+
+/* Frees the handle and its error word.  NULL is a no-op. */
+void dlm_destroy(dlm_model* model);
+
+/* Bytes of device workspace a call needs when it processes up to `max_rows`
+ * token rows in one forward (R * C for denoise/append, n for prefill) and
+ * attends to up to `max_kv_tokens` keys per request.  0 on invalid input. */
+size_t dlm_workspace_bytes(const dlm_model* model, int32_t max_rows, int32_t max_kv_tokens);
+
+/* Causal forward over ids (device int32[n]) at positions [T, T + n) of `seq`;
+ * K/V of every layer are written to cache slots [T, T + n); then seq->T += n.
+ * No LM head.  E_CAPACITY if T + n > capacity. */
+dlm_status dlm_prefill(dlm_model* model, dlm_seq* seq, const int32_t* ids, int32_t n,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* One denoising pass over the canvases of n_seqs requests.  Request r's canvas
+ * sits at positions [T_r, T_r + C); its queries attend to cache slots [0, T_r)
+ * and to all C canvas keys (no mask inside the canvas).  The canvas K/V are
+ * written to slots [T_r, T_r + C) as scratch; T does not change.
+ *   conf [n_seqs, C] fp32 (device, out): max softmax probability over the
+ *        vocabulary without [MASK];
+ *   pred [n_seqs, C] int32 (device, out): lowest-id argmax over the same set;
+ *   logits [n_seqs, C, V] fp32 (device, out, nullable): raw logits, for tests.
+ * E_CAPACITY if T_r + C > capacity for any request. */
+dlm_status dlm_denoise_step(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
+                            float* conf, int32_t* pred, float* logits,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Applies the commit rule at step `step` (0-based) to each request's canvas,
+ * in place: only positions that hold mask_id are written, always with their
+ * prediction (never with mask_id).  Ranking: higher confidence first, equal
+ * confidence -> lower position first.
+ *   n_committed [n_seqs] int32 (device, out, nullable): positions written;
+ *   n_masked    [n_seqs] int32 (device, out, nullable): positions still masked.
+ * E_ARG if step is outside [0, rule->n_steps). */
+dlm_status dlm_commit(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
+                      const float* conf, const int32_t* pred, const dlm_commit_rule* rule,
+                      int32_t step, int32_t* n_committed, int32_t* n_masked, void* stream);
+
+/* Forward over each request's finished canvas with the denoising mask; its K/V
+ * are written to slots [T_r, T_r + C); then T_r += C.  No LM head.  A masked
+ * position in a canvas sets DLM_DEVERR_MASK_APPEND on the device. */
+dlm_status dlm_append_canvas(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronises `stream`, reads and clears the device error word.  Returns
+ * DLM_OK, or DLM_E_DEVICE with the bits in *bits (nullable). */
+dlm_status dlm_check_device_status(dlm_model* model, void* stream, int32_t* bits);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* dlm_last_error(void);
+
+/* Test hook for MoE models: while `router_ids` (device int32, nullable) is set,
+ * every forward also writes each layer's selected experts there, laid out
+ * [n_layers][rows][top_k] in selection order (rows = tokens of the forward).
+ * E_CAPACITY at the forward if n_layers * rows * top_k > capacity_entries. */
+dlm_status dlm_debug_router(dlm_model* model, int32_t* router_ids, int64_t capacity_entries);
+
+/* Kernel timing.  `kernel_mask` bit i enables timing of kernel id i (0 = off):
+ * every launch of a timed kernel is bracketed by HIP events on its stream.
+ * dlm_timing_read synchronises, sums the elapsed times per kernel id since the
+ * last read, and resets.
+ *   ms[DLM_K_COUNT], launches[DLM_K_COUNT] (host, out; nullable). */
+typedef enum {
+    DLM_K_EMBED = 0, DLM_K_NORM, DLM_K_GEMM_QKV, DLM_K_ROPE_KV, DLM_K_ATTN,
+    DLM_K_ATTN_MERGE, DLM_K_GEMM_O, DLM_K_GEMM_GATE_UP, DLM_K_GEMM_DOWN,
+    DLM_K_QUANT, DLM_K_ROUTER, DLM_K_TOPK, DLM_K_PERMUTE, DLM_K_EXPERT_GATE_UP,
+    DLM_K_EXPERT_DOWN, DLM_K_COMBINE, DLM_K_LM_HEAD, DLM_K_LM_MERGE, DLM_K_COMMIT,
+    DLM_K_COUNT
+} dlm_kernel_id;
+dlm_status dlm_timing_enable(dlm_model* model, int32_t kernel_mask);
+dlm_status dlm_timing_read(dlm_model* model, float* ms, int32_t* launches);
+const char* dlm_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_H */

@@ -1,0 +1,633 @@
+// C ABI of the block-diffusion denoising library: argument validation,
+// workspace planning, and the sequence of gfx950 kernels that makes up prefill,
+// one denoising step, the commit, and the canvas append.  The operations and
+// their sources are documented in include/dlm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dlm.h"
+#include "kernels.h"
+
+using namespace dlm;
+
+namespace {
+
+thread_local std::string g_err;
+
+dlm_status fail(dlm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dlm_status fail(dlm_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+const char* kKernelNames[DLM_K_COUNT] = {
+    "embed", "rmsnorm", "gemm_qkv", "rope_kv", "attention", "attention_merge", "gemm_o",
+    "gemm_gate_up", "gemm_down", "quant", "router", "router_topk", "moe_route", "expert_gate_up",
+    "expert_down", "moe_combine", "lm_head", "lm_merge", "commit"};
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_bytes(int dtype) { return dtype == DLM_F32 ? 4 : dtype == DLM_BF16 ? 2 : 1; }
+
+}  // namespace
+
+struct dlm_model {
+    dlm_config cfg;
+    dlm_weights w;
+    std::vector<dlm_layer_weights> layers;
+    int* d_err = nullptr;
+    int device = 0;
+    int32_t* dbg_router = nullptr;   // test hook: per-layer router choices
+    int64_t dbg_cap = 0;
+    // timing
+    uint32_t timing_mask = 0;
+    struct Ev { hipEvent_t a, b; int id; };
+    std::vector<Ev> pending;
+    std::vector<hipEvent_t> pool;
+    float ms[DLM_K_COUNT] = {};
+    int launches[DLM_K_COUNT] = {};
+};
+
+namespace {
+
+// RAII bracket of one kernel launch with HIP events when that kernel id is timed.
+struct Timed {
+    dlm_model* m; hipStream_t st; int id; bool on; hipEvent_t b;
+    Timed(dlm_model* m_, int id_, hipStream_t st_) : m(m_), st(st_), id(id_) {
+        on = (m->timing_mask >> id) & 1u;
+        if (!on) return;
+        hipEvent_t a = take();
+        b = take();
+        hipEventRecord(a, st);
+        m->pending.push_back({a, b, id});
+    }
+    ~Timed() {
+        if (on) hipEventRecord(b, st);
+    }
+    hipEvent_t take() {
+        if (!m->pool.empty()) {
+            hipEvent_t e = m->pool.back();
+            m->pool.pop_back();
+            return e;
+        }
+        hipEvent_t e;
+        hipEventCreate(&e);
+        return e;
+    }
+};
+
+// ----------------------------------------------------------- workspace --
+
+struct Plan {
+    size_t x, hA, hb, hq, hs, qkv, q, ao, aoq, aos, fi, fiq, fis, rl, tid, tw, offs, tstart, sorted, inv,
+        hist, lrank, ei, eiq, eis, y, pmax, psum, pidx, opart, mlpart, total;
+};
+
+Plan plan(const dlm_config& c, int rows, int max_kv) {
+    (void)max_kv;
+    Plan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    const size_t R = rows, d = c.d_model, qd = (size_t)c.n_q_heads * c.head_dim;
+    const size_t nqkv = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+    const size_t act = c.dtype == DLM_F32 ? 4 : 2;
+    const bool fp8 = c.dtype == DLM_FP8;
+    const bool moe = c.ffn == DLM_FFN_MOE;
+    const size_t A = moe ? R * c.top_k : 0;
+    p.x = take(R * d * 4);
+    p.hA = take(R * d * act);                // fp32 (f32) or bf16 normalised activations
+    p.hb = p.hA;
+    p.hq = fp8 ? take(R * d) : 0;
+    p.hs = fp8 ? take(R * 4) : 0;
+    p.qkv = take(R * nqkv * 4);
+    p.q = take(R * qd * act);
+    p.ao = take(R * qd * act);
+    p.aoq = fp8 ? take(R * qd) : 0;
+    p.aos = fp8 ? take(R * 4) : 0;
+    p.fi = take(R * c.d_ffn * act);
+    p.fiq = fp8 ? take(R * c.d_ffn) : 0;
+    p.fis = fp8 ? take(R * 4) : 0;
+    if (moe) {
+        p.rl = take(R * c.n_experts * 4);
+        p.tid = take(A * 4);
+        p.tw = take(A * 4);
+        p.offs = take((c.n_experts + 1) * 4);
+        p.tstart = take((c.n_experts + 1) * 4);
+        p.sorted = take(A * 4);
+        p.inv = take(A * 4);
+        p.hist = take((size_t)route_blocks((int)A) * c.n_experts * 4);
+        p.lrank = take(A * 4);
+        p.ei = take(A * c.d_expert * act);
+        p.eiq = fp8 ? take(A * c.d_expert) : 0;
+        p.eis = fp8 ? take(A * 4) : 0;
+        p.y = take(A * d * 4);
+    }
+    const size_t nt = (c.vocab + lm_head_tile_n() - 1) / lm_head_tile_n();
+    p.pmax = take(R * nt * 4);
+    p.psum = take(R * nt * 4);
+    p.pidx = take(R * nt * 4);
+    const size_t af = attention_work_floats(rows, c.n_q_heads, c.head_dim);
+    p.opart = take(af / (c.head_dim + 2) * c.head_dim * 4);
+    p.mlpart = take(af / (c.head_dim + 2) * 2 * 4);
+    p.total = off;
+    return p;
+}
+
+template <typename T> T* at(void* ws, size_t off) { return (T*)((uint8_t*)ws + off); }
+
+// ------------------------------------------------------------- validation --
+
+dlm_status check_config(const dlm_config* c) {
+    if (!c) return fail(DLM_E_ARG, "config is NULL");
+    if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->vocab < 2)
+        return fail(DLM_E_SHAPE, "non-positive model dimension");
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+        return fail(DLM_E_SHAPE, "head_dim %d not in {32, 64, 128}", c->head_dim);
+    if (c->n_q_heads % c->n_kv_heads) return fail(DLM_E_SHAPE, "n_q_heads %% n_kv_heads != 0");
+    if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DLM_E_ARG, "mask_id outside [0, vocab)");
+    if (c->dtype < DLM_F32 || c->dtype > DLM_FP8) return fail(DLM_E_DTYPE, "unknown dtype %d", c->dtype);
+    if (c->ffn != DLM_FFN_DENSE && c->ffn != DLM_FFN_MOE) return fail(DLM_E_ARG, "unknown ffn kind %d", c->ffn);
+    if (c->canvas < 1 || c->canvas > 1024) return fail(DLM_E_SHAPE, "canvas %d not in [1, 1024]", c->canvas);
+    if (c->d_ffn < 1) return fail(DLM_E_SHAPE, "d_ffn < 1");
+    if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(DLM_E_ARG, "bad rms_eps / rope_base");
+    const int eb = elem_bytes(c->dtype);
+    const int kdims[4] = {c->d_model, c->n_q_heads * c->head_dim, c->d_ffn,
+                          c->ffn == DLM_FFN_MOE ? c->d_expert : c->d_model};
+    for (int k : kdims)
+        if ((k * eb) % 16) return fail(DLM_E_SHAPE, "GEMM inner dimension %d is not a multiple of 16 bytes", k);
+    if (c->ffn == DLM_FFN_MOE) {
+        if (c->n_experts < 1 || c->n_experts > 256) return fail(DLM_E_SHAPE, "n_experts not in [1, 256]");
+        if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts)
+            return fail(DLM_E_SHAPE, "top_k not in [1, min(16, n_experts)]");
+        if (c->d_expert < 1) return fail(DLM_E_SHAPE, "d_expert < 1");
+    }
+    return DLM_OK;
+}
+
+dlm_status check_weights(const dlm_config* c, const dlm_weights* w) {
+    if (!w) return fail(DLM_E_ARG, "weights is NULL");
+    if (!w->embed || !w->final_norm || !w->lm_head || !w->layers) return fail(DLM_E_ARG, "NULL top-level weight");
+    const bool fp8 = c->dtype == DLM_FP8;
+    if (fp8 && !w->lm_head_s) return fail(DLM_E_DTYPE, "fp8 model needs lm_head_s");
+    for (int l = 0; l < c->n_layers; ++l) {
+        const dlm_layer_weights& L = w->layers[l];
+        if (!L.attn_norm || !L.ffn_norm || !L.wqkv || !L.wo || !L.w_gate || !L.w_up || !L.w_down)
+            return fail(DLM_E_ARG, "layer %d: NULL weight", l);
+        if (fp8 && (!L.wqkv_s || !L.wo_s || !L.w_gate_s || !L.w_up_s || !L.w_down_s))
+            return fail(DLM_E_DTYPE, "layer %d: fp8 model needs per-channel scales", l);
+        if (c->ffn == DLM_FFN_MOE) {
+            if (!L.w_router || !L.we_gate || !L.we_up || !L.we_down)
+                return fail(DLM_E_ARG, "layer %d: NULL expert weight", l);
+            if (fp8 && (!L.we_gate_s || !L.we_up_s || !L.we_down_s))
+                return fail(DLM_E_DTYPE, "layer %d: fp8 model needs expert scales", l);
+        }
+    }
+    return DLM_OK;
+}
+
+dlm_status check_seq(const dlm_model* m, const dlm_seq* s, int extra, bool need_canvas, int idx) {
+    if (!s) return fail(DLM_E_ARG, "seq %d is NULL", idx);
+    if (!s->kv) return fail(DLM_E_ARG, "seq %d: kv is NULL", idx);
+    if (s->page_table || s->page_size) return fail(DLM_E_UNSUPPORTED, "seq %d: paged KV cache is not supported", idx);
+    if (need_canvas && !s->canvas) return fail(DLM_E_ARG, "seq %d: canvas is NULL", idx);
+    if (s->T < 0 || s->capacity < 0) return fail(DLM_E_ARG, "seq %d: negative T or capacity", idx);
+    if ((long)s->T + extra > (long)s->capacity)
+        return fail(DLM_E_CAPACITY, "seq %d: T %d + %d exceeds capacity %d", idx, s->T, extra, s->capacity);
+    (void)m;
+    return DLM_OK;
+}
+
+dlm_status check_ws(const dlm_model* m, void* ws, size_t ws_bytes, int rows, int max_kv) {
+    if (m->dbg_router && m->cfg.ffn == DLM_FFN_MOE &&
+        (int64_t)m->cfg.n_layers * rows * m->cfg.top_k > m->dbg_cap)
+        return fail(DLM_E_CAPACITY, "router debug buffer holds %lld entries, the forward needs %lld",
+                    (long long)m->dbg_cap, (long long)m->cfg.n_layers * rows * m->cfg.top_k);
+    const size_t need = plan(m->cfg, rows, max_kv).total;
+    if (!ws) return fail(DLM_E_WORKSPACE, "workspace is NULL");
+    if (ws_bytes < need) return fail(DLM_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return DLM_OK;
+}
+
+dlm_status hip_status(const char* where) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DLM_E_HIP, "%s: %s", where, hipGetErrorString(e));
+    return DLM_OK;
+}
+
+// ---------------------------------------------------------------- forward --
+
+enum Mode { PREFILL, DENOISE, APPEND };
+
+void run_gemm(dlm_model* m, int id, const GemmDesc& d, hipStream_t st, bool grouped = false) {
+    Timed t(m, id, st);
+    if (grouped) gemm_grouped(d, st);
+    else gemm(d, st);
+}
+
+void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, void* ws, float* conf, int* pred,
+             float* logits, hipStream_t st) {
+    const dlm_config& c = m->cfg;
+    const int R = seqs.n * seqs.per_seq;
+    int max_kv = 0;
+    for (int i = 0; i < seqs.n; ++i) max_kv = std::max(max_kv, seqs.T[i] + seqs.per_seq);
+    const Plan p = plan(c, R, max_kv);
+    const bool f32 = c.dtype == DLM_F32, fp8 = c.dtype == DLM_FP8;
+    const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
+    const int nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+    const int gdt = c.dtype;                       // GEMM operand type
+    float* x = at<float>(ws, p.x);
+    void* hA = at<void>(ws, p.hA);
+    uint8_t* hq = fp8 ? at<uint8_t>(ws, p.hq) : nullptr;
+    float* hs = fp8 ? at<float>(ws, p.hs) : nullptr;
+    float* qkv = at<float>(ws, p.qkv);
+    void* q = at<void>(ws, p.q);
+    void* ao = at<void>(ws, p.ao);
+    void* fi = at<void>(ws, p.fi);
+
+    {
+        Timed t(m, DLM_K_EMBED, st);
+        embed(ids, R, m->w.embed, f32 ? DT_F32 : DT_BF16, d, c.vocab, c.mask_id, mode == APPEND, x, m->d_err, st);
+    }
+
+    // RMSNorm into the GEMM operand: fp32 / bf16 in hA; fp8 also codes + scales
+    auto norm = [&](const float* g) {
+        Timed t(m, DLM_K_NORM, st);
+        rmsnorm(x, g, R, d, c.rms_eps, f32 ? (float*)hA : nullptr, f32 ? nullptr : (uint16_t*)hA, hq, hs, st);
+    };
+    auto opA = [&](const void* bf, const void* q8) { return fp8 ? q8 : bf; };
+    auto quant = [&](const void* src, int rows, int cols, uint8_t* qd8, float* sc) {
+        if (!fp8) return;
+        Timed t(m, DLM_K_QUANT, st);
+        quant_rows((const uint16_t*)src, rows, cols, qd8, sc, st);
+    };
+
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dlm_layer_weights& L = m->layers[l];
+        norm(L.attn_norm);
+        {
+            GemmDesc g;
+            g.dtype = gdt; g.epi = GEMM_STORE_F32;
+            g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
+            g.B = L.wqkv; g.ldb = d; g.b_scale = L.wqkv_s;
+            g.M = R; g.N = nqkv; g.K = d;
+            g.C = qkv; g.ldc = nqkv;
+            run_gemm(m, DLM_K_GEMM_QKV, g, st);
+        }
+        {
+            Timed t(m, DLM_K_ROPE_KV, st);
+            rope_kv(qkv, R, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, c.rope_base, f32, q, st);
+        }
+        {
+            Timed t(m, DLM_K_ATTN, st);
+            AttnWork w{at<float>(ws, p.opart), at<float>(ws, p.mlpart), 0};
+            attention(q, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, mode == PREFILL, f32, ao, w, st);
+        }
+        quant(ao, R, qd, fp8 ? at<uint8_t>(ws, p.aoq) : nullptr, fp8 ? at<float>(ws, p.aos) : nullptr);
+        {
+            GemmDesc g;
+            g.dtype = gdt; g.epi = GEMM_ADD_F32;
+            g.A = opA(ao, fp8 ? at<uint8_t>(ws, p.aoq) : nullptr); g.lda = qd;
+            g.a_scale = fp8 ? at<float>(ws, p.aos) : nullptr;
+            g.B = L.wo; g.ldb = qd; g.b_scale = L.wo_s;
+            g.M = R; g.N = d; g.K = qd;
+            g.C = x; g.ldc = d;
+            run_gemm(m, DLM_K_GEMM_O, g, st);
+        }
+        norm(L.ffn_norm);
+        if (c.ffn == DLM_FFN_MOE) {
+            const int E = c.n_experts, k = c.top_k, De = c.d_expert, A = R * k;
+            float* rl = at<float>(ws, p.rl);
+            int* tid = at<int>(ws, p.tid);
+            float* tw = at<float>(ws, p.tw);
+            int* offs = at<int>(ws, p.offs);
+            int* tstart = at<int>(ws, p.tstart);
+            int* sorted = at<int>(ws, p.sorted);
+            int* inv = at<int>(ws, p.inv);
+            {
+                GemmDesc g;   // router logits: bf16 operands (fp32 for f32 models), fp32 out
+                g.dtype = f32 ? DT_F32 : DT_BF16; g.epi = GEMM_STORE_F32;
+                g.A = hA; g.lda = d; g.B = L.w_router; g.ldb = d;
+                g.M = R; g.N = E; g.K = d; g.C = rl; g.ldc = E;
+                run_gemm(m, DLM_K_ROUTER, g, st);
+            }
+            {
+                Timed t(m, DLM_K_TOPK, st);
+                router_topk(rl, R, E, k, tid, tw, m->dbg_router ? m->dbg_router + (long)l * R * k : nullptr, st);
+            }
+            {
+                Timed t(m, DLM_K_PERMUTE, st);
+                RouteWork rw{at<int>(ws, p.hist), at<int>(ws, p.lrank)};
+                moe_route(tid, A, E, offs, tstart, sorted, inv, rw, st);
+            }
+            void* ei = at<void>(ws, p.ei);
+            {
+                GemmDesc g;
+                g.dtype = gdt; g.epi = GEMM_SWIGLU; g.out_f32 = f32;
+                g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
+                g.gather = sorted; g.gather_div = k;
+                g.B = L.we_gate; g.B2 = L.we_up; g.ldb = d; g.b_stride = (long)De * d;
+                g.b_scale = L.we_gate_s; g.b2_scale = L.we_up_s; g.bs_stride = De;
+                g.offs = offs; g.tile_start = tstart; g.E = E;
+                g.M = A; g.N = De; g.K = d; g.C = ei; g.ldc = De;
+                run_gemm(m, DLM_K_EXPERT_GATE_UP, g, st, true);
+            }
+            quant(ei, A, De, fp8 ? at<uint8_t>(ws, p.eiq) : nullptr, fp8 ? at<float>(ws, p.eis) : nullptr);
+            float* y = at<float>(ws, p.y);
+            {
+                GemmDesc g;
+                g.dtype = gdt; g.epi = GEMM_STORE_F32;
+                g.A = opA(ei, fp8 ? at<uint8_t>(ws, p.eiq) : nullptr); g.lda = De;
+                g.a_scale = fp8 ? at<float>(ws, p.eis) : nullptr;
+                g.B = L.we_down; g.ldb = De; g.b_stride = (long)d * De;
+                g.b_scale = L.we_down_s; g.bs_stride = d;
+                g.offs = offs; g.tile_start = tstart; g.E = E;
+                g.M = A; g.N = d; g.K = De; g.C = y; g.ldc = d;
+                run_gemm(m, DLM_K_EXPERT_DOWN, g, st, true);
+            }
+            {
+                Timed t(m, DLM_K_COMBINE, st);
+                moe_combine(x, y, inv, tw, R, k, d, st);
+            }
+        }
+        // dense SwiGLU FFN, or the MoE's shared expert
+        {
+            GemmDesc g;
+            g.dtype = gdt; g.epi = GEMM_SWIGLU; g.out_f32 = f32;
+            g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
+            g.B = L.w_gate; g.B2 = L.w_up; g.ldb = d; g.b_scale = L.w_gate_s; g.b2_scale = L.w_up_s;
+            g.M = R; g.N = c.d_ffn; g.K = d; g.C = fi; g.ldc = c.d_ffn;
+            run_gemm(m, DLM_K_GEMM_GATE_UP, g, st);
+        }
+        quant(fi, R, c.d_ffn, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr, fp8 ? at<float>(ws, p.fis) : nullptr);
+        {
+            GemmDesc g;
+            g.dtype = gdt; g.epi = GEMM_ADD_F32;
+            g.A = opA(fi, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr); g.lda = c.d_ffn;
+            g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
+            g.B = L.w_down; g.ldb = c.d_ffn; g.b_scale = L.w_down_s;
+            g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
+            run_gemm(m, DLM_K_GEMM_DOWN, g, st);
+        }
+    }
+    if (mode != DENOISE) return;
+
+    norm(m->w.final_norm);
+    const int nt = (c.vocab + lm_head_tile_n() - 1) / lm_head_tile_n();
+    float* pmax = at<float>(ws, p.pmax);
+    float* psum = at<float>(ws, p.psum);
+    int* pidx = at<int>(ws, p.pidx);
+    {
+        GemmDesc g;
+        g.dtype = gdt; g.epi = GEMM_LMHEAD;
+        g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
+        g.B = m->w.lm_head; g.ldb = d; g.b_scale = m->w.lm_head_s;
+        g.M = R; g.N = c.vocab; g.K = d;
+        g.pmax = pmax; g.psum = psum; g.pidx = pidx; g.mask_col = c.mask_id;
+        g.logits = logits; g.ld_logits = c.vocab;
+        run_gemm(m, DLM_K_LM_HEAD, g, st);
+    }
+    {
+        Timed t(m, DLM_K_LM_MERGE, st);
+        lm_merge(pmax, psum, pidx, R, nt, conf, pred, st);
+    }
+}
+
+dlm_status build_tab(dlm_model* m, dlm_seq* const* seqs, int n_seqs, int extra, bool need_canvas, SeqTab& tab,
+                     int& max_kv) {
+    if (!seqs) return fail(DLM_E_ARG, "seqs is NULL");
+    if (n_seqs < 1 || n_seqs > DLM_MAX_SEQS) return fail(DLM_E_ARG, "n_seqs %d not in [1, %d]", n_seqs, DLM_MAX_SEQS);
+    memset(&tab, 0, sizeof tab);
+    max_kv = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        dlm_status s = check_seq(m, seqs[i], extra, need_canvas, i);
+        if (s) return s;
+        tab.kv[i] = seqs[i]->kv;
+        tab.T[i] = seqs[i]->T;
+        tab.cap[i] = seqs[i]->capacity;
+        max_kv = std::max(max_kv, seqs[i]->T + extra);
+    }
+    tab.n = n_seqs;
+    tab.per_seq = extra;
+    return DLM_OK;
+}
+
+}  // namespace
+
+// ==================================================================== ABI ==
+
+extern "C" {
+
+const char* dlm_last_error(void) { return g_err.c_str(); }
+
+const char* dlm_kernel_name(int32_t id) {
+    return (id >= 0 && id < DLM_K_COUNT) ? kKernelNames[id] : "";
+}
+
+dlm_status dlm_create(const dlm_config* cfg, const dlm_weights* weights, dlm_model** out) {
+    g_err.clear();
+    if (!out) return fail(DLM_E_ARG, "out is NULL");
+    *out = nullptr;
+    dlm_status s = check_config(cfg);
+    if (s) return s;
+    s = check_weights(cfg, weights);
+    if (s) return s;
+    dlm_model* m = new dlm_model();
+    m->cfg = *cfg;
+    m->w = *weights;
+    m->layers.assign(weights->layers, weights->layers + cfg->n_layers);
+    m->w.layers = nullptr;
+    hipError_t e = hipGetDevice(&m->device);
+    if (e == hipSuccess) e = hipMalloc((void**)&m->d_err, sizeof(int));
+    if (e == hipSuccess) e = hipMemset(m->d_err, 0, sizeof(int));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        if (m->d_err) hipFree(m->d_err);
+        delete m;
+        return fail(DLM_E_HIP, "dlm_create: %s", hipGetErrorString(e));
+    }
+    *out = m;
+    return DLM_OK;
+}
+
+void dlm_destroy(dlm_model* m) {
+    if (!m) return;
+    for (auto& ev : m->pending) {
+        hipEventDestroy(ev.a);
+        hipEventDestroy(ev.b);
+    }
+    for (auto e : m->pool) hipEventDestroy(e);
+    if (m->d_err) hipFree(m->d_err);
+    delete m;
+}
+
+size_t dlm_workspace_bytes(const dlm_model* m, int32_t max_rows, int32_t max_kv_tokens) {
+    if (!m || max_rows < 1 || max_kv_tokens < 0) return 0;
+    return plan(m->cfg, max_rows, max_kv_tokens).total;
+}
+
+dlm_status dlm_prefill(dlm_model* m, dlm_seq* seq, const int32_t* ids, int32_t n, void* ws, size_t ws_bytes,
+                       void* stream) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    if (!ids) return fail(DLM_E_ARG, "ids is NULL");
+    if (n < 1) return fail(DLM_E_ARG, "n %d < 1", n);
+    SeqTab tab;
+    int max_kv;
+    dlm_seq* one[1] = {seq};
+    dlm_status s = build_tab(m, one, 1, n, false, tab, max_kv);
+    if (s) return s;
+    s = check_ws(m, ws, ws_bytes, n, max_kv);
+    if (s) return s;
+    IdSource src{};
+    src.flat = ids;
+    src.per_seq = n;
+    forward(m, PREFILL, tab, src, ws, nullptr, nullptr, nullptr, (hipStream_t)stream);
+    s = hip_status("dlm_prefill");
+    if (s) return s;
+    seq->T += n;
+    return DLM_OK;
+}
+
+dlm_status dlm_denoise_step(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, float* conf, int32_t* pred,
+                            float* logits, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    if (!conf || !pred) return fail(DLM_E_ARG, "conf / pred is NULL");
+    SeqTab tab;
+    int max_kv;
+    dlm_status s = build_tab(m, seqs, n_seqs, m->cfg.canvas, true, tab, max_kv);
+    if (s) return s;
+    s = check_ws(m, ws, ws_bytes, n_seqs * m->cfg.canvas, max_kv);
+    if (s) return s;
+    IdSource src{};
+    for (int i = 0; i < n_seqs; ++i) src.canvas[i] = seqs[i]->canvas;
+    src.per_seq = m->cfg.canvas;
+    forward(m, DENOISE, tab, src, ws, conf, pred, logits, (hipStream_t)stream);
+    return hip_status("dlm_denoise_step");
+}
+
+dlm_status dlm_commit(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, const float* conf, const int32_t* pred,
+                      const dlm_commit_rule* rule, int32_t step, int32_t* n_committed, int32_t* n_masked,
+                      void* stream) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    if (!conf || !pred) return fail(DLM_E_ARG, "conf / pred is NULL");
+    if (!rule) return fail(DLM_E_ARG, "rule is NULL");
+    if (!seqs) return fail(DLM_E_ARG, "seqs is NULL");
+    if (n_seqs < 1 || n_seqs > DLM_MAX_SEQS) return fail(DLM_E_ARG, "n_seqs %d not in [1, %d]", n_seqs, DLM_MAX_SEQS);
+    if (rule->n_steps < 1) return fail(DLM_E_ARG, "rule n_steps < 1");
+    if (step < 0 || step >= rule->n_steps) return fail(DLM_E_ARG, "step %d outside [0, %d)", step, rule->n_steps);
+    int kind, k = 0;
+    bool force = false;
+    if (rule->kind == DLM_COMMIT_TOPK) {
+        if (!rule->k_per_step) return fail(DLM_E_ARG, "k_per_step is NULL");
+        k = rule->k_per_step[step];
+        if (k < 0) return fail(DLM_E_ARG, "k_per_step[%d] < 0", step);
+        kind = 0;
+    } else if (rule->kind == DLM_COMMIT_THRESHOLD) {
+        if (!(rule->threshold >= 0.f)) return fail(DLM_E_ARG, "threshold must be >= 0");
+        kind = 1;
+        force = step == rule->n_steps - 1;
+    } else {
+        return fail(DLM_E_ARG, "unknown commit rule %d", rule->kind);
+    }
+    int32_t* canv[DLM_MAX_SEQS];
+    for (int i = 0; i < n_seqs; ++i) {
+        if (!seqs[i] || !seqs[i]->canvas) return fail(DLM_E_ARG, "seq %d: canvas is NULL", i);
+        canv[i] = seqs[i]->canvas;
+    }
+    {
+        Timed t(m, DLM_K_COMMIT, (hipStream_t)stream);
+        commit(canv, n_seqs, m->cfg.canvas, conf, pred, m->cfg.mask_id, kind, k, rule->threshold, force,
+               n_committed, n_masked, (hipStream_t)stream);
+    }
+    return hip_status("dlm_commit");
+}
+
+dlm_status dlm_append_canvas(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, void* ws, size_t ws_bytes,
+                             void* stream) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    SeqTab tab;
+    int max_kv;
+    dlm_status s = build_tab(m, seqs, n_seqs, m->cfg.canvas, true, tab, max_kv);
+    if (s) return s;
+    s = check_ws(m, ws, ws_bytes, n_seqs * m->cfg.canvas, max_kv);
+    if (s) return s;
+    IdSource src{};
+    for (int i = 0; i < n_seqs; ++i) src.canvas[i] = seqs[i]->canvas;
+    src.per_seq = m->cfg.canvas;
+    forward(m, APPEND, tab, src, ws, nullptr, nullptr, nullptr, (hipStream_t)stream);
+    s = hip_status("dlm_append_canvas");
+    if (s) return s;
+    for (int i = 0; i < n_seqs; ++i) seqs[i]->T += m->cfg.canvas;
+    return DLM_OK;
+}
+
+dlm_status dlm_check_device_status(dlm_model* m, void* stream, int32_t* bits) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    int v = 0;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpy(&v, m->d_err, sizeof(int), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v) e = hipMemset(m->d_err, 0, sizeof(int));
+    if (e != hipSuccess) return fail(DLM_E_HIP, "dlm_check_device_status: %s", hipGetErrorString(e));
+    if (bits) *bits = v;
+    if (v) return fail(DLM_E_DEVICE, "device error word 0x%x", v);
+    return DLM_OK;
+}
+
+dlm_status dlm_debug_router(dlm_model* m, int32_t* router_ids, int64_t capacity_entries) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    if (router_ids && capacity_entries < 0) return fail(DLM_E_ARG, "negative capacity");
+    m->dbg_router = router_ids;
+    m->dbg_cap = router_ids ? capacity_entries : 0;
+    return DLM_OK;
+}
+
+dlm_status dlm_timing_enable(dlm_model* m, int32_t mask) {
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    m->timing_mask = (uint32_t)mask;
+    return DLM_OK;
+}
+
+dlm_status dlm_timing_read(dlm_model* m, float* ms, int32_t* launches) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    for (auto& ev : m->pending) {
+        hipError_t e = hipEventSynchronize(ev.b);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, ev.a, ev.b);
+        if (e != hipSuccess) return fail(DLM_E_HIP, "dlm_timing_read: %s", hipGetErrorString(e));
+        m->ms[ev.id] += t;
+        m->launches[ev.id] += 1;
+        m->pool.push_back(ev.a);
+        m->pool.push_back(ev.b);
+    }
+    m->pending.clear();
+    for (int i = 0; i < DLM_K_COUNT; ++i) {
+        if (ms) ms[i] = m->ms[i];
+        if (launches) launches[i] = m->launches[i];
+        m->ms[i] = 0.f;
+        m->launches[i] = 0;
+    }
+    return DLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Host-side launchers of the gfx950 kernels.  Every launcher enqueues on the
+// given stream and returns immediately; shapes are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dlm {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+enum GemmEpi { GEMM_STORE_F32 = 0, GEMM_STORE_BF16, GEMM_ADD_F32, GEMM_SWIGLU, GEMM_LMHEAD };
+
+constexpr int MAX_SEQS = 64;
+
+// m-tile rows of the grouped (per-expert) GEMMs; the routing scan computes
+// each expert's first m-tile for this tile height.
+constexpr int GROUPED_BM = 32;
+
+// C[M, N] (op)= A[M, K] * B[N, K]^T.  Leading dimensions in elements.
+struct GemmDesc {
+    int dtype = DT_BF16;        // element type of A and B
+    int epi = GEMM_STORE_F32;
+    bool out_f32 = false;       // SwiGLU output in fp32 (f32 models) instead of bf16
+    const void* A = nullptr; long lda = 0;
+    const void* B = nullptr; const void* B2 = nullptr; long ldb = 0;
+    const float* a_scale = nullptr;   // fp8: per A row
+    const float* b_scale = nullptr;   // fp8: per output column (B row)
+    const float* b2_scale = nullptr;
+    int M = 0, N = 0, K = 0;
+    void* C = nullptr; long ldc = 0;
+    // LM head reduction: partials [M, ceil(N / lm_head_tile_n())]
+    float* pmax = nullptr; float* psum = nullptr; int* pidx = nullptr;
+    int mask_col = -1;
+    float* logits = nullptr; long ld_logits = 0;
+    // grouped
+    const int* gather = nullptr; int gather_div = 1;
+    long b_stride = 0;          // elements between experts' B matrices
+    long bs_stride = 0;         // elements between experts' scale vectors
+    const int* offs = nullptr;  // [E + 1]
+    const int* tile_start = nullptr;  // [E + 1]
+    int E = 0;
+};
+
+void gemm(const GemmDesc& d, hipStream_t st);
+void gemm_grouped(const GemmDesc& d, hipStream_t st);
+int lm_head_tile_n();
+
+// Token ids of one forward: one flat array, or per-request canvases.
+struct IdSource {
+    const int32_t* flat;               // nullable
+    const int32_t* canvas[MAX_SEQS];   // per request (when flat is null)
+    int per_seq;                       // rows per request
+};
+
+// Requests of one forward: KV cache base, cached tokens T and capacity.
+struct SeqTab {
+    void* kv[MAX_SEQS];
+    int T[MAX_SEQS];
+    int cap[MAX_SEQS];   // capacity (tokens) of each request's cache
+    int n;
+    int per_seq;         // rows per request in this forward
+};
+
+// x[r] = float(embed[id_r]); ids outside [0, vocab) set DEVERR_TOKEN_RANGE
+// (and read row 0); with check_mask, ids equal to mask_id set DEVERR_MASK_APPEND.
+void embed(const IdSource& ids, int rows, const void* table, int dtype, int d, int vocab,
+           int mask_id, bool check_mask, float* x, int* err, hipStream_t st);
+
+// h = x / sqrt(mean(x^2) + eps) * g per row, written to every non-null output:
+// hf fp32, hb bf16, and (fp8 models) hq E4M3 codes with per-row scales hs
+// quantised from the bf16 value.
+void rmsnorm(const float* x, const float* g, int rows, int d, float eps, float* hf,
+             uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st);
+
+// Per-row E4M3 quantisation of a bf16 matrix [rows, d]: s = amax / 448 (1 for a
+// zero row), q = e4m3(x / s).
+void quant_rows(const uint16_t* x, int rows, int d, uint8_t* q, float* s, hipStream_t st);
+
+// RoPE on Q and K of qkv (fp32 [rows, (Hq + 2 Hkv) * dh]) at absolute positions
+// T_r + i; Q -> q_out [rows, Hq * dh]; K, V -> cache slots T_r + i of layer l.
+// Element type of q_out and the cache: fp32 (f32 models) or bf16.
+void rope_kv(const float* qkv, int rows, const SeqTab& seqs, int layer, int n_layers, int hq,
+             int hkv, int dh, float base, bool f32, void* q_out, hipStream_t st);
+
+// Attention of rows' queries (q [rows, Hq * dh]) over request r's cache slots
+// [0, T_r + per_seq): causal (prefill: key t visible to the query at position
+// p iff t <= p) or block (every key visible).  out [rows, Hq * dh].
+struct AttnWork {
+    float* o_part;      // split-KV partial outputs
+    float* ml_part;     // split-KV partial (max, sum)
+    long capacity;      // floats available in o_part
+};
+void attention(const void* q, const SeqTab& seqs, int layer, int n_layers, int hq, int hkv,
+               int dh, bool causal, bool f32, void* out, const AttnWork& w, hipStream_t st);
+long attention_work_floats(int rows, int hq, int dh);
+
+// Router: logits fp32 [rows, E] -> top-k experts (ties -> lower id), weights =
+// softmax probabilities renormalised over the chosen k.
+void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy, hipStream_t st);
+
+// Stable counting sort of the rows*k assignments by expert: offs [E + 1],
+// tile_start [E + 1] (GROUPED_BM-row tiles), sorted_assign [A] (assignment
+// index a = row * k + slot, ordered by (expert, a)), inv [A] (position of a).
+struct RouteWork { int* hist; int* local_rank; };   // hist [blocks * E], local_rank [A]
+void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, int* sorted_assign,
+               int* inv, const RouteWork& w, hipStream_t st);
+int route_blocks(int n_assign);
+
+// x[r] += sum_s w[r, s] * y[inv[r * k + s]]   (y fp32 [A, d] in sorted order)
+void moe_combine(float* x, const float* y, const int* inv, const float* w, int rows, int k, int d,
+                 hipStream_t st);
+
+// LM-head partials (max, sum exp, argmax) per (row, vocab tile) -> conf = 1/Z,
+// pred = lowest argmax.
+void lm_merge(const float* pmax, const float* psum, const int* pidx, int rows, int n_tiles,
+              float* conf, int* pred, hipStream_t st);
+
+// Commit (one workgroup per request).  kind 0: top-k with k; kind 1: threshold
+// (all masked with conf >= thr, at least the most confident one); force_all:
+// every masked position.
+void commit(int32_t* const* canvases, int n_seqs, int C, const float* conf, const int* pred,
+            int mask_id, int kind, int k, float thr, bool force_all, int* n_committed,
+            int* n_masked, hipStream_t st);
+
+}  // namespace dlm

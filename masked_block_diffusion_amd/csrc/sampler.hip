@@ -1,0 +1,119 @@
+// Prediction and commit for gfx950.
+//
+//  lm_merge  per canvas row, folds the LM-head GEMM's per-vocab-tile partials
+//            (tile max, lowest argmax, sum exp(l - tile max)) into the row's
+//            prediction (lowest-id argmax over the vocabulary without [MASK])
+//            and confidence = max softmax probability = 1 / sum exp(l - max).
+//            One wave per row; fixed lane/tile assignment, so deterministic.
+//  commit    one workgroup per request.  Each masked position's rank is the
+//            number of masked positions that beat it (higher confidence, or
+//            equal confidence and a lower position) -- an exact, total order.
+//            Top-k rule: commit rank < k.  Threshold rule: commit conf >= thr
+//            or rank 0 (if any masked position reaches thr, the rank-0 one
+//            does, so "at least the most confident one" is exactly this).
+//            Forced fill: commit every masked position.  Only [MASK] entries
+//            are written, always with the prediction.
+#include "common.h"
+#include "kernels.h"
+
+namespace dlm {
+
+__global__ __launch_bounds__(256) void lm_merge_kernel(const float* pmax, const float* psum, const int* pidx,
+                                                        int rows, int n_tiles, float* conf, int* pred) {
+    const int lane = threadIdx.x % WAVE;
+    const int r = blockIdx.x * 4 + threadIdx.x / WAVE;
+    if (r >= rows) return;
+    const float* pm = pmax + (long)r * n_tiles;
+    const float* ps = psum + (long)r * n_tiles;
+    const int* pi = pidx + (long)r * n_tiles;
+    float m = -INFINITY;
+    int ix = 0x7fffffff;
+    for (int t = lane; t < n_tiles; t += WAVE) {
+        const float v = pm[t];
+        const int i = pi[t];
+        if (v > m || (v == m && i < ix)) { m = v; ix = i; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float om = __shfl_xor(m, o, WAVE);
+        const int oi = __shfl_xor(ix, o, WAVE);
+        if (om > m || (om == m && oi < ix)) { m = om; ix = oi; }
+    }
+    float z = 0.f;
+    for (int t = lane; t < n_tiles; t += WAVE) {
+        const float v = pm[t];
+        if (v != -INFINITY) z += ps[t] * __expf(v - m);
+    }
+    z = wave_sum(z);
+    if (lane == 0) {
+        conf[r] = 1.0f / z;
+        pred[r] = ix;
+    }
+}
+
+void lm_merge(const float* pmax, const float* psum, const int* pidx, int rows, int n_tiles, float* conf, int* pred,
+              hipStream_t st) {
+    if (rows <= 0) return;
+    hipLaunchKernelGGL(lm_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, pmax, psum, pidx, rows, n_tiles,
+                       conf, pred);
+}
+
+struct CanvasTab {
+    int32_t* c[MAX_SEQS];
+};
+
+constexpr int CMAX = 1024;
+
+__global__ __launch_bounds__(256) void commit_kernel(CanvasTab tab, int C, const float* conf, const int* pred,
+                                                      int mask_id, int kind, int k, float thr, int force_all,
+                                                      int* n_committed, int* n_masked) {
+    __shared__ float sc[CMAX];
+    __shared__ int sm[CMAX];
+    __shared__ int cnt[2];
+    const int s = blockIdx.x;
+    int32_t* canvas = tab.c[s];
+    const float* cf = conf + (long)s * C;
+    const int* pr = pred + (long)s * C;
+    if (threadIdx.x < 2) cnt[threadIdx.x] = 0;
+    for (int j = threadIdx.x; j < C; j += 256) {
+        sm[j] = canvas[j] == mask_id;
+        sc[j] = cf[j];
+    }
+    __syncthreads();
+    int my_commit = 0, my_left = 0;
+    for (int j = threadIdx.x; j < C; j += 256) {
+        if (!sm[j]) continue;
+        const float cj = sc[j];
+        int rank = 0;
+        for (int i = 0; i < C; ++i)
+            rank += sm[i] && (sc[i] > cj || (sc[i] == cj && i < j));
+        bool take;
+        if (force_all) take = true;
+        else if (kind == 0) take = rank < k;
+        else take = (cj >= thr) || rank == 0;
+        if (take) {
+            canvas[j] = pr[j];
+            ++my_commit;
+        } else {
+            ++my_left;
+        }
+    }
+    atomicAdd(&cnt[0], my_commit);
+    atomicAdd(&cnt[1], my_left);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (n_committed) n_committed[s] = cnt[0];
+        if (n_masked) n_masked[s] = cnt[1];
+    }
+}
+
+void commit(int32_t* const* canvases, int n_seqs, int C, const float* conf, const int* pred, int mask_id, int kind,
+            int k, float thr, bool force_all, int* n_committed, int* n_masked, hipStream_t st) {
+    if (n_seqs <= 0) return;
+    CanvasTab tab;
+    for (int i = 0; i < n_seqs; ++i) tab.c[i] = canvases[i];
+    hipLaunchKernelGGL(commit_kernel, dim3(n_seqs), dim3(256), 0, st, tab, C, conf, pred, mask_id, kind, k, thr,
+                       (int)force_all, n_committed, n_masked);
+}
+
+}  // namespace dlm

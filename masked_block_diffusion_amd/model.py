@@ -1,0 +1,261 @@
+"""Python binding over libdlm.so: the same four operations as the C ABI.
+
+`DLM` packs a weight dictionary into the ABI's layout (Q/K/V rows concatenated
+into one [(Hq + 2 Hkv) dh, d] matrix, fp8 codes plus their per-channel scales),
+creates the library handle, and exposes dlm_prefill / dlm_denoise_step /
+dlm_commit / dlm_append_canvas over torch tensors.  torch provides device
+memory and the stream; every step of the path runs in the library's kernels.
+
+`generate` is the host iteration loop of block diffusion: prefill the prompt,
+then per canvas start all-[MASK], alternate denoise and commit for the
+schedule's steps (stopping early once nothing is masked), and append the
+finished canvas to the KV cache (rahulsharmavishwakarma.github.io, "Diffusion
+LLMs: what changes when you stop generating one token at a time", sections 2,
+4.1 and 4.2).
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import abi
+from .abi import check
+
+_DTYPES = {"f32": abi.DLM_F32, "bf16": abi.DLM_BF16, "fp8": abi.DLM_FP8}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Seq:
+    """One request: its KV cache [L, 2, Hkv, capacity, dh], its canvas int32[C]
+    and the ABI struct pointing at both (T lives in the struct)."""
+    kv: torch.Tensor
+    canvas: torch.Tensor
+    raw: abi.dlm_seq
+
+    @property
+    def T(self) -> int:
+        return self.raw.T
+
+
+class DLM:
+    def __init__(self, cfg, weights: Dict[str, torch.Tensor], canvas: int, device="cuda"):
+        self.lib = abi.load_library()
+        if not torch.cuda.is_available():
+            raise RuntimeError("DLM needs a HIP device")
+        self.cfg = cfg
+        self.C = canvas
+        self.device = torch.device(device)
+        self.dtype = cfg.dtype
+        self._keep: List[torch.Tensor] = []
+        c = abi.dlm_config(
+            n_layers=cfg.n_layers, d_model=cfg.d_model, n_q_heads=cfg.n_q_heads,
+            n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, vocab=cfg.vocab,
+            mask_id=cfg.mask_id, ffn=abi.DLM_FFN_MOE if cfg.ffn == "moe" else abi.DLM_FFN_DENSE,
+            d_ffn=cfg.d_ffn, n_experts=cfg.n_experts, top_k=cfg.top_k, d_expert=cfg.d_expert,
+            dtype=_DTYPES[cfg.dtype], canvas=canvas, rms_eps=cfg.rms_eps,
+            rope_base=cfg.rope_base)
+        self.raw_cfg = c
+        W = self._pack(cfg, weights)
+        self._layers = (abi.dlm_layer_weights * cfg.n_layers)(*W["layers"])
+        w = abi.dlm_weights(embed=W["embed"], final_norm=W["final_norm"], lm_head=W["lm_head"],
+                            lm_head_s=W["lm_head_s"],
+                            layers=ctypes.cast(self._layers, ctypes.POINTER(abi.dlm_layer_weights)))
+        h = ctypes.c_void_p()
+        check(self.lib.dlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)), "dlm_create")
+        self.handle = h
+        self.kv_dtype = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+    # ------------------------------------------------------------ weights --
+    def _dev(self, t: torch.Tensor) -> torch.Tensor:
+        t = t.to(self.device).contiguous()
+        self._keep.append(t)
+        return t
+
+    def _proj(self, weights, name, cat: Sequence[str] = ()):
+        """(codes-or-values pointer, scale pointer) of a projection; `cat`
+        concatenates several along the output dimension."""
+        names = list(cat) or [name]
+        if self.dtype == "fp8":
+            q = torch.cat([weights[n + ".q"] for n in names], dim=-2) if len(names) > 1 else weights[name + ".q"]
+            s = torch.cat([weights[n + ".s"] for n in names], dim=-1) if len(names) > 1 else weights[name + ".s"]
+            return _ptr(self._dev(q)), _ptr(self._dev(s.float()))
+        w = torch.cat([weights[n] for n in names], dim=-2) if len(names) > 1 else weights[name]
+        return _ptr(self._dev(w)), None
+
+    def _pack(self, cfg, weights):
+        W = {"embed": _ptr(self._dev(weights["embed"])),
+             "final_norm": _ptr(self._dev(weights["final_norm"].float()))}
+        W["lm_head"], W["lm_head_s"] = self._proj(weights, "lm_head")
+        layers = []
+        for l in range(cfg.n_layers):
+            p = f"{l}."
+            L = abi.dlm_layer_weights()
+            L.attn_norm = _ptr(self._dev(weights[p + "attn_norm"].float()))
+            L.ffn_norm = _ptr(self._dev(weights[p + "ffn_norm"].float()))
+            L.wqkv, L.wqkv_s = self._proj(weights, p + "wqkv", cat=(p + "wq", p + "wk", p + "wv"))
+            L.wo, L.wo_s = self._proj(weights, p + "wo")
+            L.w_gate, L.w_gate_s = self._proj(weights, p + "w_gate")
+            L.w_up, L.w_up_s = self._proj(weights, p + "w_up")
+            L.w_down, L.w_down_s = self._proj(weights, p + "w_down")
+            if cfg.ffn == "moe":
+                L.w_router = _ptr(self._dev(weights[p + "w_router"]))
+                L.we_gate, L.we_gate_s = self._proj(weights, p + "we_gate")
+                L.we_up, L.we_up_s = self._proj(weights, p + "we_up")
+                L.we_down, L.we_down_s = self._proj(weights, p + "we_down")
+            layers.append(L)
+        W["layers"] = layers
+        return W
+
+    # -------------------------------------------------------------- state --
+    def new_seq(self, capacity: int) -> Seq:
+        c = self.cfg
+        kv = torch.empty((c.n_layers, 2, c.n_kv_heads, capacity, c.head_dim), dtype=self.kv_dtype,
+                         device=self.device)
+        canvas = torch.full((self.C,), c.mask_id, dtype=torch.int32, device=self.device)
+        raw = abi.dlm_seq(kv=kv.data_ptr(), capacity=capacity, T=0, canvas=canvas.data_ptr(),
+                          page_table=None, page_size=0)
+        return Seq(kv, canvas, raw)
+
+    def workspace_bytes(self, max_rows: int, max_kv: int) -> int:
+        return int(self.lib.dlm_workspace_bytes(self.handle, max_rows, max_kv))
+
+    def workspace(self, max_rows: int, max_kv: int) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(max_rows, max_kv), dtype=torch.uint8, device=self.device)
+
+    @staticmethod
+    def _seq_array(seqs: Sequence[Seq]):
+        arr = (ctypes.POINTER(abi.dlm_seq) * len(seqs))(*[ctypes.pointer(s.raw) for s in seqs])
+        return arr
+
+    # --------------------------------------------------------- operations --
+    def dlm_prefill(self, seq: Seq, ids: torch.Tensor, ws: torch.Tensor) -> None:
+        assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.device.type == "cuda"
+        check(self.lib.dlm_prefill(self.handle, ctypes.byref(seq.raw), ids.data_ptr(), ids.numel(),
+                                   ws.data_ptr(), ws.numel(), _stream()), "dlm_prefill")
+
+    def dlm_denoise_step(self, seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor,
+                         ws: torch.Tensor, logits: Optional[torch.Tensor] = None) -> None:
+        n = len(seqs)
+        assert conf.dtype == torch.float32 and conf.numel() >= n * self.C
+        assert pred.dtype == torch.int32 and pred.numel() >= n * self.C
+        if logits is not None:
+            assert logits.dtype == torch.float32 and logits.numel() >= n * self.C * self.cfg.vocab
+        arr = self._seq_array(seqs)
+        check(self.lib.dlm_denoise_step(self.handle, arr, n, conf.data_ptr(), pred.data_ptr(),
+                                        _ptr(logits), ws.data_ptr(), ws.numel(), _stream()),
+              "dlm_denoise_step")
+
+    def dlm_commit(self, seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor, rule: "Rule",
+                   step: int, n_committed: Optional[torch.Tensor] = None,
+                   n_masked: Optional[torch.Tensor] = None) -> None:
+        arr = self._seq_array(seqs)
+        check(self.lib.dlm_commit(self.handle, arr, len(seqs), conf.data_ptr(), pred.data_ptr(),
+                                  ctypes.byref(rule.raw), step, _ptr(n_committed), _ptr(n_masked),
+                                  _stream()), "dlm_commit")
+
+    def dlm_append_canvas(self, seqs: Sequence[Seq], ws: torch.Tensor) -> None:
+        arr = self._seq_array(seqs)
+        check(self.lib.dlm_append_canvas(self.handle, arr, len(seqs), ws.data_ptr(), ws.numel(),
+                                         _stream()), "dlm_append_canvas")
+
+    def dlm_check_device_status(self) -> int:
+        bits = ctypes.c_int32(0)
+        st = self.lib.dlm_check_device_status(self.handle, _stream(), ctypes.byref(bits))
+        if st not in (abi.DLM_OK, abi.DLM_E_DEVICE):
+            check(st, "dlm_check_device_status")
+        return bits.value
+
+    def dlm_debug_router(self, out: Optional[torch.Tensor]) -> None:
+        """Test hook: record each layer's router choices into `out` (int32)."""
+        check(self.lib.dlm_debug_router(self.handle, _ptr(out), 0 if out is None else out.numel()),
+              "dlm_debug_router")
+
+    # ------------------------------------------------------------- timing --
+    def timing_enable(self, kernel_ids: Sequence[int]) -> None:
+        mask = 0
+        for k in kernel_ids:
+            mask |= 1 << k
+        check(self.lib.dlm_timing_enable(self.handle, mask), "dlm_timing_enable")
+
+    def timing_read(self) -> Dict[str, tuple]:
+        ms = (ctypes.c_float * abi.DLM_K_COUNT)()
+        n = (ctypes.c_int32 * abi.DLM_K_COUNT)()
+        check(self.lib.dlm_timing_read(self.handle, ms, n), "dlm_timing_read")
+        return {self.lib.dlm_kernel_name(i).decode(): (ms[i], n[i])
+                for i in range(abi.DLM_K_COUNT) if n[i]}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            self.lib.dlm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Rule:
+    """A commit rule (top-k schedule or confidence threshold) in ABI form."""
+
+    def __init__(self, kind: str, n_steps: int, k_per_step: Optional[Sequence[int]] = None,
+                 threshold: float = 0.5):
+        self.kind, self.n_steps = kind, n_steps
+        self._k = (ctypes.c_int32 * n_steps)(*(k_per_step or [0] * n_steps))
+        self.raw = abi.dlm_commit_rule(
+            kind=abi.DLM_COMMIT_TOPK if kind == "topk" else abi.DLM_COMMIT_THRESHOLD,
+            n_steps=n_steps, k_per_step=ctypes.cast(self._k, ctypes.POINTER(ctypes.c_int32)),
+            threshold=threshold)
+
+    @staticmethod
+    def topk(canvas: int, n_steps: int) -> "Rule":
+        """Commit C // S per step, one more on the first C % S steps."""
+        base, extra = divmod(canvas, n_steps)
+        return Rule("topk", n_steps, [base + (1 if s < extra else 0) for s in range(n_steps)])
+
+    @staticmethod
+    def threshold(n_steps: int, thr: float) -> "Rule":
+        return Rule("threshold", n_steps, None, thr)
+
+
+def generate(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], rule: Rule,
+             n_canvases: int, ws: torch.Tensor, on_step=None):
+    """Prefill each request, then for each canvas: reset to [MASK], denoise and
+    commit until the schedule ends (for the threshold rule, until nothing is
+    masked in any request), append.  Returns the finished canvases
+    [n_canvases][n_seqs, C] (device int32) and the steps run per canvas."""
+    n = len(seqs)
+    C = model.C
+    for s, ids in zip(seqs, prefixes):
+        model.dlm_prefill(s, ids, ws)
+    conf = torch.empty(n * C, dtype=torch.float32, device=model.device)
+    pred = torch.empty(n * C, dtype=torch.int32, device=model.device)
+    n_masked = torch.empty(n, dtype=torch.int32, device=model.device)
+    outs, steps = [], []
+    for ci in range(n_canvases):
+        for s in seqs:
+            s.canvas.fill_(model.cfg.mask_id)
+        st = 0
+        for st in range(rule.n_steps):
+            model.dlm_denoise_step(seqs, conf, pred, ws)
+            model.dlm_commit(seqs, conf, pred, rule, st, None, n_masked)
+            if on_step is not None:
+                on_step(ci, st, conf, pred)
+            if rule.kind == "threshold" and int(n_masked.cpu().max()) == 0:
+                break
+        steps.append(st + 1)
+        outs.append(torch.stack([s.canvas.clone() for s in seqs]))
+        model.dlm_append_canvas(seqs, ws)
+    return outs, steps

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import masked_block_diffusion_amd.abi as abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlm.h")
+
+
+def _lib():
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.skip("libdlm.so not built")
+    return abi.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dlm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dlm_\w+)", out))
+    missing = set(header_functions()) - exported
+    assert not missing, f"not exported: {sorted(missing)}"
+
+
+def test_struct_sizes_match_the_c_layout():
+    # 16 int/float fields; 19 pointers; 4 pointers + a pointer; seq: p, i, i, p, p, i (+pad)
+    assert ctypes.sizeof(abi.dlm_config) == 16 * 4
+    assert ctypes.sizeof(abi.dlm_layer_weights) == 19 * 8
+    assert ctypes.sizeof(abi.dlm_weights) == 5 * 8
+    assert ctypes.sizeof(abi.dlm_seq) == 8 + 4 + 4 + 8 + 8 + 8
+    assert ctypes.sizeof(abi.dlm_commit_rule) == 4 + 4 + 8 + 8
+
+
+def _cfg(**kw):
+    c = dict(n_layers=2, d_model=128, n_q_heads=4, n_kv_heads=4, head_dim=32, vocab=512,
+             mask_id=511, ffn=abi.DLM_FFN_DENSE, d_ffn=512, n_experts=0, top_k=0, d_expert=0,
+             dtype=abi.DLM_F32, canvas=32, rms_eps=1e-6, rope_base=10000.0)
+    c.update(kw)
+    return abi.dlm_config(**c)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), abi.DLM_E_SHAPE),
+    (dict(n_q_heads=6, n_kv_heads=4), abi.DLM_E_SHAPE),
+    (dict(mask_id=512), abi.DLM_E_ARG),
+    (dict(mask_id=-1), abi.DLM_E_ARG),
+    (dict(dtype=7), abi.DLM_E_DTYPE),
+    (dict(ffn=3), abi.DLM_E_ARG),
+    (dict(canvas=0), abi.DLM_E_SHAPE),
+    (dict(canvas=2048), abi.DLM_E_SHAPE),
+    (dict(d_model=98), abi.DLM_E_SHAPE),            # 392 bytes: not a multiple of 16
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=300, top_k=8, d_expert=64), abi.DLM_E_SHAPE),
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=9, d_expert=64), abi.DLM_E_SHAPE),
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=64, top_k=17, d_expert=64), abi.DLM_E_SHAPE),
+    (dict(n_layers=0), abi.DLM_E_SHAPE),
+])
+def test_create_rejects_bad_config(kw, status):
+    lib = _lib()
+    c = _cfg(**kw)
+    h = ctypes.c_void_p()
+    w = abi.dlm_weights()
+    assert lib.dlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == status
+    assert h.value is None
+    assert lib.dlm_last_error().decode()
+
+
+def test_create_rejects_missing_weights():
+    lib = _lib()
+    c = _cfg()
+    h = ctypes.c_void_p()
+    assert lib.dlm_create(ctypes.byref(c), None, ctypes.byref(h)) == abi.DLM_E_ARG
+    w = abi.dlm_weights()                           # all NULL
+    assert lib.dlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == abi.DLM_E_ARG
+    # fp8 without scales
+    layers = (abi.dlm_layer_weights * 2)()
+    for L in layers:
+        for f, _ in abi.dlm_layer_weights._fields_:
+            if not f.endswith("_s") and f not in ("w_router", "we_gate", "we_up", "we_down"):
+                setattr(L, f, 0x1000)
+    w = abi.dlm_weights(embed=0x1000, final_norm=0x1000, lm_head=0x1000, lm_head_s=0x1000,
+                        layers=ctypes.cast(layers, ctypes.POINTER(abi.dlm_layer_weights)))
+    c8 = _cfg(dtype=abi.DLM_FP8)
+    assert lib.dlm_create(ctypes.byref(c8), ctypes.byref(w), ctypes.byref(h)) == abi.DLM_E_DTYPE
+    assert "scale" in lib.dlm_last_error().decode()
+
+
+def test_calls_on_null_model_fail_cleanly():
+    lib = _lib()
+    assert lib.dlm_workspace_bytes(None, 32, 96) == 0
+    seq = abi.dlm_seq()
+    assert lib.dlm_prefill(None, ctypes.byref(seq), None, 4, None, 0, None) == abi.DLM_E_ARG
+    arr = (ctypes.POINTER(abi.dlm_seq) * 1)(ctypes.pointer(seq))
+    assert lib.dlm_denoise_step(None, arr, 1, None, None, None, None, 0, None) == abi.DLM_E_ARG
+    assert lib.dlm_append_canvas(None, arr, 1, None, 0, None) == abi.DLM_E_ARG
+    rule = abi.dlm_commit_rule()
+    assert lib.dlm_commit(None, arr, 1, None, None, ctypes.byref(rule), 0, None, None, None) == abi.DLM_E_ARG
+    assert lib.dlm_check_device_status(None, None, None) == abi.DLM_E_ARG
+    assert lib.dlm_timing_enable(None, 1) == abi.DLM_E_ARG
+    assert lib.dlm_debug_router(None, None, 0) == abi.DLM_E_ARG
+    lib.dlm_destroy(None)                           # no-op
+
+
+def test_kernel_names():
+    lib = _lib()
+    names = [lib.dlm_kernel_name(i).decode() for i in range(abi.DLM_K_COUNT)]
+    assert all(names) and len(set(names)) == abi.DLM_K_COUNT
+    assert lib.dlm_kernel_name(abi.DLM_K_COUNT).decode() == ""
+    assert names[abi.DLM_K_LM_HEAD] == "lm_head"
