@@ -234,11 +234,20 @@ dlm_status dlm_check_device_status(dlm_model* model, void* stream, int32_t* bits
 /* Description of the last failure on the calling thread ("" if none). */
 const char* dlm_last_error(void);
 
-/* Test hook for MoE models: while `router_ids` (device int32, nullable) is set,
- * every forward also writes each layer's selected experts there, laid out
- * [n_layers][rows][top_k] in selection order (rows = tokens of the forward).
- * E_CAPACITY at the forward if n_layers * rows * top_k > capacity_entries. */
-dlm_status dlm_debug_router(dlm_model* model, int32_t* router_ids, int64_t capacity_entries);
+/* Test hook for MoE models.  While set, every forward also writes, for each
+ * layer and each token row of the forward (device, nullable each):
+ *   router_ids    int32 [n_layers][rows][top_k], the experts in selection order;
+ *   router_logits fp32  [n_layers][rows][n_experts], the router logits.
+ * capacity_rows: (layer, row) pairs the buffers hold; a forward needing more
+ * (n_layers * rows) fails with E_CAPACITY before enqueuing anything. */
+dlm_status dlm_debug_router(dlm_model* model, int32_t* router_ids, float* router_logits, int64_t capacity_rows);
+
+/* Test hook: the per-token activation quantiser the fp8 models apply to every
+ * GEMM A-operand.  x: device bf16 [rows, d]; q: device uint8 [rows, d] OCP
+ * E4M3FN codes (out); s: device fp32 [rows] (out).  Per row: s = amax / 448
+ * (1 for an all-zero row), q = nearest E4M3 value of x / s, ties to even,
+ * saturating at +-448.  E_ARG on null pointers or rows / d < 1. */
+dlm_status dlm_op_quant_rows(const void* x, int32_t rows, int32_t d, void* q, float* s, void* stream);
 
 /* Kernel timing.  `kernel_mask` bit i enables timing of kernel id i (0 = off):
  * every launch of a timed kernel is bracketed by HIP events on its stream.

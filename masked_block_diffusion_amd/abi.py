@@ -51,6 +51,7 @@ EXPORTS = [
     "dlm_create", "dlm_destroy", "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
     "dlm_commit", "dlm_append_canvas", "dlm_check_device_status", "dlm_last_error",
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
+    "dlm_op_quant_rows",
 ]
 
 
@@ -126,7 +127,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_timing_enable": (c_int32, [P, c_int32]),
         "dlm_timing_read": (c_int32, [P, POINTER(c_float), POINTER(c_int32)]),
         "dlm_kernel_name": (c_char_p, [c_int32]),
-        "dlm_debug_router": (c_int32, [P, P, ctypes.c_int64]),
+        "dlm_debug_router": (c_int32, [P, P, P, ctypes.c_int64]),
+        "dlm_op_quant_rows": (c_int32, [P, c_int32, c_int32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -14,7 +14,8 @@
 //     online softmax are per-lane scalars, and the probabilities P^T are
 //     already laid out as the B operand of O^T = V^T P^T (the K order inside
 //     one MFMA is a permutation shared by both operands).  V is staged
-//     transposed in LDS so the A operand reads are 8-byte vectors.
+//     transposed in LDS so the A operand reads are 8-byte vectors.  P is fed
+//     as two bf16 terms (hi + lo), so P V carries fp32-level precision.
 //   * Long key ranges are split across workgroups (split-KV); partial (max,
 //     sum, unnormalised O) are merged by a second kernel in fixed split order.
 // fp32 kernel (fp32 models): one thread per (query, head), online softmax,
@@ -188,7 +189,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         l_run *= alpha;
 #pragma unroll
         for (int d = 0; d < ND; ++d) o[d] *= alpha;
-        bf16_t pb[4][4];
+        // P = hi + lo, both bf16: the product with V is then exact to ~2^-16
+        // relative instead of bf16's 2^-9 (two MFMAs per step).
+        bf16_t pb[4][4], pl[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -196,16 +199,20 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
                 const float p = (st[u][v] == -INFINITY) ? 0.f : exp2f(st[u][v] - m_new);
                 l_run += p;
                 pb[u][v] = f32_to_bf16(p);
+                pl[u][v] = f32_to_bf16(p - bf16_to_f32(pb[u][v]));
             }
         // O^T += V^T P^T over two 32-key MFMA steps
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            bf16x8 pf;
+            bf16x8 pf, pf_lo;
             uint16_t* pu = (uint16_t*)&pf;
+            uint16_t* pv = (uint16_t*)&pf_lo;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 pu[v] = pb[2 * h2][v];
                 pu[4 + v] = pb[2 * h2 + 1][v];
+                pv[v] = pl[2 * h2][v];
+                pv[4 + v] = pl[2 * h2 + 1][v];
             }
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
@@ -216,6 +223,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
                 ((uint64_t*)&vf)[0] = lo;
                 ((uint64_t*)&vf)[1] = hi;
                 o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf_lo, o[d], 0, 0, 0);
             }
         }
     }

@@ -49,7 +49,8 @@ struct dlm_model {
     int* d_err = nullptr;
     int device = 0;
     int32_t* dbg_router = nullptr;   // test hook: per-layer router choices
-    int64_t dbg_cap = 0;
+    float* dbg_router_logits = nullptr;
+    int64_t dbg_cap = 0;             // (layer, row) pairs the hook buffers hold
     // timing
     uint32_t timing_mask = 0;
     struct Ev { hipEvent_t a, b; int id; };
@@ -91,8 +92,29 @@ struct Timed {
 
 struct Plan {
     size_t x, hA, hb, hq, hs, qkv, q, ao, aoq, aos, fi, fiq, fis, rl, tid, tw, offs, tstart, sorted, inv,
-        hist, lrank, ei, eiq, eis, y, pmax, psum, pidx, opart, mlpart, total;
+        hist, lrank, ei, eiq, eis, y, pmax, psum, pidx, opart, mlpart, splitk, total;
+    long splitk_floats;
 };
+
+// Largest split-K partial space any dense GEMM of a forward over `rows` rows uses.
+long splitk_need(const dlm_config& c, int rows) {
+    const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
+    const int nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+    auto need = [&](int dtype, int epi, int N, int K) {
+        GemmDesc g;
+        g.dtype = dtype; g.epi = epi; g.out_f32 = c.dtype == DLM_F32;
+        g.M = rows; g.N = N; g.K = K;
+        return gemm_splitk_floats(g);
+    };
+    long m = 0;
+    m = std::max(m, need(c.dtype, GEMM_STORE_F32, nqkv, d));
+    m = std::max(m, need(c.dtype, GEMM_ADD_F32, d, qd));
+    m = std::max(m, need(c.dtype, GEMM_SWIGLU, c.d_ffn, d));
+    m = std::max(m, need(c.dtype, GEMM_ADD_F32, d, c.d_ffn));
+    if (c.ffn == DLM_FFN_MOE)
+        m = std::max(m, need(c.dtype == DLM_F32 ? DT_F32 : DT_BF16, GEMM_STORE_F32, c.n_experts, d));
+    return m;
+}
 
 Plan plan(const dlm_config& c, int rows, int max_kv) {
     (void)max_kv;
@@ -144,6 +166,8 @@ Plan plan(const dlm_config& c, int rows, int max_kv) {
     const size_t af = attention_work_floats(rows, c.n_q_heads, c.head_dim);
     p.opart = take(af / (c.head_dim + 2) * c.head_dim * 4);
     p.mlpart = take(af / (c.head_dim + 2) * 2 * 4);
+    p.splitk_floats = splitk_need(c, rows);
+    p.splitk = take(std::max(1L, p.splitk_floats) * 4);
     p.total = off;
     return p;
 }
@@ -169,7 +193,7 @@ dlm_status check_config(const dlm_config* c) {
     const int kdims[4] = {c->d_model, c->n_q_heads * c->head_dim, c->d_ffn,
                           c->ffn == DLM_FFN_MOE ? c->d_expert : c->d_model};
     for (int k : kdims)
-        if ((k * eb) % 16) return fail(DLM_E_SHAPE, "GEMM inner dimension %d is not a multiple of 16 bytes", k);
+        if ((k * eb) % 128) return fail(DLM_E_SHAPE, "GEMM inner dimension %d is not a multiple of 128 bytes", k);
     if (c->ffn == DLM_FFN_MOE) {
         if (c->n_experts < 1 || c->n_experts > 256) return fail(DLM_E_SHAPE, "n_experts not in [1, 256]");
         if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts)
@@ -213,10 +237,10 @@ dlm_status check_seq(const dlm_model* m, const dlm_seq* s, int extra, bool need_
 }
 
 dlm_status check_ws(const dlm_model* m, void* ws, size_t ws_bytes, int rows, int max_kv) {
-    if (m->dbg_router && m->cfg.ffn == DLM_FFN_MOE &&
-        (int64_t)m->cfg.n_layers * rows * m->cfg.top_k > m->dbg_cap)
-        return fail(DLM_E_CAPACITY, "router debug buffer holds %lld entries, the forward needs %lld",
-                    (long long)m->dbg_cap, (long long)m->cfg.n_layers * rows * m->cfg.top_k);
+    if ((m->dbg_router || m->dbg_router_logits) && m->cfg.ffn == DLM_FFN_MOE &&
+        (int64_t)m->cfg.n_layers * rows > m->dbg_cap)
+        return fail(DLM_E_CAPACITY, "router debug buffers hold %lld (layer, row) pairs, the forward needs %lld",
+                    (long long)m->dbg_cap, (long long)m->cfg.n_layers * rows);
     const size_t need = plan(m->cfg, rows, max_kv).total;
     if (!ws) return fail(DLM_E_WORKSPACE, "workspace is NULL");
     if (ws_bytes < need) return fail(DLM_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -270,6 +294,11 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
         rmsnorm(x, g, R, d, c.rms_eps, f32 ? (float*)hA : nullptr, f32 ? nullptr : (uint16_t*)hA, hq, hs, st);
     };
     auto opA = [&](const void* bf, const void* q8) { return fp8 ? q8 : bf; };
+    auto dense = [&](int id, GemmDesc g) {
+        g.splitk = at<float>(ws, p.splitk);
+        g.splitk_floats = p.splitk_floats;
+        run_gemm(m, id, g, st);
+    };
     auto quant = [&](const void* src, int rows, int cols, uint8_t* qd8, float* sc) {
         if (!fp8) return;
         Timed t(m, DLM_K_QUANT, st);
@@ -286,7 +315,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.B = L.wqkv; g.ldb = d; g.b_scale = L.wqkv_s;
             g.M = R; g.N = nqkv; g.K = d;
             g.C = qkv; g.ldc = nqkv;
-            run_gemm(m, DLM_K_GEMM_QKV, g, st);
+            dense(DLM_K_GEMM_QKV, g);
         }
         {
             Timed t(m, DLM_K_ROPE_KV, st);
@@ -306,7 +335,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.B = L.wo; g.ldb = qd; g.b_scale = L.wo_s;
             g.M = R; g.N = d; g.K = qd;
             g.C = x; g.ldc = d;
-            run_gemm(m, DLM_K_GEMM_O, g, st);
+            dense(DLM_K_GEMM_O, g);
         }
         norm(L.ffn_norm);
         if (c.ffn == DLM_FFN_MOE) {
@@ -323,11 +352,12 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                 g.dtype = f32 ? DT_F32 : DT_BF16; g.epi = GEMM_STORE_F32;
                 g.A = hA; g.lda = d; g.B = L.w_router; g.ldb = d;
                 g.M = R; g.N = E; g.K = d; g.C = rl; g.ldc = E;
-                run_gemm(m, DLM_K_ROUTER, g, st);
+                dense(DLM_K_ROUTER, g);
             }
             {
                 Timed t(m, DLM_K_TOPK, st);
-                router_topk(rl, R, E, k, tid, tw, m->dbg_router ? m->dbg_router + (long)l * R * k : nullptr, st);
+                router_topk(rl, R, E, k, tid, tw, m->dbg_router ? m->dbg_router + (long)l * R * k : nullptr,
+                            m->dbg_router_logits ? m->dbg_router_logits + (long)l * R * E : nullptr, st);
             }
             {
                 Timed t(m, DLM_K_PERMUTE, st);
@@ -371,7 +401,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
             g.B = L.w_gate; g.B2 = L.w_up; g.ldb = d; g.b_scale = L.w_gate_s; g.b2_scale = L.w_up_s;
             g.M = R; g.N = c.d_ffn; g.K = d; g.C = fi; g.ldc = c.d_ffn;
-            run_gemm(m, DLM_K_GEMM_GATE_UP, g, st);
+            dense(DLM_K_GEMM_GATE_UP, g);
         }
         quant(fi, R, c.d_ffn, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr, fp8 ? at<float>(ws, p.fis) : nullptr);
         {
@@ -381,7 +411,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
             g.B = L.w_down; g.ldb = c.d_ffn; g.b_scale = L.w_down_s;
             g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
-            run_gemm(m, DLM_K_GEMM_DOWN, g, st);
+            dense(DLM_K_GEMM_DOWN, g);
         }
     }
     if (mode != DENOISE) return;
@@ -399,7 +429,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
         g.M = R; g.N = c.vocab; g.K = d;
         g.pmax = pmax; g.psum = psum; g.pidx = pidx; g.mask_col = c.mask_id;
         g.logits = logits; g.ld_logits = c.vocab;
-        run_gemm(m, DLM_K_LM_HEAD, g, st);
+        dense(DLM_K_LM_HEAD, g);
     }
     {
         Timed t(m, DLM_K_LM_MERGE, st);
@@ -592,12 +622,21 @@ dlm_status dlm_check_device_status(dlm_model* m, void* stream, int32_t* bits) {
     return DLM_OK;
 }
 
-dlm_status dlm_debug_router(dlm_model* m, int32_t* router_ids, int64_t capacity_entries) {
+dlm_status dlm_op_quant_rows(const void* x, int32_t rows, int32_t d, void* q, float* s, void* stream) {
+    g_err.clear();
+    if (!x || !q || !s) return fail(DLM_E_ARG, "null pointer");
+    if (rows < 1 || d < 1) return fail(DLM_E_ARG, "rows and d must be >= 1");
+    quant_rows((const uint16_t*)x, rows, d, (uint8_t*)q, s, (hipStream_t)stream);
+    return hip_status("dlm_op_quant_rows");
+}
+
+dlm_status dlm_debug_router(dlm_model* m, int32_t* router_ids, float* router_logits, int64_t capacity_rows) {
     g_err.clear();
     if (!m) return fail(DLM_E_ARG, "model is NULL");
-    if (router_ids && capacity_entries < 0) return fail(DLM_E_ARG, "negative capacity");
+    if ((router_ids || router_logits) && capacity_rows < 0) return fail(DLM_E_ARG, "negative capacity");
     m->dbg_router = router_ids;
-    m->dbg_cap = router_ids ? capacity_entries : 0;
+    m->dbg_router_logits = router_logits;
+    m->dbg_cap = (router_ids || router_logits) ? capacity_rows : 0;
     return DLM_OK;
 }
 

@@ -7,14 +7,26 @@
 // A grouped variant runs one GEMM per expert over the token rows routed to it,
 // gathering A rows through the permutation.
 //
-// Tiling: a 256-thread workgroup (4 waves) owns a BM x BN output tile; A and B
-// K-tiles of 128 bytes per row are staged through LDS (double-buffered, the next
-// tile prefetched into registers while the current one feeds the MFMAs).  Each
-// wave owns a (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA blocks.  The workgroup
-// order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so the
-// linear tile index is remapped to give each XCD a contiguous range of
-// (n-tile, m-tile) pairs, n-major, so that the m-tiles reading one weight tile
-// run together on one XCD and share its L2.
+// Data movement.  A 256-thread workgroup (4 waves) owns a BM x BN output tile.
+// K advances in stages of 128 bytes per row; each stage (the A rows, then the B
+// rows, then for SwiGLU the second weight's rows) is copied global -> LDS by
+// global_load_lds_dwordx4, which writes each wave's 64 x 16 bytes straight into
+// LDS without passing through registers.  NS stages are in flight at once (an
+// LDS ring), so the weight stream keeps several tens of KB outstanding per CU
+// -- what HBM latency needs at 8 TB/s.  One barrier per stage: wait for the
+// stage's loads, barrier, refill the slot the previous stage used, then run the
+// stage's MFMAs.  The 16-byte chunks of a row are XOR-swizzled by (row & 7) so
+// the fragment reads of 16 consecutive rows spread over the LDS banks.
+//
+// Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
+// the linear tile index is remapped to give each XCD a contiguous range, in an
+// order where the m-tiles reading one weight K-slice are adjacent (one L2).
+//
+// Weight-streaming shapes (a 256-row canvas against a 2048-wide projection)
+// have too few output tiles for 256 CUs, so K is split across workgroups.
+// Partial tiles go to the workspace with plain stores and a second kernel sums
+// them in split order and applies the epilogue: deterministic, and no
+// device-scope fences (which on this chip write back and invalidate L2).
 #include "common.h"
 #include "kernels.h"
 
@@ -22,45 +34,77 @@ namespace dlm {
 
 enum Epi { EPI_F32 = 0, EPI_BF16, EPI_ADD_F32, EPI_SWIGLU_BF16, EPI_SWIGLU_F32, EPI_LMHEAD };
 
-constexpr int BKB = 128;             // K bytes per pipeline stage
-constexpr int LDS_ROW = BKB + 16;    // padded LDS row (bytes)
+constexpr int BKB = 128;             // K bytes per stage row
 
-template <int BM, int BN, bool DUAL>
-struct Smem {
-    static constexpr int A = BM * LDS_ROW;
-    static constexpr int B = BN * LDS_ROW;
-    static constexpr int STAGE = A + B * (DUAL ? 2 : 1);
-    static constexpr int BYTES = 2 * STAGE;
-};
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Per-thread 16-byte chunks of a tile with R rows: chunk c = tid + 256 j covers
-// row c / 8, bytes (c % 8) * 16.
-template <int R> struct Chunks { static constexpr int N = (R * 8 + 255) / 256; };
+// s_waitcnt on vector-memory operations only: vmcnt <= N (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
 
-struct TileRows {
-    // Address of each chunk row (or null when the row is outside the matrix).
-    const uint8_t* p;
-};
+// Workgroup barrier for the LDS ring.  __syncthreads() would add a release
+// fence that drains every outstanding LDS-DMA load (all stages in flight);
+// here each wave has already waited for the stage it needs (wait_stages), so
+// the barrier only has to order LDS reads: lgkmcnt(0), s_barrier, and a
+// compiler memory clobber so no LDS access moves across it.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("s_barrier" ::: "memory");
+}
 
-template <typename T, int BM, int BN, int WM, int WN, bool DUAL>
+// Wait until at most p stages (of LPW loads each) are still outstanding.
+template <int LPW, int P>
+__device__ __forceinline__ void wait_stages(int p) {
+    if constexpr (P <= 0) {
+        wait_vm<0>();
+    } else {
+        if (p >= P) wait_vm<P * LPW>();
+        else wait_stages<LPW, P - 1>(p);
+    }
+}
+
+template <typename T, int BM_, int BN_, int WM_, int WN_, bool DUAL, int NS>
 struct Core {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr bool TWO_B = DUAL;
     static constexpr int TM = BM / WM / 16;
     static constexpr int TN = BN / WN / 16;
     static constexpr int KSB = Mfma<T>::KSTEP * (int)sizeof(T);   // bytes per MFMA k-step
     static constexpr int LB = Mfma<T>::LANE_BYTES;
-    static constexpr int AC = Chunks<BM>::N;
-    static constexpr int BC = Chunks<BN>::N;
+    static constexpr int ROWS = BM + BN * (DUAL ? 2 : 1);           // rows per stage
+    static constexpr int STAGE = ROWS * BKB;
+    static constexpr int LDS_BYTES = NS * STAGE;
+    static constexpr int LPW = ROWS / 32;                           // 1-KB loads per wave per stage
+    static constexpr int PART = TM * TN * 4;
     typedef typename Mfma<T>::frag frag;
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile");
     static_assert(WM * WN == 4, "4 waves");
+    static_assert(ROWS % 32 == 0, "stage rows");
+    static_assert((NS - 2) * LPW < 64, "vmcnt");
 
-    const uint8_t* arow[AC];
-    const uint8_t* brow[BC];
-    const uint8_t* b2row[BC];
-    u32x4 ra[AC], rb[BC], rb2[BC];
+    const uint8_t* src[LPW];     // this lane's source (row + swizzled chunk) per load
     f32x4 acc[TM][TN];
     f32x4 acc2[DUAL ? TM : 1][DUAL ? TN : 1];
-    long kbytes;
+    int wave;
+
+    // rowptr(R) -> address of stage row R (A rows, then B, then B2), always a
+    // readable row (rows outside the matrix are clamped by the caller: they
+    // only feed outputs that are not stored).
+    template <class F>
+    __device__ __forceinline__ void init(F rowptr) {
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+        const int lane = threadIdx.x % WAVE;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int R = (wave * LPW + j) * 8 + lane / 8;
+            const int chunk = (lane % 8) ^ (R & 7);
+            src[j] = rowptr(R) + chunk * 16;
+        }
+    }
 
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -72,58 +116,29 @@ struct Core {
             }
     }
 
-    __device__ __forceinline__ void load(int kt) {
-        const int tid = threadIdx.x;
-        const long kb = (long)kt * BKB + (tid % 8) * 16;
-        const bool kin = kb < kbytes;
+    __device__ __forceinline__ void load_stage(uint8_t* smem, int kt, int slot) {
+        uint8_t* dst = smem + slot * STAGE + wave * LPW * 1024;
 #pragma unroll
-        for (int j = 0; j < AC; ++j) {
-            const uint8_t* p = arow[j];
-            ra[j] = (p && kin) ? *(const u32x4*)(p + kb) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int j = 0; j < BC; ++j) {
-            const uint8_t* p = brow[j];
-            rb[j] = (p && kin) ? __builtin_nontemporal_load((const u32x4*)(p + kb)) : u32x4{0, 0, 0, 0};
-            if constexpr (DUAL) {
-                const uint8_t* p2 = b2row[j];
-                rb2[j] = (p2 && kin) ? __builtin_nontemporal_load((const u32x4*)(p2 + kb)) : u32x4{0, 0, 0, 0};
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(uint8_t* stage) {
-        const int tid = threadIdx.x;
-        uint8_t* sa = stage;
-        uint8_t* sb = stage + Smem<BM, BN, DUAL>::A;
-        uint8_t* sb2 = sb + Smem<BM, BN, DUAL>::B;
-#pragma unroll
-        for (int j = 0; j < AC; ++j) {
-            const int c = tid + 256 * j;
-            if (c < BM * 8) *(u32x4*)(sa + (c / 8) * LDS_ROW + (c % 8) * 16) = ra[j];
-        }
-#pragma unroll
-        for (int j = 0; j < BC; ++j) {
-            const int c = tid + 256 * j;
-            if (c < BN * 8) {
-                *(u32x4*)(sb + (c / 8) * LDS_ROW + (c % 8) * 16) = rb[j];
-                if constexpr (DUAL) *(u32x4*)(sb2 + (c / 8) * LDS_ROW + (c % 8) * 16) = rb2[j];
-            }
-        }
+        for (int j = 0; j < LPW; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long)kt * BKB), (lds_ptr)(dst + j * 1024), 16,
+                                             0, 0);
     }
 
     __device__ __forceinline__ void compute(const uint8_t* stage) {
-        const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
+        const int lane = threadIdx.x % WAVE;
         const int wm = wave / WN, wn = wave % WN;
-        const uint8_t* sa = stage + (wm * (BM / WM) + lane % 16) * LDS_ROW + (lane / 16) * LB;
-        const uint8_t* sb = stage + Smem<BM, BN, DUAL>::A + (wn * (BN / WN) + lane % 16) * LDS_ROW + (lane / 16) * LB;
+        const int sw = lane & 7;                       // rows of a fragment are 16-aligned: row & 7 == lane & 7
+        const uint8_t* sa = stage + (wm * (BM / WM) + lane % 16) * BKB;
+        const uint8_t* sb = stage + (BM + wn * (BN / WN) + lane % 16) * BKB;
 #pragma unroll
         for (int s = 0; s < BKB / KSB; ++s) {
+            const int off = s * KSB + (lane / 16) * LB;
+            const int phys = (((off >> 4) ^ sw) << 4) | (off & 15);
             frag af[TM], bf[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *(const frag*)(sa + i * 16 * LDS_ROW + s * KSB);
+            for (int i = 0; i < TM; ++i) af[i] = *(const frag*)(sa + i * 16 * BKB + phys);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = *(const frag*)(sb + j * 16 * LDS_ROW + s * KSB);
+            for (int j = 0; j < TN; ++j) bf[j] = *(const frag*)(sb + j * 16 * BKB + phys);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -131,8 +146,7 @@ struct Core {
             if constexpr (DUAL) {
                 frag bf2[TN];
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    bf2[j] = *(const frag*)(sb + Smem<BM, BN, DUAL>::B + j * 16 * LDS_ROW + s * KSB);
+                for (int j = 0; j < TN; ++j) bf2[j] = *(const frag*)(sb + (BN + j * 16) * BKB + phys);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -141,19 +155,19 @@ struct Core {
         }
     }
 
-    __device__ __forceinline__ void run(uint8_t* smem) {
+    // Accumulates K stages [kt0, kt1).
+    __device__ __forceinline__ void run(uint8_t* smem, int kt0, int kt1) {
         zero();
-        const int nkt = (int)((kbytes + BKB - 1) / BKB);
-        load(0);
-        store(smem);
-        __syncthreads();
-        for (int kt = 0; kt < nkt; ++kt) {
-            uint8_t* cur = smem + (kt & 1) * Smem<BM, BN, DUAL>::STAGE;
-            uint8_t* nxt = smem + ((kt + 1) & 1) * Smem<BM, BN, DUAL>::STAGE;
-            if (kt + 1 < nkt) load(kt + 1);
-            compute(cur);
-            if (kt + 1 < nkt) store(nxt);
-            __syncthreads();
+        const int n = kt1 - kt0;
+        if (n <= 0) return;
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < n) load_stage(smem, kt0 + s, s);
+        for (int t = 0; t < n; ++t) {
+            wait_stages<LPW, NS - 2>(min(NS - 2, n - 1 - t));
+            stage_barrier();
+            if (t + NS - 1 < n) load_stage(smem, kt0 + t + NS - 1, (t + NS - 1) % NS);
+            compute(smem + (t % NS) * STAGE);
         }
     }
 };
@@ -165,7 +179,6 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 }
 
 struct EpiArgs {
-    int epi;
     void* C; long ldc;                   // elements
     const float* a_scale;                // fp8: per A-source-row
     const float* b_scale;                // fp8: per output column
@@ -175,19 +188,38 @@ struct EpiArgs {
     float* logits; long ld_logits;
 };
 
-// Applies the epilogue to one wave's accumulators.  rows/cols are global
-// indices; srow[i] = A source row (for per-token scales), M/N bounds.
-template <typename T, int BM, int BN, int WM, int WN, bool DUAL, int EPI>
-__device__ __forceinline__ void epilogue(Core<T, BM, BN, WM, WN, DUAL>& c, const EpiArgs& e,
-                                         int m0, int n0, int mlim, int N, const int* gather,
+// One output element: x = accumulated A B^T (u: the second weight's, SwiGLU).
+template <int EPI, bool FP8>
+__device__ __forceinline__ void epi_elem(const EpiArgs& e, int row, int col, int src_row, float x, float u) {
+    if constexpr (FP8) {
+        const float sa = e.a_scale[src_row];
+        x *= sa * e.b_scale[col];
+        if constexpr (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32) u *= sa * e.b2_scale[col];
+    }
+    const long off = (long)row * e.ldc + col;
+    if constexpr (EPI == EPI_F32) {
+        ((float*)e.C)[off] = x;
+    } else if constexpr (EPI == EPI_BF16) {
+        ((bf16_t*)e.C)[off] = f32_to_bf16(x);
+    } else if constexpr (EPI == EPI_ADD_F32) {
+        ((float*)e.C)[off] += x;
+    } else if constexpr (EPI == EPI_SWIGLU_BF16) {
+        ((bf16_t*)e.C)[off] = f32_to_bf16(silu_f(x) * u);
+    } else if constexpr (EPI == EPI_SWIGLU_F32) {
+        ((float*)e.C)[off] = silu_f(x) * u;
+    }
+}
+
+// Applies the epilogue to one wave's accumulators.
+template <class C, bool FP8, int EPI>
+__device__ __forceinline__ void epilogue(C& c, const EpiArgs& e, int m0, int n0, int mlim, int N, const int* gather,
                                          int gather_div, int ntile) {
-    typedef Core<T, BM, BN, WM, WN, DUAL> C;
-    const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE;
-    const int wm = wave / WN, wn = wave % WN;
-    const int rbase = m0 + wm * (BM / WM) + 4 * (lane / 16);
-    const int cbase = n0 + wn * (BN / WN) + lane % 16;
+    const int lane = threadIdx.x % WAVE;
+    const int wm = c.wave / C::WN, wn = c.wave % C::WN;
+    const int rbase = m0 + wm * (C::BM / C::WM) + 4 * (lane / 16);
+    const int cbase = n0 + wn * (C::BN / C::WN) + lane % 16;
     if constexpr (EPI == EPI_LMHEAD) {
-        static_assert(WN == 1, "LM head epilogue needs whole-tile columns per wave");
+        static_assert(C::WN == 1, "LM head epilogue needs whole-tile columns per wave");
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -195,7 +227,7 @@ __device__ __forceinline__ void epilogue(Core<T, BM, BN, WM, WN, DUAL>& c, const
                 const int row = rbase + i * 16 + v;
                 const bool rok = row < mlim;
                 float sa = 1.f;
-                if constexpr (sizeof(T) == 1) sa = rok ? e.a_scale[row] : 1.f;
+                if constexpr (FP8) sa = rok ? e.a_scale[row] : 1.f;
                 float vals[C::TN];
                 float mx = -INFINITY;
                 int ix = 0x7fffffff;
@@ -203,7 +235,7 @@ __device__ __forceinline__ void epilogue(Core<T, BM, BN, WM, WN, DUAL>& c, const
                 for (int j = 0; j < C::TN; ++j) {
                     const int col = cbase + j * 16;
                     float x = c.acc[i][j][v];
-                    if constexpr (sizeof(T) == 1) x *= sa * (col < N ? e.b_scale[col] : 0.f);
+                    if constexpr (FP8) x *= sa * (col < N ? e.b_scale[col] : 0.f);
                     if (rok && e.logits && col < N) e.logits[(long)row * e.ld_logits + col] = x;
                     if (col >= N || col == e.mask_col) x = -INFINITY;
                     vals[j] = x;
@@ -228,7 +260,6 @@ __device__ __forceinline__ void epilogue(Core<T, BM, BN, WM, WN, DUAL>& c, const
                     e.pidx[k] = ix;
                 }
             }
-        return;
     } else {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
@@ -236,67 +267,100 @@ __device__ __forceinline__ void epilogue(Core<T, BM, BN, WM, WN, DUAL>& c, const
             for (int v = 0; v < 4; ++v) {
                 const int row = rbase + i * 16 + v;
                 if (row >= mlim) continue;
-                float sa = 1.f;
-                if constexpr (sizeof(T) == 1) {
-                    const int src = gather ? gather[row] / gather_div : row;
-                    sa = e.a_scale[src];
-                }
+                const int src = gather ? gather[row] / gather_div : row;
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j) {
                     const int col = cbase + j * 16;
                     if (col >= N) continue;
-                    float x = c.acc[i][j][v];
-                    if constexpr (sizeof(T) == 1) x *= sa * e.b_scale[col];
-                    const long off = (long)row * e.ldc + col;
-                    if constexpr (EPI == EPI_F32) {
-                        ((float*)e.C)[off] = x;
-                    } else if constexpr (EPI == EPI_BF16) {
-                        ((bf16_t*)e.C)[off] = f32_to_bf16(x);
-                    } else if constexpr (EPI == EPI_ADD_F32) {
-                        ((float*)e.C)[off] += x;
-                    } else if constexpr (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32) {
-                        float u = c.acc2[i][j][v];
-                        if constexpr (sizeof(T) == 1) u *= sa * e.b2_scale[col];
-                        const float y = silu_f(x) * u;
-                        if constexpr (EPI == EPI_SWIGLU_BF16) ((bf16_t*)e.C)[off] = f32_to_bf16(y);
-                        else ((float*)e.C)[off] = y;
-                    }
+                    float u = 0.f;
+                    if constexpr (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32) u = c.acc2[i][j][v];
+                    epi_elem<EPI, FP8>(e, row, col, src, c.acc[i][j][v], u);
                 }
             }
     }
+}
+
+// Raw split-K partials: part[split][row][col] (and the second weight's at
+// part2) for rows < M, cols < N.
+template <class C>
+__device__ __forceinline__ void store_partial(C& c, float* part, float* part2, int m0, int n0, int M, int N) {
+    const int lane = threadIdx.x % WAVE;
+    const int wm = c.wave / C::WN, wn = c.wave % C::WN;
+    const int rbase = m0 + wm * (C::BM / C::WM) + 4 * (lane / 16);
+    const int cbase = n0 + wn * (C::BN / C::WN) + lane % 16;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = rbase + i * 16 + v;
+            if (row >= M) continue;
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                const int col = cbase + j * 16;
+                if (col >= N) continue;
+                part[(long)row * N + col] = c.acc[i][j][v];
+                if constexpr (C::TWO_B) part2[(long)row * N + col] = c.acc2[i][j][v];
+            }
+        }
 }
 
 struct DenseArgs {
     const uint8_t* A; long lda;          // bytes
     const uint8_t* B; const uint8_t* B2; long ldb;
     int M, N, K;
+    int splits;                          // split-K factor (1 = none)
+    float* part;                         // [splits][M][N] (+ the same again for the second weight)
     EpiArgs e;
 };
 
-template <typename T, int BM, int BN, int WM, int WN, bool DUAL, int EPI>
+// Workgroup order: ((n-tile * splits + split) * m-tiles + m-tile), remapped so
+// each XCD runs a contiguous range of it.
+template <class C, typename T, int EPI>
 __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<BM, BN, DUAL>::BYTES];
-    const int mt_n = (a.M + BM - 1) / BM, nt_n = (a.N + BN - 1) / BN;
-    const int lin = xcd_remap(blockIdx.x, mt_n * nt_n);
-    const int nt = lin / mt_n, mt = lin % mt_n;
-    const int m0 = mt * BM, n0 = nt * BN;
-    Core<T, BM, BN, WM, WN, DUAL> c;
-    c.kbytes = (long)a.K * sizeof(T);
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < Core<T, BM, BN, WM, WN, DUAL>::AC; ++j) {
-        const int r = (tid + 256 * j) / 8 + m0;
-        c.arow[j] = (r < a.M && tid + 256 * j < BM * 8) ? a.A + (long)r * a.lda : nullptr;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+    const int mt_n = (a.M + C::BM - 1) / C::BM, nt_n = (a.N + C::BN - 1) / C::BN;
+    const int lin = xcd_remap(blockIdx.x, mt_n * nt_n * a.splits);
+    const int mt = lin % mt_n;
+    const int split = (lin / mt_n) % a.splits;
+    const int nt = lin / mt_n / a.splits;
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    C c;
+    c.init([&](int R) -> const uint8_t* {
+        if (R < C::BM) {
+            const int r = min(m0 + R, a.M - 1);
+            return a.A + (long)r * a.lda;
+        }
+        R -= C::BM;
+        const uint8_t* B = a.B;
+        if (R >= C::BN) { R -= C::BN; B = a.B2; }
+        const int r = min(n0 + R, a.N - 1);
+        return B + (long)r * a.ldb;
+    });
+    const int nkt = (int)((long)a.K * sizeof(T) / BKB);
+    const int per = (nkt + a.splits - 1) / a.splits;
+    c.run(smem, split * per, min(nkt, (split + 1) * per));
+    if (a.splits > 1) {
+        const long mn = (long)a.M * a.N;
+        store_partial(c, a.part + split * mn, a.part + (a.splits + split) * mn, m0, n0, a.M, a.N);
+        return;
     }
-#pragma unroll
-    for (int j = 0; j < Core<T, BM, BN, WM, WN, DUAL>::BC; ++j) {
-        const int r = (tid + 256 * j) / 8 + n0;
-        const bool ok = r < a.N && tid + 256 * j < BN * 8;
-        c.brow[j] = ok ? a.B + (long)r * a.ldb : nullptr;
-        if constexpr (DUAL) c.b2row[j] = ok ? a.B2 + (long)r * a.ldb : nullptr;
+    epilogue<C, sizeof(T) == 1, EPI>(c, a.e, m0, n0, a.M, a.N, nullptr, 1, nt);
+}
+
+// Sum of the split partials in split order, then the epilogue.
+template <int EPI, bool FP8, bool DUAL>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(const float* part, int splits, int M, int N,
+                                                               EpiArgs e) {
+    const int row = blockIdx.y;
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= N) return;
+    const long mn = (long)M * N, off = (long)row * N + col;
+    float x = 0.f, u = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        x += part[s * mn + off];
+        if constexpr (DUAL) u += part[(splits + s) * mn + off];
     }
-    c.run(smem);
-    epilogue<T, BM, BN, WM, WN, DUAL, EPI>(c, a.e, m0, n0, a.M, a.N, nullptr, 1, nt);
+    epi_elem<EPI, FP8>(e, row, col, row, x, u);
 }
 
 struct GroupedArgs {
@@ -310,10 +374,10 @@ struct GroupedArgs {
     EpiArgs e;
 };
 
-template <typename T, int BM, int BN, int WM, int WN, bool DUAL, int EPI>
+template <class C, typename T, int EPI>
 __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<BM, BN, DUAL>::BYTES];
-    const int nt_n = (a.N + BN - 1) / BN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+    const int nt_n = (a.N + C::BN - 1) / C::BN;
     const int lin = xcd_remap(blockIdx.x, a.max_mtiles * nt_n);
     const int nt = lin / a.max_mtiles, mt = lin % a.max_mtiles;
     if (mt >= a.tile_start[a.E]) return;
@@ -324,55 +388,101 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs a) {
         if (a.tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     const int ex = lo;
-    const int m0 = a.offs[ex] + (mt - a.tile_start[ex]) * BM;
+    const int m0 = a.offs[ex] + (mt - a.tile_start[ex]) * C::BM;
     const int mlim = a.offs[ex + 1];
-    const int n0 = nt * BN;
-    Core<T, BM, BN, WM, WN, DUAL> c;
-    c.kbytes = (long)a.K * sizeof(T);
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < Core<T, BM, BN, WM, WN, DUAL>::AC; ++j) {
-        const int r = (tid + 256 * j) / 8 + m0;
-        const bool ok = r < mlim && tid + 256 * j < BM * 8;
-        const int src = ok ? (a.gather ? a.gather[r] / a.gather_div : r) : 0;
-        c.arow[j] = ok ? a.A + (long)src * a.lda : nullptr;
-    }
+    const int n0 = nt * C::BN;
     const uint8_t* Be = a.B + (long)ex * a.b_stride;
-    const uint8_t* B2e = DUAL ? a.B2 + (long)ex * a.b_stride : nullptr;
-#pragma unroll
-    for (int j = 0; j < Core<T, BM, BN, WM, WN, DUAL>::BC; ++j) {
-        const int r = (tid + 256 * j) / 8 + n0;
-        const bool ok = r < a.N && tid + 256 * j < BN * 8;
-        c.brow[j] = ok ? Be + (long)r * a.ldb : nullptr;
-        if constexpr (DUAL) c.b2row[j] = ok ? B2e + (long)r * a.ldb : nullptr;
-    }
-    c.run(smem);
+    const uint8_t* B2e = C::TWO_B ? a.B2 + (long)ex * a.b_stride : nullptr;
+    C c;
+    c.init([&](int R) -> const uint8_t* {
+        if (R < C::BM) {
+            const int r = min(m0 + R, mlim - 1);
+            const int src = a.gather ? a.gather[r] / a.gather_div : r;
+            return a.A + (long)src * a.lda;
+        }
+        R -= C::BM;
+        const uint8_t* B = Be;
+        if (R >= C::BN) { R -= C::BN; B = B2e; }
+        const int r = min(n0 + R, a.N - 1);
+        return B + (long)r * a.ldb;
+    });
+    c.run(smem, 0, (int)((long)a.K * sizeof(T) / BKB));
     EpiArgs e = a.e;
     if constexpr (sizeof(T) == 1) {
         e.b_scale = a.b_scale + (long)ex * a.bs_stride;
-        if constexpr (DUAL) e.b2_scale = a.b2_scale + (long)ex * a.bs_stride;
+        if (a.b2_scale) e.b2_scale = a.b2_scale + (long)ex * a.bs_stride;
     }
-    epilogue<T, BM, BN, WM, WN, DUAL, EPI>(c, e, m0, n0, mlim, a.N, a.gather, a.gather_div, nt);
+    epilogue<C, sizeof(T) == 1, EPI>(c, e, m0, n0, mlim, a.N, a.gather, a.gather_div, nt);
 }
 
 // ------------------------------------------------------------- launchers --
 
-template <typename T, int BM, int BN, int WM, int WN, bool DUAL, int EPI>
+// Tile shapes (BM, BN, WM, WN, stages):
+//   small M (<= 64; the tiny model, short canvases)     32 x 64,  waves 1x4, 4 stages
+//   canvas M (<= 256; one request's canvas)             256 x 64, waves 4x1, 3 stages
+//   prefill M                                           128 x 128, waves 2x2, 4 stages
+//   LM head (whole-tile columns per wave)               64 x 64 / 256 x 64, waves 4x1
+//   grouped (experts)                                   GROUPED_BM x 64, waves 1x4, 4 stages
+template <typename T, bool DUAL> using CoreS = Core<T, 32, 64, 1, 4, DUAL, 4>;
+template <typename T, bool DUAL> using CoreW = Core<T, 256, 64, 4, 1, DUAL, 3>;
+template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4>;
+template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
+template <typename T> using CoreHw = Core<T, 256, 64, 4, 1, false, 3>;
+template <typename T, bool DUAL> using CoreG = Core<T, GROUPED_BM, 64, 1, 4, DUAL, 4>;
+
+constexpr int SPLIT_TARGET_WG = 256;
+
+// Split-K factor: enough workgroups for the chip when the output tiles alone
+// are too few; every split keeps at least 4 K-stages; equalised so that no
+// split is empty.  LM-head and prefill-sized GEMMs are never split.
+template <class C, typename T, int EPI>
+static int splits_for(const GemmDesc& d) {
+    if constexpr (EPI == EPI_LMHEAD) return 1;
+    const long tiles = (long)((d.M + C::BM - 1) / C::BM) * ((d.N + C::BN - 1) / C::BN);
+    const int nkt = (int)((long)d.K * sizeof(T) / BKB);
+    if (tiles >= SPLIT_TARGET_WG * 3 / 4 || d.M > 256) return 1;
+    int s = (int)((SPLIT_TARGET_WG + tiles - 1) / tiles);
+    s = std::min(s, std::max(1, nkt / 4));
+    s = std::min(s, 16);
+    const int per = (nkt + s - 1) / s;
+    return std::max(1, (nkt + per - 1) / per);
+}
+
+template <class C, typename T, bool DUAL, int EPI>
+static long part_floats(const GemmDesc& d) {
+    const int s = splits_for<C, T, EPI>(d);
+    return s == 1 ? 0 : (long)s * d.M * d.N * (DUAL ? 2 : 1);
+}
+
+static EpiArgs make_epi(const GemmDesc& d, int bn) {
+    EpiArgs e;
+    e.C = d.C; e.ldc = d.ldc;
+    e.a_scale = d.a_scale; e.b_scale = d.b_scale; e.b2_scale = d.b2_scale;
+    e.pmax = d.pmax; e.psum = d.psum; e.pidx = d.pidx; e.n_tiles = (d.N + bn - 1) / bn;
+    e.mask_col = d.mask_col; e.logits = d.logits; e.ld_logits = d.ld_logits;
+    return e;
+}
+
+template <class C, typename T, bool DUAL, int EPI>
 static void launch_dense(const GemmDesc& d, hipStream_t st) {
     DenseArgs a;
     a.A = (const uint8_t*)d.A; a.lda = d.lda * (long)sizeof(T);
     a.B = (const uint8_t*)d.B; a.B2 = (const uint8_t*)d.B2; a.ldb = d.ldb * (long)sizeof(T);
     a.M = d.M; a.N = d.N; a.K = d.K;
-    a.e.epi = EPI; a.e.C = d.C; a.e.ldc = d.ldc;
-    a.e.a_scale = d.a_scale; a.e.b_scale = d.b_scale; a.e.b2_scale = d.b2_scale;
-    a.e.pmax = d.pmax; a.e.psum = d.psum; a.e.pidx = d.pidx; a.e.n_tiles = (d.N + BN - 1) / BN;
-    a.e.mask_col = d.mask_col; a.e.logits = d.logits; a.e.ld_logits = d.ld_logits;
-    const int grid = ((d.M + BM - 1) / BM) * ((d.N + BN - 1) / BN);
+    a.splits = splits_for<C, T, EPI>(d);
+    if (a.splits > 1 && (!d.splitk || part_floats<C, T, DUAL, EPI>(d) > d.splitk_floats))
+        a.splits = 1;   // no room: unsplit (correct, fewer workgroups)
+    a.part = d.splitk;
+    a.e = make_epi(d, C::BN);
+    const int grid = ((d.M + C::BM - 1) / C::BM) * ((d.N + C::BN - 1) / C::BN) * a.splits;
     if (grid == 0) return;
-    hipLaunchKernelGGL((gemm_dense_kernel<T, BM, BN, WM, WN, DUAL, EPI>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_dense_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
+    if (a.splits > 1)
+        hipLaunchKernelGGL((splitk_epilogue_kernel<EPI, sizeof(T) == 1, DUAL>), dim3((d.N + 255) / 256, d.M),
+                           dim3(256), 0, st, d.splitk, a.splits, d.M, d.N, a.e);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool DUAL, int EPI>
+template <class C, typename T, int EPI>
 static void launch_grouped(const GemmDesc& d, hipStream_t st) {
     GroupedArgs a;
     a.A = (const uint8_t*)d.A; a.lda = d.lda * (long)sizeof(T);
@@ -381,67 +491,76 @@ static void launch_grouped(const GemmDesc& d, hipStream_t st) {
     a.b_stride = d.b_stride * (long)sizeof(T);
     a.b_scale = d.b_scale; a.b2_scale = d.b2_scale; a.bs_stride = d.bs_stride;
     a.offs = d.offs; a.tile_start = d.tile_start; a.E = d.E; a.N = d.N; a.K = d.K;
-    a.max_mtiles = (d.M + BM - 1) / BM + d.E;
-    a.e.epi = EPI; a.e.C = d.C; a.e.ldc = d.ldc;
-    a.e.a_scale = d.a_scale; a.e.b_scale = nullptr; a.e.b2_scale = nullptr;
-    a.e.pmax = nullptr; a.e.psum = nullptr; a.e.pidx = nullptr; a.e.n_tiles = 0;
-    a.e.mask_col = -1; a.e.logits = nullptr; a.e.ld_logits = 0;
-    const int grid = a.max_mtiles * ((d.N + BN - 1) / BN);
+    a.max_mtiles = (d.M + C::BM - 1) / C::BM + d.E;
+    a.e = make_epi(d, C::BN);
+    const int grid = a.max_mtiles * ((d.N + C::BN - 1) / C::BN);
     if (d.M == 0 || grid == 0) return;
-    hipLaunchKernelGGL((gemm_grouped_kernel<T, BM, BN, WM, WN, DUAL, EPI>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_grouped_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
 }
 
-// Tile shapes.  Small-M problems (the tiny model's canvas) use 32-row tiles;
-// canvas-sized M (256 rows per request) 128 x 64; prefill-sized M 128 x 128.
-template <typename T, bool DUAL, int EPI>
-static void dispatch_dense(const GemmDesc& d, hipStream_t st) {
+template <bool DUAL, int EPI, typename T, class F>
+static void with_core(const GemmDesc& d, F f) {
     if constexpr (EPI == EPI_LMHEAD) {
-        if (d.M <= 64) launch_dense<T, 64, 64, 4, 1, false, EPI>(d, st);
-        else launch_dense<T, 128, 64, 4, 1, false, EPI>(d, st);
-    } else if constexpr (DUAL) {
-        if (d.M <= 64) launch_dense<T, 32, 64, 1, 4, true, EPI>(d, st);
-        else launch_dense<T, 128, 64, 2, 2, true, EPI>(d, st);
+        if (d.M <= 64) f(CoreHs<T>{});
+        else f(CoreHw<T>{});
     } else {
-        if (d.M <= 64) launch_dense<T, 32, 64, 1, 4, false, EPI>(d, st);
-        else if (d.M <= 512) launch_dense<T, 128, 64, 2, 2, false, EPI>(d, st);
-        else launch_dense<T, 128, 128, 2, 2, false, EPI>(d, st);
+        if (d.M <= 64) f(CoreS<T, DUAL>{});
+        else if (d.M <= 256) f(CoreW<T, DUAL>{});
+        else f(CoreL<T, DUAL>{});
     }
 }
 
+template <typename T, bool DUAL, int EPI>
+static void dense_t(const GemmDesc& d, hipStream_t st, long* need) {
+    with_core<DUAL, EPI, T>(d, [&](auto core) {
+        using C = decltype(core);
+        if (need) *need = part_floats<C, T, DUAL, EPI>(d);
+        else launch_dense<C, T, DUAL, EPI>(d, st);
+    });
+}
+
 template <typename T>
-static void gemm_t(const GemmDesc& d, hipStream_t st) {
+static void gemm_t(const GemmDesc& d, hipStream_t st, long* need) {
     switch (d.epi) {
-        case GEMM_STORE_F32: dispatch_dense<T, false, EPI_F32>(d, st); break;
-        case GEMM_STORE_BF16: dispatch_dense<T, false, EPI_BF16>(d, st); break;
-        case GEMM_ADD_F32: dispatch_dense<T, false, EPI_ADD_F32>(d, st); break;
+        case GEMM_STORE_F32: dense_t<T, false, EPI_F32>(d, st, need); break;
+        case GEMM_STORE_BF16: dense_t<T, false, EPI_BF16>(d, st, need); break;
+        case GEMM_ADD_F32: dense_t<T, false, EPI_ADD_F32>(d, st, need); break;
         case GEMM_SWIGLU:
-            if (d.out_f32) dispatch_dense<T, true, EPI_SWIGLU_F32>(d, st);
-            else dispatch_dense<T, true, EPI_SWIGLU_BF16>(d, st);
+            if (d.out_f32) dense_t<T, true, EPI_SWIGLU_F32>(d, st, need);
+            else dense_t<T, true, EPI_SWIGLU_BF16>(d, st, need);
             break;
-        case GEMM_LMHEAD: dispatch_dense<T, false, EPI_LMHEAD>(d, st); break;
+        case GEMM_LMHEAD: dense_t<T, false, EPI_LMHEAD>(d, st, need); break;
     }
 }
 
 template <typename T>
 static void grouped_t(const GemmDesc& d, hipStream_t st) {
-    // one tile row count for both expert GEMMs: GROUPED_BM (the routing scan
-    // computes each expert's first m-tile for this BM)
     switch (d.epi) {
         case GEMM_SWIGLU:
-            if (d.out_f32) launch_grouped<T, GROUPED_BM, 64, 1, 4, true, EPI_SWIGLU_F32>(d, st);
-            else launch_grouped<T, GROUPED_BM, 64, 1, 4, true, EPI_SWIGLU_BF16>(d, st);
+            if (d.out_f32) launch_grouped<CoreG<T, true>, T, EPI_SWIGLU_F32>(d, st);
+            else launch_grouped<CoreG<T, true>, T, EPI_SWIGLU_BF16>(d, st);
             break;
-        case GEMM_STORE_F32: launch_grouped<T, GROUPED_BM, 64, 1, 4, false, EPI_F32>(d, st); break;
+        case GEMM_STORE_F32: launch_grouped<CoreG<T, false>, T, EPI_F32>(d, st); break;
         default: break;
     }
 }
 
 void gemm(const GemmDesc& d, hipStream_t st) {
     switch (d.dtype) {
-        case DT_F32: gemm_t<float>(d, st); break;
-        case DT_BF16: gemm_t<bf16_t>(d, st); break;
-        case DT_FP8: gemm_t<fp8_t>(d, st); break;
+        case DT_F32: gemm_t<float>(d, st, nullptr); break;
+        case DT_BF16: gemm_t<bf16_t>(d, st, nullptr); break;
+        case DT_FP8: gemm_t<fp8_t>(d, st, nullptr); break;
     }
+}
+
+long gemm_splitk_floats(const GemmDesc& d) {
+    long need = 0;
+    switch (d.dtype) {
+        case DT_F32: gemm_t<float>(d, nullptr, &need); break;
+        case DT_BF16: gemm_t<bf16_t>(d, nullptr, &need); break;
+        case DT_FP8: gemm_t<fp8_t>(d, nullptr, &need); break;
+    }
+    return need;
 }
 
 void gemm_grouped(const GemmDesc& d, hipStream_t st) {

@@ -39,10 +39,15 @@ struct GemmDesc {
     const int* offs = nullptr;  // [E + 1]
     const int* tile_start = nullptr;  // [E + 1]
     int E = 0;
+    // split-K (dense GEMMs): fp32 partials [splits][M][N] (x2 for SwiGLU)
+    float* splitk = nullptr; long splitk_floats = 0;
 };
 
+// Dense and grouped GEMMs.  K * element size must be a multiple of 128 bytes.
 void gemm(const GemmDesc& d, hipStream_t st);
 void gemm_grouped(const GemmDesc& d, hipStream_t st);
+// fp32 partial space the dense GEMM d uses for split-K (0 if unsplit)
+long gemm_splitk_floats(const GemmDesc& d);
 int lm_head_tile_n();
 
 // Token ids of one forward: one flat array, or per-request canvases.
@@ -96,7 +101,8 @@ long attention_work_floats(int rows, int hq, int dh);
 
 // Router: logits fp32 [rows, E] -> top-k experts (ties -> lower id), weights =
 // softmax probabilities renormalised over the chosen k.
-void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy, hipStream_t st);
+void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
+                 float* logits_copy, hipStream_t st);
 
 // Stable counting sort of the rows*k assignments by expert: offs [E + 1],
 // tile_start [E + 1] (GROUPED_BM-row tiles), sorted_assign [A] (assignment

@@ -22,7 +22,7 @@ namespace dlm {
 constexpr int MAX_E = 256;
 
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, int rows, int E, int k, int* ids,
-                                                           float* w, int* ids_copy) {
+                                                           float* w, int* ids_copy, float* logits_copy) {
     const int lane = threadIdx.x % WAVE;
     const int r = blockIdx.x * 4 + threadIdx.x / WAVE;
     if (r >= rows) return;
@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, i
     for (int j = 0; j < PER; ++j) {
         const int e = lane + WAVE * j;
         v[j] = e < E ? logits[(long)r * E + e] : -INFINITY;
+        if (logits_copy && e < E) logits_copy[(long)r * E + e] = v[j];
     }
     float m = -INFINITY;
 #pragma unroll
@@ -69,10 +70,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, i
         for (int s = 0; s < k; ++s) w[(long)r * k + s] /= sel_sum;
 }
 
-void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy, hipStream_t st) {
+void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
+                 float* logits_copy, hipStream_t st) {
     if (rows <= 0) return;
     hipLaunchKernelGGL(router_topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, logits, rows, E, k, ids, w,
-                       ids_copy);
+                       ids_copy, logits_copy);
 }
 
 // ------------------------------------------------------------------ route --

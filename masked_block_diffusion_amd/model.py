@@ -176,9 +176,11 @@ class DLM:
             check(st, "dlm_check_device_status")
         return bits.value
 
-    def dlm_debug_router(self, out: Optional[torch.Tensor]) -> None:
-        """Test hook: record each layer's router choices into `out` (int32)."""
-        check(self.lib.dlm_debug_router(self.handle, _ptr(out), 0 if out is None else out.numel()),
+    def dlm_debug_router(self, ids: Optional[torch.Tensor], logits: Optional[torch.Tensor] = None,
+                         capacity_rows: int = 0) -> None:
+        """Test hook: record each layer's router choices (int32 [L, rows, k]) and
+        router logits (fp32 [L, rows, E]) of every forward."""
+        check(self.lib.dlm_debug_router(self.handle, _ptr(ids), _ptr(logits), capacity_rows),
               "dlm_debug_router")
 
     # ------------------------------------------------------------- timing --

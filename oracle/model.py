@@ -161,6 +161,7 @@ class StepDebug:
     logits: Optional[np.ndarray] = None          # [C, V] with mask column = -inf
     router_sets: List[np.ndarray] = field(default_factory=list)   # per layer [C, k]
     router_gap: List[np.ndarray] = field(default_factory=list)    # per layer [C] k-th minus (k+1)-th logit
+    router_logits: List[np.ndarray] = field(default_factory=list)  # per layer [C, E]
 
 
 class OracleModel:
@@ -216,16 +217,17 @@ class OracleModel:
         w = ps / ps.sum(axis=-1, keepdims=True)
         rs = np.take_along_axis(r, order, axis=-1)
         gap = rs[:, c.top_k - 1] - rs[:, c.top_k] if c.top_k < c.n_experts else np.full(len(r), np.inf)
-        return sel, w, gap
+        return sel, w, gap, r
 
     def moe(self, h: np.ndarray, l: int, dbg: Optional[StepDebug] = None) -> np.ndarray:
         """sum over the chosen experts of weight * SwiGLU_e(h), plus the ungated
         shared SwiGLU(h)."""
         p = f"{l}."
-        sel, w, gap = self.router(h, l)
+        sel, w, gap, logits = self.router(h, l)
         if dbg is not None:
             dbg.router_sets.append(np.sort(sel, axis=-1))
             dbg.router_gap.append(gap)
+            dbg.router_logits.append(logits)
         y = self.swiglu(h, p + "w_gate", p + "w_up", p + "w_down")
         for e in range(self.cfg.n_experts):
             rows, slots = np.nonzero(sel == e)

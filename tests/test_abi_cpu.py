@@ -112,7 +112,7 @@ def test_calls_on_null_model_fail_cleanly():
     assert lib.dlm_commit(None, arr, 1, None, None, ctypes.byref(rule), 0, None, None, None) == abi.DLM_E_ARG
     assert lib.dlm_check_device_status(None, None, None) == abi.DLM_E_ARG
     assert lib.dlm_timing_enable(None, 1) == abi.DLM_E_ARG
-    assert lib.dlm_debug_router(None, None, 0) == abi.DLM_E_ARG
+    assert lib.dlm_debug_router(None, None, None, 0) == abi.DLM_E_ARG
     lib.dlm_destroy(None)                           # no-op
 
 

@@ -238,7 +238,8 @@ def test_router_ties_go_to_lower_expert():
     m.W.w["0.w_router"] = np.array([[1.0] + [0.0] * 31, [2.0] + [0.0] * 31,
                                     [2.0] + [0.0] * 31, [2.0] + [0.0] * 31])
     h = np.zeros((1, 32)); h[0, 0] = 1.0
-    sel, w, gap = m.router(h, 0)
+    sel, w, gap, logits = m.router(h, 0)
+    np.testing.assert_allclose(logits, [[1.0, 2.0, 2.0, 2.0]])
     assert sel.tolist() == [[1, 2]]
     np.testing.assert_allclose(w, [[0.5, 0.5]])
     assert gap[0] == 0.0
