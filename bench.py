@@ -9,13 +9,16 @@ second over the K timed steps, inputs already resident in HBM.
 Default workload: the dense 16-layer d=2048 bf16 model (16 Q / 4 KV heads x
 128, SwiGLU 8192, vocab 32768) with a 1024-token prefix and one 256-token
 canvas, 16 steps x 16 commits, then the append.  Weights and prompt are seeded
-synthetic draws (random init), generated on the host so the CPU baseline reads
+synthetic draws (random init) generated on the host, so the CPU baseline reads
 the same bytes.
 
 Also reported: ms per denoising step (denoise + commit, CUDA events on the
-library's stream), the dominant kernel's roofline from the library's own HIP
-event timing over the timed region, and the CPU oracle timed on a bounded
-sample of the same workload.
+library's stream), and the roofline of the dominant kernel of the denoising
+step.  The dominant kernel is found in an untimed warmup request with every
+kernel timed; in the timed region only it is bracketed by the library's HIP
+events (on the stream it runs on), and its algorithmic bytes and flops per
+launch (models below) over its average launch time give the achieved rate.
+The CPU oracle is timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -31,8 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "committed tokens/s at batch 1 (256-canvas); ms per denoise step; MFMA util %"
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
-FP8_PEAK_TFLOPS = 5000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 
 
 def _workload_text(run) -> str:
@@ -46,37 +48,58 @@ def _workload_text(run) -> str:
             f"{rule}, append")
 
 
-def gemm_roofline(cfg, C: int, avg_ms: float, kernel: str):
-    """Algorithmic bytes / flops of one launch of the dominant GEMM at M = C rows."""
-    d, F = cfg.d_model, cfg.d_ffn
-    eb = 1 if cfg.dtype == "fp8" else 2
-    if kernel == "gemm_gate_up":        # SwiGLU: A [C, d], gate and up [F, d], out bf16 [C, F]
-        wbytes = 2 * F * d * eb
-        abytes = C * d * eb
-        obytes = C * F * 2
-        flops = 2.0 * C * (2 * F) * d
-    else:
-        raise ValueError(kernel)
-    total = wbytes + abytes + obytes
+def kernel_model(name: str, cfg, C: int, keys: int):
+    """Algorithmic (bytes, flops) of one launch of a denoising-step kernel over
+    a C-row canvas attending to `keys` keys.  Bytes: weights and activations
+    read once, outputs written once (x read and written for residual adds);
+    flops: 2 per multiply-add of the contraction."""
+    d, F, dh = cfg.d_model, cfg.d_ffn, cfg.head_dim
+    qd, kvd = cfg.n_q_heads * dh, cfg.n_kv_heads * dh
+    nqkv = qd + 2 * kvd
+    eb = 1 if cfg.dtype == "fp8" else (4 if cfg.dtype == "f32" else 2)
+    ab = 4 if cfg.dtype == "f32" else 2          # stored activation element
+    if name == "gemm_qkv":
+        return nqkv * d * eb + C * d * eb + C * nqkv * 4, 2.0 * C * nqkv * d
+    if name == "gemm_o":
+        return d * qd * eb + C * qd * eb + 2 * C * d * 4, 2.0 * C * d * qd
+    if name == "gemm_gate_up":
+        return 2 * F * d * eb + C * d * eb + C * F * ab, 2.0 * C * 2 * F * d
+    if name == "gemm_down":
+        return d * F * eb + C * F * eb + 2 * C * d * 4, 2.0 * C * d * F
+    if name == "lm_head":
+        return cfg.vocab * d * eb + C * d * eb, 2.0 * C * cfg.vocab * d
+    if name == "attention":
+        return (2 * keys * kvd * ab + 2 * C * qd * ab,
+                4.0 * C * cfg.n_q_heads * keys * dh)
+    return None
+
+
+def roofline(name, cfg, C, keys, avg_ms):
+    m = kernel_model(name, cfg, C, keys)
+    if m is None or avg_ms <= 0:
+        return None
+    nbytes, flops = m
     s = avg_ms * 1e-3
-    return {
-        "kernel": f"{kernel} (M={C}, N=2x{F}, K={d}, {cfg.dtype})",
-        "bound": "hbm",
-        "achieved": total / s / 1e9,
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": total / s / 1e9 / HBM_PEAK_GBS,
-        "traffic": None,
-        "bytes_per_launch": total,
-        "flops_per_launch": flops,
-        "avg_launch_ms": avg_ms,
-        "mfma_util_pct": 100.0 * flops / s / 1e12 / (FP8_PEAK_TFLOPS if cfg.dtype == "fp8" else BF16_PEAK_TFLOPS),
-    }
+    peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (peak_tf * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    out = {"kernel": name, "bound": bound}
+    if bound == "hbm":
+        out.update(achieved=nbytes / s / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                   frac=nbytes / s / 1e9 / HBM_PEAK_GBS)
+    else:
+        out.update(achieved=flops / s / 1e12, peak=peak_tf, unit="TFLOP/s",
+                   frac=flops / s / 1e12 / peak_tf)
+    out.update(traffic=None, algorithmic_bytes_per_launch=nbytes, flops_per_launch=flops,
+               avg_launch_ms=avg_ms, mfma_util_pct=100.0 * flops / s / 1e12 / peak_tf,
+               hbm_gbs=nbytes / s / 1e9)
+    return out
 
 
 def cpu_baseline(run, weights_cpu, prefix_cpu):
     """The oracle on the host, on a bounded sample of the same workload: prefill
-    of the full prompt, one denoising step with its commit, and the append;
+    of the full prompt, one denoising step with its commit, and one append;
     the request time is extrapolated to the schedule's step count."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -97,18 +120,17 @@ def cpu_baseline(run, weights_cpu, prefix_cpu):
     canvas[canvas == cfg.mask_id] = 0
     om.append(st, canvas)
     t3 = time.perf_counter()
-    per_req = (t1 - t0) + run.n_steps * (t2 - t1) + (t3 - t2)
+    per_req = (t1 - t0) + run.n_canvases * (run.n_steps * (t2 - t1) + (t3 - t2))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {
-        "value": run.canvas * run.n_canvases / per_req if run.n_canvases == 1 else
-        run.canvas * run.n_canvases / ((t1 - t0) + run.n_canvases * (run.n_steps * (t2 - t1) + (t3 - t2))),
+        "value": run.canvas * run.n_canvases / per_req,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle on the host: prefill of the {len(prefix_cpu)}-token prompt "
-                   f"({t1 - t0:.2f} s), one denoising step + commit ({t2 - t1:.2f} s) and one append "
-                   f"({t3 - t2:.2f} s) of the same workload and weights; the request is extrapolated to "
-                   f"{run.n_steps} steps per canvas"),
+        "sample": (f"float64 numpy oracle on the host ({threads} BLAS threads): prefill of the "
+                   f"{len(prefix_cpu)}-token prompt ({t1 - t0:.2f} s), one denoising step + commit "
+                   f"({t2 - t1:.2f} s) and one append ({t3 - t2:.2f} s) of the same workload and weights; "
+                   f"the request is extrapolated to {run.n_steps} steps per canvas"),
         "s_per_denoise_step": t2 - t1,
     }
 
@@ -149,16 +171,15 @@ def main():
     pred = torch.empty(C, dtype=torch.int32, device="cuda")
     n_masked = torch.empty(1, dtype=torch.int32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * run.n_canvases)]
-    timed_kernel = "gemm_gate_up"
+    all_ids = list(range(abi.DLM_K_COUNT))
 
-    def one_request(timing: bool):
+    def one_request(timed_ids):
         seq.raw.T = 0
         model.dlm_prefill(seq, prefix, ws)
         steps_run = 0
         for ci in range(run.n_canvases):
             seq.canvas.fill_(cfg.mask_id)
-            if timing:
-                model.timing_enable([abi.DLM_K_GEMM_GATE_UP])
+            model.timing_enable(timed_ids)
             ev[2 * ci].record()
             for s in range(run.n_steps):
                 model.dlm_denoise_step([seq], conf, pred, ws)
@@ -167,27 +188,30 @@ def main():
                 if run.rule == "threshold" and int(n_masked.cpu()[0]) == 0:
                     break
             ev[2 * ci + 1].record()
-            if timing:
-                model.timing_enable([])
+            model.timing_enable([])
             model.dlm_append_canvas([seq], ws)
         return steps_run
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] warmup {args.warmup} (+1 with every kernel timed)", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        one_request(False)
+        one_request([])
     torch.cuda.synchronize()
     model.timing_read()
-    denoise_ms, n_denoise = 0.0, 0
+    one_request(all_ids)
+    torch.cuda.synchronize()
+    per_kernel = model.timing_read()
+    dominant = max(per_kernel, key=lambda k: per_kernel[k][0])
+    dom_id = [i for i in all_ids if model.lib.dlm_kernel_name(i).decode() == dominant][0]
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    n_denoise = 0
     for _ in range(args.steps):
-        n_denoise += one_request(True)
+        n_denoise += one_request([dom_id])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # per-canvas denoise loop times of the last timed request, then all requests' kernel timing
     kt = model.timing_read()
-    for ci in range(run.n_canvases):
-        denoise_ms += ev[2 * ci].elapsed_time(ev[2 * ci + 1])
+    denoise_ms = sum(ev[2 * ci].elapsed_time(ev[2 * ci + 1]) for ci in range(run.n_canvases))
     status = model.dlm_check_device_status()
     if status:
         print(f"[bench] device error word {status}", file=sys.stderr)
@@ -195,7 +219,9 @@ def main():
     elapsed = t1 - t0
     tokens = args.steps * C * run.n_canvases
     steps_last = n_denoise // args.steps
-    ms_k, n_k = kt.get(timed_kernel, (0.0, 0))
+    ms_k, n_k = kt.get(dominant, (0.0, 0))
+    keys = run.max_prefix + C
+    step_ms = denoise_ms / max(1, steps_last)
     out = {
         "metric": METRIC,
         "value": tokens / elapsed,
@@ -207,7 +233,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else cfg.dtype,
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded random-init weights and uniform random prompt ids)",
         "config": {
             "workload": _workload_text(run),
@@ -218,10 +244,17 @@ def main():
             "denoise_steps_per_canvas": steps_last / run.n_canvases,
             "parallelism": "single GPU",
         },
-        "ms_per_denoise_step": denoise_ms / max(1, steps_last),
+        "ms_per_denoise_step": step_ms,
         "decode_tokens_per_s": C * run.n_canvases / (denoise_ms * 1e-3) if denoise_ms else None,
-        "roofline": gemm_roofline(cfg, C, ms_k / max(1, n_k), timed_kernel) if n_k else None,
+        "roofline": roofline(dominant, cfg, C, keys, ms_k / max(1, n_k)),
+        "denoise_step_kernels_ms": {k: round(v[0] / max(1, steps_last), 4) for k, v in
+                                    sorted(per_kernel.items(), key=lambda kv: -kv[1][0])},
     }
+    for name, (ms, n) in per_kernel.items():
+        r = roofline(name, cfg, C, keys, ms / max(1, n))
+        if r:
+            out.setdefault("kernel_rooflines", {})[name] = {k: r[k] for k in ("bound", "frac", "hbm_gbs",
+                                                                              "mfma_util_pct", "avg_launch_ms")}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         del model

@@ -90,7 +90,7 @@ typedef enum { DLM_FFN_DENSE = 0, DLM_FFN_MOE = 1 } dlm_ffn_kind;
 /* Model shape.  Constraints checked by dlm_create: head_dim in {32, 64, 128};
  * n_q_heads a multiple of n_kv_heads; d_model, d_ffn, d_expert multiples of 32
  * (f32) / 64 (bf16) / 128 (fp8) elements; top_k <= n_experts <= 256,
- * top_k <= 16; 0 <= mask_id < vocab; canvas in [1, 1024]. */
+ * top_k <= 16; 0 <= mask_id < vocab; canvas in [1, 1024]; d_model <= 4096. */
 typedef struct {
     int32_t n_layers;
     int32_t d_model;
@@ -249,6 +249,24 @@ dlm_status dlm_debug_router(dlm_model* model, int32_t* router_ids, float* router
  * saturating at +-448.  E_ARG on null pointers or rows / d < 1. */
 dlm_status dlm_op_quant_rows(const void* x, int32_t rows, int32_t d, void* q, float* s, void* stream);
 
+/* Test hook: one dense GEMM of the kind the model runs, C = A B^T, with A
+ * [M, K] and B [N, K] row-major (device).  dtype DLM_F32, DLM_BF16 or DLM_FP8
+ * (E4M3FN codes; then every product is scaled by a_scale[m] * b_scale[n], and
+ * b2_scale[n] for B2 -- device fp32 arrays, required for DLM_FP8 only).
+ *   swiglu = 0: C fp32 [M, N].
+ *   swiglu = 1: C = silu(A B^T) * (A B2^T), bf16 (fp32 for DLM_F32) [M, N].
+ * variant: tile shape, 0 = the one the model would pick, 1..8 forced (bf16
+ * only); splits: split-K factor, 0 = the model's choice.  ws / ws_bytes: room
+ * for split-K partials (see dlm_op_gemm_workspace).  ms (host, nullable): when
+ * set, the GEMM kernel is timed with events in its dispatch, the call
+ * synchronises and writes the kernel's duration.  E_SHAPE unless K * element
+ * size is a multiple of 128 bytes; E_ARG for a variant outside 0..8. */
+dlm_status dlm_op_gemm(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                       const void* B2, const float* a_scale, const float* b_scale, const float* b2_scale, void* C,
+                       void* ws, size_t ws_bytes, int32_t variant, int32_t splits, float* ms, void* stream);
+size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, int32_t variant,
+                             int32_t splits);
+
 /* Kernel timing.  `kernel_mask` bit i enables timing of kernel id i (0 = off):
  * every launch of a timed kernel is bracketed by HIP events on its stream.
  * dlm_timing_read synchronises, sums the elapsed times per kernel id since the
@@ -259,6 +277,7 @@ typedef enum {
     DLM_K_ATTN_MERGE, DLM_K_GEMM_O, DLM_K_GEMM_GATE_UP, DLM_K_GEMM_DOWN,
     DLM_K_QUANT, DLM_K_ROUTER, DLM_K_TOPK, DLM_K_PERMUTE, DLM_K_EXPERT_GATE_UP,
     DLM_K_EXPERT_DOWN, DLM_K_COMBINE, DLM_K_LM_HEAD, DLM_K_LM_MERGE, DLM_K_COMMIT,
+    DLM_K_SPLITK_EPILOGUE,
     DLM_K_COUNT
 } dlm_kernel_id;
 dlm_status dlm_timing_enable(dlm_model* model, int32_t kernel_mask);

@@ -41,6 +41,7 @@ KERNEL_IDS = [
     "DLM_K_ATTN_MERGE", "DLM_K_GEMM_O", "DLM_K_GEMM_GATE_UP", "DLM_K_GEMM_DOWN",
     "DLM_K_QUANT", "DLM_K_ROUTER", "DLM_K_TOPK", "DLM_K_PERMUTE", "DLM_K_EXPERT_GATE_UP",
     "DLM_K_EXPERT_DOWN", "DLM_K_COMBINE", "DLM_K_LM_HEAD", "DLM_K_LM_MERGE", "DLM_K_COMMIT",
+    "DLM_K_SPLITK_EPILOGUE",
 ]
 for _i, _n in enumerate(KERNEL_IDS):
     globals()[_n] = _i
@@ -51,7 +52,7 @@ EXPORTS = [
     "dlm_create", "dlm_destroy", "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
     "dlm_commit", "dlm_append_canvas", "dlm_check_device_status", "dlm_last_error",
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
-    "dlm_op_quant_rows",
+    "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace",
 ]
 
 
@@ -129,6 +130,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_kernel_name": (c_char_p, [c_int32]),
         "dlm_debug_router": (c_int32, [P, P, P, ctypes.c_int64]),
         "dlm_op_quant_rows": (c_int32, [P, c_int32, c_int32, P, P, P]),
+        "dlm_op_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, P, P, P,
+                                  c_size_t, c_int32, c_int32, POINTER(c_float), P]),
+        "dlm_op_gemm_workspace": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -16,6 +16,13 @@
 
 using namespace dlm;
 
+namespace dlm {
+LaunchTimer*& launch_timer() {
+    thread_local LaunchTimer* t = nullptr;
+    return t;
+}
+}  // namespace dlm
+
 namespace {
 
 thread_local std::string g_err;
@@ -34,7 +41,7 @@ dlm_status fail(dlm_status s, const char* fmt, ...) {
 const char* kKernelNames[DLM_K_COUNT] = {
     "embed", "rmsnorm", "gemm_qkv", "rope_kv", "attention", "attention_merge", "gemm_o",
     "gemm_gate_up", "gemm_down", "quant", "router", "router_topk", "moe_route", "expert_gate_up",
-    "expert_down", "moe_combine", "lm_head", "lm_merge", "commit"};
+    "expert_down", "moe_combine", "lm_head", "lm_merge", "commit", "splitk_epilogue"};
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -62,19 +69,36 @@ struct dlm_model {
 
 namespace {
 
-// RAII bracket of one kernel launch with HIP events when that kernel id is timed.
+// RAII scope around one kernel launch of a timed kernel id: the first kernel
+// launched in the scope carries the start / stop events in its dispatch.
+// With install = false the timer is only prepared (timer() hands it to a
+// launcher that arms it for a specific kernel of its own).
 struct Timed {
-    dlm_model* m; hipStream_t st; int id; bool on; hipEvent_t b;
-    Timed(dlm_model* m_, int id_, hipStream_t st_) : m(m_), st(st_), id(id_) {
+    dlm_model* m; int id; bool on, installed = false;
+    LaunchTimer lt;
+    LaunchTimer* prev = nullptr;
+    Timed(dlm_model* m_, int id_, hipStream_t, bool install = true) : m(m_), id(id_) {
         on = (m->timing_mask >> id) & 1u;
         if (!on) return;
-        hipEvent_t a = take();
-        b = take();
-        hipEventRecord(a, st);
-        m->pending.push_back({a, b, id});
+        lt.start = take();
+        lt.stop = take();
+        lt.armed = true;
+        if (install) {
+            installed = true;
+            prev = launch_timer();
+            launch_timer() = &lt;
+        }
     }
+    LaunchTimer* timer() { return on ? &lt : nullptr; }
     ~Timed() {
-        if (on) hipEventRecord(b, st);
+        if (!on) return;
+        if (installed) launch_timer() = prev;
+        if (lt.armed) {                  // nothing launched (empty problem)
+            m->pool.push_back(lt.start);
+            m->pool.push_back(lt.stop);
+        } else {
+            m->pending.push_back({lt.start, lt.stop, id});
+        }
     }
     hipEvent_t take() {
         if (!m->pool.empty()) {
@@ -159,7 +183,7 @@ Plan plan(const dlm_config& c, int rows, int max_kv) {
         p.eis = fp8 ? take(A * 4) : 0;
         p.y = take(A * d * 4);
     }
-    const size_t nt = (c.vocab + lm_head_tile_n() - 1) / lm_head_tile_n();
+    const size_t nt = (c.vocab + lm_head_tile_n(1) - 1) / lm_head_tile_n(1);   // the narrowest vocab tile
     p.pmax = take(R * nt * 4);
     p.psum = take(R * nt * 4);
     p.pidx = take(R * nt * 4);
@@ -188,6 +212,7 @@ dlm_status check_config(const dlm_config* c) {
     if (c->ffn != DLM_FFN_DENSE && c->ffn != DLM_FFN_MOE) return fail(DLM_E_ARG, "unknown ffn kind %d", c->ffn);
     if (c->canvas < 1 || c->canvas > 1024) return fail(DLM_E_SHAPE, "canvas %d not in [1, 1024]", c->canvas);
     if (c->d_ffn < 1) return fail(DLM_E_SHAPE, "d_ffn < 1");
+    if (c->d_model > rmsnorm_max_dim()) return fail(DLM_E_SHAPE, "d_model above %d", rmsnorm_max_dim());
     if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(DLM_E_ARG, "bad rms_eps / rope_base");
     const int eb = elem_bytes(c->dtype);
     const int kdims[4] = {c->d_model, c->n_q_heads * c->head_dim, c->d_ffn,
@@ -257,10 +282,31 @@ dlm_status hip_status(const char* where) {
 
 enum Mode { PREFILL, DENOISE, APPEND };
 
-void run_gemm(dlm_model* m, int id, const GemmDesc& d, hipStream_t st, bool grouped = false) {
-    Timed t(m, id, st);
-    if (grouped) gemm_grouped(d, st);
-    else gemm(d, st);
+// Runs a GEMM.  A split-K result is either summed right away by the split-K
+// epilogue kernel, or -- when `consumed` -- handed back as Partials for the
+// kernel that reads the result next (RMSNorm, RoPE, MoE combine) to sum.  An
+// unsplit result is already applied (or stored in d.C).
+Partials run_gemm(dlm_model* m, int id, const GemmDesc& d, hipStream_t st, bool consumed = false) {
+    int splits;
+    {
+        Timed t(m, id, st);
+        splits = gemm_main(d, st);
+    }
+    Partials out;
+    if (splits <= 1) return out;
+    if (consumed) {
+        out.p = d.splitk;
+        out.splits = splits;
+        out.stride = (long)d.M * d.N;
+        if (d.dtype == DT_FP8) {
+            out.a_scale = d.a_scale;
+            out.b_scale = d.b_scale;
+        }
+        return out;
+    }
+    Timed t(m, DLM_K_SPLITK_EPILOGUE, st);
+    gemm_splitk_finish(d, splits, st);
+    return out;
 }
 
 void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, void* ws, float* conf, int* pred,
@@ -282,22 +328,25 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
     void* q = at<void>(ws, p.q);
     void* ao = at<void>(ws, p.ao);
     void* fi = at<void>(ws, p.fi);
+    Partials pending;                              // split residual update not yet added to x
 
     {
         Timed t(m, DLM_K_EMBED, st);
         embed(ids, R, m->w.embed, f32 ? DT_F32 : DT_BF16, d, c.vocab, c.mask_id, mode == APPEND, x, m->d_err, st);
     }
 
-    // RMSNorm into the GEMM operand: fp32 / bf16 in hA; fp8 also codes + scales
+    // x += pending; RMSNorm into the GEMM operand: fp32 / bf16 in hA, fp8 also codes + scales
     auto norm = [&](const float* g) {
         Timed t(m, DLM_K_NORM, st);
-        rmsnorm(x, g, R, d, c.rms_eps, f32 ? (float*)hA : nullptr, f32 ? nullptr : (uint16_t*)hA, hq, hs, st);
+        rmsnorm(x, pending, g, R, d, c.rms_eps, f32 ? (float*)hA : nullptr, f32 ? nullptr : (uint16_t*)hA, hq, hs,
+                st);
+        pending = Partials();
     };
     auto opA = [&](const void* bf, const void* q8) { return fp8 ? q8 : bf; };
-    auto dense = [&](int id, GemmDesc g) {
+    auto dense = [&](int id, GemmDesc g, bool consumed = false) {
         g.splitk = at<float>(ws, p.splitk);
         g.splitk_floats = p.splitk_floats;
-        run_gemm(m, id, g, st);
+        return run_gemm(m, id, g, st, consumed);
     };
     auto quant = [&](const void* src, int rows, int cols, uint8_t* qd8, float* sc) {
         if (!fp8) return;
@@ -308,6 +357,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
     for (int l = 0; l < c.n_layers; ++l) {
         const dlm_layer_weights& L = m->layers[l];
         norm(L.attn_norm);
+        Partials qkv_res;
         {
             GemmDesc g;
             g.dtype = gdt; g.epi = GEMM_STORE_F32;
@@ -315,15 +365,20 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.B = L.wqkv; g.ldb = d; g.b_scale = L.wqkv_s;
             g.M = R; g.N = nqkv; g.K = d;
             g.C = qkv; g.ldc = nqkv;
-            dense(DLM_K_GEMM_QKV, g);
+            qkv_res = dense(DLM_K_GEMM_QKV, g, true);
+            if (!qkv_res.p) qkv_res.p = qkv;
         }
         {
             Timed t(m, DLM_K_ROPE_KV, st);
-            rope_kv(qkv, R, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, c.rope_base, f32, q, st);
+            rope_kv(qkv_res, R, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, c.rope_base, f32, q, st);
         }
+        // Prefill and append produce the KV cache only: the last layer's
+        // attention output, O projection and FFN feed nothing they return.
+        if (mode != DENOISE && l == c.n_layers - 1) break;
         {
+            Timed tm(m, DLM_K_ATTN_MERGE, st, false);   // handed to the split-KV merge launch
             Timed t(m, DLM_K_ATTN, st);
-            AttnWork w{at<float>(ws, p.opart), at<float>(ws, p.mlpart), 0};
+            AttnWork w{at<float>(ws, p.opart), at<float>(ws, p.mlpart), 0, tm.timer()};
             attention(q, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, mode == PREFILL, f32, ao, w, st);
         }
         quant(ao, R, qd, fp8 ? at<uint8_t>(ws, p.aoq) : nullptr, fp8 ? at<float>(ws, p.aos) : nullptr);
@@ -335,10 +390,21 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.B = L.wo; g.ldb = qd; g.b_scale = L.wo_s;
             g.M = R; g.N = d; g.K = qd;
             g.C = x; g.ldc = d;
-            dense(DLM_K_GEMM_O, g);
+            pending = dense(DLM_K_GEMM_O, g, true);
         }
         norm(L.ffn_norm);
+        // dense SwiGLU FFN, or the MoE's shared expert
+        {
+            GemmDesc g;
+            g.dtype = gdt; g.epi = GEMM_SWIGLU; g.out_f32 = f32;
+            g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
+            g.B = L.w_gate; g.B2 = L.w_up; g.ldb = d; g.b_scale = L.w_gate_s; g.b2_scale = L.w_up_s;
+            g.M = R; g.N = c.d_ffn; g.K = d; g.C = fi; g.ldc = c.d_ffn;
+            dense(DLM_K_GEMM_GATE_UP, g);
+        }
+        quant(fi, R, c.d_ffn, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr, fp8 ? at<float>(ws, p.fis) : nullptr);
         if (c.ffn == DLM_FFN_MOE) {
+            // routing reads hA, which the shared expert left untouched
             const int E = c.n_experts, k = c.top_k, De = c.d_expert, A = R * k;
             float* rl = at<float>(ws, p.rl);
             int* tid = at<int>(ws, p.tid);
@@ -374,7 +440,8 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                 g.b_scale = L.we_gate_s; g.b2_scale = L.we_up_s; g.bs_stride = De;
                 g.offs = offs; g.tile_start = tstart; g.E = E;
                 g.M = A; g.N = De; g.K = d; g.C = ei; g.ldc = De;
-                run_gemm(m, DLM_K_EXPERT_GATE_UP, g, st, true);
+                Timed t(m, DLM_K_EXPERT_GATE_UP, st);
+                gemm_grouped(g, st);
             }
             quant(ei, A, De, fp8 ? at<uint8_t>(ws, p.eiq) : nullptr, fp8 ? at<float>(ws, p.eis) : nullptr);
             float* y = at<float>(ws, p.y);
@@ -387,37 +454,37 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                 g.b_scale = L.we_down_s; g.bs_stride = d;
                 g.offs = offs; g.tile_start = tstart; g.E = E;
                 g.M = A; g.N = d; g.K = De; g.C = y; g.ldc = d;
-                run_gemm(m, DLM_K_EXPERT_DOWN, g, st, true);
+                Timed t(m, DLM_K_EXPERT_DOWN, st);
+                gemm_grouped(g, st);
+            }
+            Partials shared;
+            {
+                GemmDesc g;
+                g.dtype = gdt; g.epi = GEMM_ADD_F32;
+                g.A = opA(fi, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr); g.lda = c.d_ffn;
+                g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
+                g.B = L.w_down; g.ldb = c.d_ffn; g.b_scale = L.w_down_s;
+                g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
+                shared = dense(DLM_K_GEMM_DOWN, g, true);
             }
             {
                 Timed t(m, DLM_K_COMBINE, st);
-                moe_combine(x, y, inv, tw, R, k, d, st);
+                moe_combine(x, shared, y, inv, tw, R, k, d, st);
             }
-        }
-        // dense SwiGLU FFN, or the MoE's shared expert
-        {
-            GemmDesc g;
-            g.dtype = gdt; g.epi = GEMM_SWIGLU; g.out_f32 = f32;
-            g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
-            g.B = L.w_gate; g.B2 = L.w_up; g.ldb = d; g.b_scale = L.w_gate_s; g.b2_scale = L.w_up_s;
-            g.M = R; g.N = c.d_ffn; g.K = d; g.C = fi; g.ldc = c.d_ffn;
-            dense(DLM_K_GEMM_GATE_UP, g);
-        }
-        quant(fi, R, c.d_ffn, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr, fp8 ? at<float>(ws, p.fis) : nullptr);
-        {
+        } else {
             GemmDesc g;
             g.dtype = gdt; g.epi = GEMM_ADD_F32;
             g.A = opA(fi, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr); g.lda = c.d_ffn;
             g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
             g.B = L.w_down; g.ldb = c.d_ffn; g.b_scale = L.w_down_s;
             g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
-            dense(DLM_K_GEMM_DOWN, g);
+            pending = dense(DLM_K_GEMM_DOWN, g, true);
         }
     }
     if (mode != DENOISE) return;
 
     norm(m->w.final_norm);
-    const int nt = (c.vocab + lm_head_tile_n() - 1) / lm_head_tile_n();
+    const int nt = (c.vocab + lm_head_tile_n(R) - 1) / lm_head_tile_n(R);
     float* pmax = at<float>(ws, p.pmax);
     float* psum = at<float>(ws, p.psum);
     int* pidx = at<int>(ws, p.pidx);
@@ -620,6 +687,75 @@ dlm_status dlm_check_device_status(dlm_model* m, void* stream, int32_t* bits) {
     if (bits) *bits = v;
     if (v) return fail(DLM_E_DEVICE, "device error word 0x%x", v);
     return DLM_OK;
+}
+
+static GemmDesc op_gemm_desc(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, int32_t variant,
+                             int32_t splits) {
+    GemmDesc g;
+    g.dtype = dtype;
+    g.epi = swiglu ? GEMM_SWIGLU : GEMM_STORE_F32;
+    g.out_f32 = dtype == DLM_F32;
+    g.M = M; g.N = N; g.K = K;
+    g.lda = K; g.ldb = K; g.ldc = N;
+    g.variant = variant;
+    g.force_splits = splits;
+    return g;
+}
+
+static dlm_status op_gemm_check(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t variant, int32_t splits) {
+    if (dtype != DLM_F32 && dtype != DLM_BF16 && dtype != DLM_FP8) return fail(DLM_E_UNSUPPORTED, "dtype %d", dtype);
+    if (M < 1 || N < 1 || K < 1) return fail(DLM_E_ARG, "M, N, K must be >= 1");
+    if (((long)K * elem_bytes(dtype)) % 128) return fail(DLM_E_SHAPE, "K * element size not a multiple of 128");
+    if (variant < 0 || variant > gemm_variants()) return fail(DLM_E_ARG, "variant %d", variant);
+    if (splits < 0) return fail(DLM_E_ARG, "splits %d", splits);
+    return DLM_OK;
+}
+
+size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, int32_t variant,
+                             int32_t splits) {
+    if (op_gemm_check(dtype, M, N, K, variant, splits)) return 0;
+    return (size_t)gemm_splitk_floats(op_gemm_desc(dtype, swiglu, M, N, K, variant, splits)) * 4;
+}
+
+dlm_status dlm_op_gemm(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                       const void* B2, const float* a_scale, const float* b_scale, const float* b2_scale, void* C,
+                       void* ws, size_t ws_bytes, int32_t variant, int32_t splits, float* ms, void* stream) {
+    g_err.clear();
+    dlm_status s = op_gemm_check(dtype, M, N, K, variant, splits);
+    if (s) return s;
+    if (!A || !B || !C || (swiglu && !B2)) return fail(DLM_E_ARG, "null pointer");
+    if (dtype == DLM_FP8 && (!a_scale || !b_scale || (swiglu && !b2_scale)))
+        return fail(DLM_E_ARG, "fp8 needs a_scale, b_scale (and b2_scale)");
+    GemmDesc g = op_gemm_desc(dtype, swiglu, M, N, K, variant, splits);
+    g.a_scale = a_scale; g.b_scale = b_scale; g.b2_scale = b2_scale;
+    const long need = gemm_splitk_floats(g);
+    if (need > 0 && (!ws || ws_bytes < (size_t)need * 4))
+        return fail(DLM_E_WORKSPACE, "split-K needs %ld bytes", need * 4);
+    g.A = A; g.B = B; g.B2 = B2; g.C = C;
+    g.splitk = (float*)ws;
+    g.splitk_floats = (long)(ws_bytes / 4);
+    hipStream_t st = (hipStream_t)stream;
+    LaunchTimer lt;
+    if (ms) {
+        hipEventCreate(&lt.start);
+        hipEventCreate(&lt.stop);
+        lt.armed = true;
+        launch_timer() = &lt;
+    }
+    const int used = gemm_main(g, st);
+    launch_timer() = nullptr;
+    if (used > 1) gemm_splitk_finish(g, used, st);
+    s = hip_status("dlm_op_gemm");
+    if (ms) {
+        if (!s) {
+            hipError_t e = hipEventSynchronize(lt.stop);
+            if (e == hipSuccess) e = hipEventElapsedTime(ms, lt.start, lt.stop);
+            if (e != hipSuccess) s = fail(DLM_E_HIP, "dlm_op_gemm timing: %s", hipGetErrorString(e));
+        }
+        hipEventDestroy(lt.start);
+        hipEventDestroy(lt.stop);
+    }
+    return s;
 }
 
 dlm_status dlm_op_quant_rows(const void* x, int32_t rows, int32_t d, void* q, float* s, void* stream) {

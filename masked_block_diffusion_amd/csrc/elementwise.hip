@@ -1,8 +1,14 @@
 // Row-wise kernels of the transformer block: embedding gather, RMSNorm with the
-// GEMM-operand casts fused in (bf16, and per-token E4M3 for fp8 models),
-// per-row E4M3 quantisation, and rotary embedding fused with the K/V cache
-// write.  All are HBM/latency bound: one workgroup per token row, coalesced
-// row accesses, deterministic fixed-order reductions.
+// residual update and the GEMM-operand casts fused in (bf16, and per-token E4M3
+// for fp8 models), per-row E4M3 quantisation, and rotary embedding fused with
+// the K/V cache write.  All are HBM/latency bound: one wave per token row where
+// a row fits the wave's registers, 16-byte accesses, fixed-order reductions.
+//
+// Split-K consumers.  A weight-streaming GEMM that split its K range leaves
+// fp32 partials [splits][rows][cols]; the kernel that reads its result next
+// sums them in split order (applying the fp8 scales): RMSNorm adds the O- and
+// down-projection partials into the residual stream, RoPE sums the QKV
+// partials.
 #include "common.h"
 #include "kernels.h"
 
@@ -10,28 +16,26 @@ namespace dlm {
 
 constexpr int NT = 256;
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-    v = wave_sum(v);
-    const int w = threadIdx.x / WAVE;
-    __syncthreads();
-    if (threadIdx.x % WAVE == 0) red[w] = v;
-    __syncthreads();
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT / WAVE; ++i) s += red[i];
-    return s;
+// Value of output element (row, col) of a GEMM, from its direct fp32 output
+// (splits == 1, already scaled) or from its split-K partials.
+__device__ __forceinline__ float partial_sum(const Partials& p, int row, int col, int ncols) {
+    const long off = (long)row * ncols + col;
+    float v = 0.f;
+    for (int s = 0; s < p.splits; ++s) v += p.p[s * p.stride + off];
+    if (p.a_scale) v *= p.a_scale[row] * p.b_scale[col];
+    return v;
 }
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-    v = wave_max(v);
-    const int w = threadIdx.x / WAVE;
-    __syncthreads();
-    if (threadIdx.x % WAVE == 0) red[w] = v;
-    __syncthreads();
-    float s = red[0];
-#pragma unroll
-    for (int i = 1; i < NT / WAVE; ++i) s = fmaxf(s, red[i]);
-    return s;
+__device__ __forceinline__ f32x4 partial_sum4(const Partials& p, int row, int col, int ncols) {
+    const long off = (long)row * ncols + col;
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splits; ++s) v += *(const f32x4*)(p.p + s * p.stride + off);
+    if (p.a_scale) {
+        const float sa = p.a_scale[row];
+        const f32x4 sb = *(const f32x4*)(p.b_scale + col);
+        v = v * sa * sb;
+    }
+    return v;
 }
 
 // ------------------------------------------------------------------ embed --
@@ -59,48 +63,100 @@ __global__ __launch_bounds__(NT) void embed_kernel(IdSource ids, const void* tab
 void embed(const IdSource& ids, int rows, const void* table, int dtype, int d, int vocab,
            int mask_id, bool check_mask, float* x, int* err, hipStream_t st) {
     if (rows <= 0) return;
-    hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(NT), 0, st, ids, table, dtype, d, vocab, mask_id,
-                       (int)check_mask, x, err);
+    launch(embed_kernel, dim3(rows), dim3(NT), 0, st, ids, table, dtype, d, vocab, mask_id, (int)check_mask, x,
+           err);
 }
 
 // ---------------------------------------------------------------- rmsnorm --
+// One wave per row; lane l holds the float4 chunks l, l + 64, ... of the row
+// (d <= 4 * 64 * MAXC).  x += residual partials (if any), then
+// h = x / sqrt(mean(x^2) + eps) * g.
 
-__global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, const float* g, int d, float eps,
-                                                      float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
-    __shared__ float red[NT / WAVE];
-    const long r = blockIdx.x;
-    const float* xr = x + r * d;
+constexpr int MAXC = 16;
+
+__global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, const float* g, int rows, int d,
+                                                        float eps, float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
+    const int lane = threadIdx.x;
+    const int r = blockIdx.x;          // one single-wave workgroup per row: every row on its own CU slot
+    if (r >= rows) return;
+    const int nc = d / 4;
+    float* xr = x + (long)r * d;
+    f32x4 v[MAXC];
     float ss = 0.f;
-    for (int c = threadIdx.x; c < d; c += NT) {
-        const float v = xr[c];
-        ss += v * v;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+        const int c = lane + WAVE * k;
+        if (c < nc) {
+            v[k] = *(const f32x4*)(xr + 4 * c);
+            if (res.p) {
+                v[k] += partial_sum4(res, r, 4 * c, d);
+                *(f32x4*)(xr + 4 * c) = v[k];
+            }
+            ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+        }
     }
-    const float ms = block_sum(ss, red) / (float)d;
-    const float den = sqrtf(ms + eps);
+    if (!hf && !hb) return;                        // residual update only
+    const float den = sqrtf(wave_sum(ss) / (float)d + eps);
     float amax = 0.f;
-    for (int c = threadIdx.x; c < d; c += NT) {
-        const float h = xr[c] / den * g[c];
-        if (hf) hf[r * d + c] = h;
-        if (hb) {
-            const bf16_t b = f32_to_bf16(h);
-            hb[r * d + c] = b;
-            amax = fmaxf(amax, fabsf(bf16_to_f32(b)));
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+        const int c = lane + WAVE * k;
+        if (c < nc) {
+            const f32x4 gg = *(const f32x4*)(g + 4 * c);
+            f32x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = v[k][e] / den * gg[e];
+            if (hf) *(f32x4*)(hf + (long)r * d + 4 * c) = h;
+            if (hb) {
+                uint64_t packed = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16_t b = f32_to_bf16(h[e]);
+                    packed |= (uint64_t)b << (16 * e);
+                    v[k][e] = bf16_to_f32(b);          // keep the stored value for quantisation
+                    amax = fmaxf(amax, fabsf(v[k][e]));
+                }
+                *(uint64_t*)(hb + (long)r * d + 4 * c) = packed;
+            }
         }
     }
     if (!hq) return;
-    amax = block_max(amax, red);
+    amax = wave_max(amax);
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-    for (int c = threadIdx.x; c < d; c += NT) hq[r * d + c] = f32_to_e4m3(bf16_to_f32(hb[r * d + c]) / s);
-    if (threadIdx.x == 0) hs[r] = s;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+        const int c = lane + WAVE * k;
+        if (c < nc) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) packed |= (uint32_t)f32_to_e4m3(v[k][e] / s) << (8 * e);
+            *(uint32_t*)(hq + (long)r * d + 4 * c) = packed;
+        }
+    }
+    if (lane == 0) hs[r] = s;
 }
 
-void rmsnorm(const float* x, const float* g, int rows, int d, float eps, float* hf, uint16_t* hb,
+void rmsnorm(float* x, const Partials& res, const float* g, int rows, int d, float eps, float* hf, uint16_t* hb,
              uint8_t* hq, float* hs, hipStream_t st) {
     if (rows <= 0) return;
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(NT), 0, st, x, g, d, eps, hf, hb, hq, hs);
+    launch(rmsnorm_kernel, dim3(rows), dim3(WAVE), 0, st, x, res, g, rows, d, eps, hf, hb, hq, hs);
 }
 
+int rmsnorm_max_dim() { return 4 * WAVE * MAXC; }
+
 // ------------------------------------------------------------- quant_rows --
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x / WAVE;
+    __syncthreads();
+    if (threadIdx.x % WAVE == 0) red[w] = v;
+    __syncthreads();
+    float s = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / WAVE; ++i) s = fmaxf(s, red[i]);
+    return s;
+}
 
 __global__ __launch_bounds__(NT) void quant_rows_kernel(const bf16_t* x, int d, fp8_t* q, float* s) {
     __shared__ float red[NT / WAVE];
@@ -115,7 +171,7 @@ __global__ __launch_bounds__(NT) void quant_rows_kernel(const bf16_t* x, int d, 
 
 void quant_rows(const uint16_t* x, int rows, int d, uint8_t* q, float* s, hipStream_t st) {
     if (rows <= 0) return;
-    hipLaunchKernelGGL(quant_rows_kernel, dim3(rows), dim3(NT), 0, st, x, d, q, s);
+    launch(quant_rows_kernel, dim3(rows), dim3(NT), 0, st, x, d, q, s);
 }
 
 // ---------------------------------------------------------------- rope_kv --
@@ -124,8 +180,8 @@ void quant_rows(const uint16_t* x, int rows, int d, uint8_t* q, float* s, hipStr
 // double precision (positions reach several thousand), then applied in fp32.
 
 template <bool F32>
-__global__ __launch_bounds__(NT) void rope_kv_kernel(const float* qkv, SeqTab seqs, int layer, int hq,
-                                                      int hkv, int dh, float base, void* q_out) {
+__global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, int layer, int hq, int hkv, int dh,
+                                                      float base, void* q_out) {
     const int r = blockIdx.x;
     const int s = r / seqs.per_seq, i = r % seqs.per_seq;
     const int pos = seqs.T[s] + i;
@@ -138,10 +194,11 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(const float* qkv, SeqTab se
     sincos((double)pos * theta, &sd, &cd);
     const float sn = (float)sd, cs = (float)cd;
     const int nh = hq + 2 * hkv;
-    const float* row = qkv + (long)r * nh * dh;
+    const int ncols = nh * dh;
     const long cap = seqs.cap[s];
     for (int h = hg; h < nh; h += ngroups) {
-        const float a = row[h * dh + j], b = row[h * dh + j + half];
+        const float a = partial_sum(qkv, r, h * dh + j, ncols);
+        const float b = partial_sum(qkv, r, h * dh + j + half, ncols);
         float ra = a, rb = b;
         if (h < hq + hkv) {
             ra = a * cs - b * sn;
@@ -171,16 +228,14 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(const float* qkv, SeqTab se
     }
 }
 
-void rope_kv(const float* qkv, int rows, const SeqTab& seqs, int layer, int n_layers, int hq, int hkv,
-             int dh, float base, bool f32, void* q_out, hipStream_t st) {
+void rope_kv(const Partials& qkv, int rows, const SeqTab& seqs, int layer, int n_layers, int hq, int hkv, int dh,
+             float base, bool f32, void* q_out, hipStream_t st) {
     (void)n_layers;
     if (rows <= 0) return;
     if (f32)
-        hipLaunchKernelGGL(rope_kv_kernel<true>, dim3(rows), dim3(NT), 0, st, qkv, seqs, layer, hq, hkv, dh,
-                           base, q_out);
+        launch(rope_kv_kernel<true>, dim3(rows), dim3(NT), 0, st, qkv, seqs, layer, hq, hkv, dh, base, q_out);
     else
-        hipLaunchKernelGGL(rope_kv_kernel<false>, dim3(rows), dim3(NT), 0, st, qkv, seqs, layer, hq, hkv, dh,
-                           base, q_out);
+        launch(rope_kv_kernel<false>, dim3(rows), dim3(NT), 0, st, qkv, seqs, layer, hq, hkv, dh, base, q_out);
 }
 
 }  // namespace dlm

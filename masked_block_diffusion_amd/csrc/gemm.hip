@@ -124,6 +124,19 @@ struct Core {
                                              0, 0);
     }
 
+    // One MFMA step into an fp32 accumulator.  fp8: the instruction starts
+    // from zero and its 32-term result is added on the vector ALU, so the
+    // running sum is kept in full fp32 (accumulating inside the fp8 MFMA
+    // measured far outside the fp32 rounding bound on this chip).
+    __device__ __forceinline__ static f32x4 mac(frag a, frag b, f32x4 c) {
+        if constexpr (sizeof(T) == 1) {
+            const f32x4 t = Mfma<T>::mma(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+            return c + t;
+        } else {
+            return Mfma<T>::mma(a, b, c);
+        }
+    }
+
     __device__ __forceinline__ void compute(const uint8_t* stage) {
         const int lane = threadIdx.x % WAVE;
         const int wm = wave / WN, wn = wave % WN;
@@ -142,7 +155,7 @@ struct Core {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::mma(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = mac(af[i], bf[j], acc[i][j]);
             if constexpr (DUAL) {
                 frag bf2[TN];
 #pragma unroll
@@ -150,7 +163,7 @@ struct Core {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) acc2[i][j] = Mfma<T>::mma(af[i], bf2[j], acc2[i][j]);
+                    for (int j = 0; j < TN; ++j) acc2[i][j] = mac(af[i], bf2[j], acc2[i][j]);
             }
         }
     }
@@ -419,15 +432,23 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs a) {
 
 // Tile shapes (BM, BN, WM, WN, stages):
 //   small M (<= 64; the tiny model, short canvases)     32 x 64,  waves 1x4, 4 stages
-//   canvas M (<= 256; one request's canvas)             256 x 64, waves 4x1, 3 stages
+//   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2, 4 stages
+//     (SwiGLU pair: 128 x 64 x 2 weights if N >= 4096, else 64 x 32 x 2)
 //   prefill M                                           128 x 128, waves 2x2, 4 stages
-//   LM head (whole-tile columns per wave)               64 x 64 / 256 x 64, waves 4x1
+//   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128, waves 4x1
 //   grouped (experts)                                   GROUPED_BM x 64, waves 1x4, 4 stages
+// The canvas choices come from a sweep of every variant and split factor on
+// the workloads' projection shapes: small tiles give enough workgroups to keep
+// weight bytes in flight on every CU; the m-tiles sharing a weight tile are
+// adjacent in the XCD-aware order, so the weights are fetched from HBM once.
+// The wider LM-head tile halves the activation re-reads over the vocabulary.
 template <typename T, bool DUAL> using CoreS = Core<T, 32, 64, 1, 4, DUAL, 4>;
-template <typename T, bool DUAL> using CoreW = Core<T, 256, 64, 4, 1, DUAL, 3>;
+template <typename T, bool DUAL> using CoreM = Core<T, 64, 64, 2, 2, DUAL, 4>;
+template <typename T, bool DUAL>
+using CoreW = std::conditional_t<DUAL, Core<T, 128, 64, 2, 2, true, 4>, Core<T, 256, 64, 4, 1, false, 3>>;
 template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4>;
 template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
-template <typename T> using CoreHw = Core<T, 256, 64, 4, 1, false, 3>;
+template <typename T> using CoreHw = Core<T, 256, 128, 4, 1, false, 3>;
 template <typename T, bool DUAL> using CoreG = Core<T, GROUPED_BM, 64, 1, 4, DUAL, 4>;
 
 constexpr int SPLIT_TARGET_WG = 256;
@@ -440,10 +461,16 @@ static int splits_for(const GemmDesc& d) {
     if constexpr (EPI == EPI_LMHEAD) return 1;
     const long tiles = (long)((d.M + C::BM - 1) / C::BM) * ((d.N + C::BN - 1) / C::BN);
     const int nkt = (int)((long)d.K * sizeof(T) / BKB);
-    if (tiles >= SPLIT_TARGET_WG * 3 / 4 || d.M > 256) return 1;
+    if (d.force_splits > 0) {
+        const int per = (nkt + std::min(d.force_splits, nkt) - 1) / std::min(d.force_splits, nkt);
+        return (nkt + per - 1) / per;
+    }
+    // a SwiGLU split would need its own epilogue kernel (the nonlinearity
+    // needs the full sums): never split it
+    if (C::TWO_B || tiles >= SPLIT_TARGET_WG * 3 / 4 || d.M > 256) return 1;
     int s = (int)((SPLIT_TARGET_WG + tiles - 1) / tiles);
     s = std::min(s, std::max(1, nkt / 4));
-    s = std::min(s, 16);
+    s = std::min(s, 2);
     const int per = (nkt + s - 1) / s;
     return std::max(1, (nkt + per - 1) / per);
 }
@@ -463,8 +490,9 @@ static EpiArgs make_epi(const GemmDesc& d, int bn) {
     return e;
 }
 
+// Launches the GEMM; returns its split-K factor.
 template <class C, typename T, bool DUAL, int EPI>
-static void launch_dense(const GemmDesc& d, hipStream_t st) {
+static int launch_dense(const GemmDesc& d, hipStream_t st) {
     DenseArgs a;
     a.A = (const uint8_t*)d.A; a.lda = d.lda * (long)sizeof(T);
     a.B = (const uint8_t*)d.B; a.B2 = (const uint8_t*)d.B2; a.ldb = d.ldb * (long)sizeof(T);
@@ -475,11 +503,18 @@ static void launch_dense(const GemmDesc& d, hipStream_t st) {
     a.part = d.splitk;
     a.e = make_epi(d, C::BN);
     const int grid = ((d.M + C::BM - 1) / C::BM) * ((d.N + C::BN - 1) / C::BN) * a.splits;
-    if (grid == 0) return;
-    hipLaunchKernelGGL((gemm_dense_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
-    if (a.splits > 1)
-        hipLaunchKernelGGL((splitk_epilogue_kernel<EPI, sizeof(T) == 1, DUAL>), dim3((d.N + 255) / 256, d.M),
-                           dim3(256), 0, st, d.splitk, a.splits, d.M, d.N, a.e);
+    if (grid == 0) return 1;
+    launch((gemm_dense_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
+    return a.splits;
+}
+
+template <typename T, bool DUAL, int EPI>
+static void finish_dense(const GemmDesc& d, int splits, hipStream_t st) {
+    if constexpr (EPI != EPI_LMHEAD) {
+        const EpiArgs e = make_epi(d, 64);
+        launch((splitk_epilogue_kernel<EPI, sizeof(T) == 1, DUAL>), dim3((d.N + 255) / 256, d.M),
+                           dim3(256), 0, st, d.splitk, splits, d.M, d.N, e);
+    }
 }
 
 template <class C, typename T, int EPI>
@@ -495,41 +530,87 @@ static void launch_grouped(const GemmDesc& d, hipStream_t st) {
     a.e = make_epi(d, C::BN);
     const int grid = a.max_mtiles * ((d.N + C::BN - 1) / C::BN);
     if (d.M == 0 || grid == 0) return;
-    hipLaunchKernelGGL((gemm_grouped_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
+    launch((gemm_grouped_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
 }
+
+// Tile variants a caller may force (GemmDesc::variant, the GEMM test entry
+// point): bf16 operands, fp32-store or SwiGLU epilogue.
+template <typename T, bool DUAL, class F>
+static bool with_variant(int v, F f) {
+    switch (v) {
+        case 1: f(Core<T, 128, 64, 2, 2, DUAL, 4>{}); return true;
+        case 2: f(Core<T, 64, 64, 2, 2, DUAL, 4>{}); return true;
+        case 3: f(Core<T, 256, 64, 4, 1, DUAL, 3>{}); return true;
+        case 4: f(Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4>{}); return true;
+        case 5: f(Core<T, 64, 128, 2, 2, DUAL, DUAL ? 3 : 4>{}); return true;
+        case 6: f(Core<T, 64, 32, 2, 2, DUAL, 4>{}); return true;
+        case 7: f(Core<T, 32, 64, 1, 4, DUAL, 4>{}); return true;
+        case 8: f(Core<T, 64, 64, 2, 2, DUAL, 6>{}); return true;
+        default: return false;
+    }
+}
+constexpr int GEMM_VARIANTS = 8;
 
 template <bool DUAL, int EPI, typename T, class F>
 static void with_core(const GemmDesc& d, F f) {
+    if constexpr (std::is_same_v<T, bf16_t> && (EPI == EPI_F32 || EPI == EPI_SWIGLU_BF16)) {
+        if (d.variant && with_variant<T, DUAL>(d.variant, f)) return;
+    }
     if constexpr (EPI == EPI_LMHEAD) {
         if (d.M <= 64) f(CoreHs<T>{});
         else f(CoreHw<T>{});
     } else {
         if (d.M <= 64) f(CoreS<T, DUAL>{});
-        else if (d.M <= 256) f(CoreW<T, DUAL>{});
-        else f(CoreL<T, DUAL>{});
+        else if (d.M <= 256) {
+            // measured on the canvas shapes (M = 256) with weights streamed
+            // from HBM: 64 x 64 tiles for the projections; a SwiGLU pair gets
+            // 128 x 64 tiles when wide, 64 x 32 when narrow
+            if constexpr (DUAL) {
+                if (d.N >= 4096) f(Core<T, 128, 64, 2, 2, true, 4>{});
+                else f(Core<T, 64, 32, 2, 2, true, 4>{});
+            } else {
+                f(CoreM<T, false>{});
+            }
+        } else f(CoreL<T, DUAL>{});
     }
 }
 
+enum DenseOp { OP_LAUNCH, OP_NEED, OP_FINISH };
+
+// OP_LAUNCH: launch, *io = splits.  OP_NEED: *io = partial floats.
+// OP_FINISH: split-K epilogue for *io splits.
 template <typename T, bool DUAL, int EPI>
-static void dense_t(const GemmDesc& d, hipStream_t st, long* need) {
+static void dense_t(const GemmDesc& d, hipStream_t st, DenseOp op, long* io) {
+    if (op == OP_FINISH) {
+        finish_dense<T, DUAL, EPI>(d, (int)*io, st);
+        return;
+    }
     with_core<DUAL, EPI, T>(d, [&](auto core) {
         using C = decltype(core);
-        if (need) *need = part_floats<C, T, DUAL, EPI>(d);
-        else launch_dense<C, T, DUAL, EPI>(d, st);
+        if (op == OP_NEED) *io = part_floats<C, T, DUAL, EPI>(d);
+        else *io = launch_dense<C, T, DUAL, EPI>(d, st);
     });
 }
 
 template <typename T>
-static void gemm_t(const GemmDesc& d, hipStream_t st, long* need) {
+static void gemm_t(const GemmDesc& d, hipStream_t st, DenseOp op, long* io) {
     switch (d.epi) {
-        case GEMM_STORE_F32: dense_t<T, false, EPI_F32>(d, st, need); break;
-        case GEMM_STORE_BF16: dense_t<T, false, EPI_BF16>(d, st, need); break;
-        case GEMM_ADD_F32: dense_t<T, false, EPI_ADD_F32>(d, st, need); break;
+        case GEMM_STORE_F32: dense_t<T, false, EPI_F32>(d, st, op, io); break;
+        case GEMM_STORE_BF16: dense_t<T, false, EPI_BF16>(d, st, op, io); break;
+        case GEMM_ADD_F32: dense_t<T, false, EPI_ADD_F32>(d, st, op, io); break;
         case GEMM_SWIGLU:
-            if (d.out_f32) dense_t<T, true, EPI_SWIGLU_F32>(d, st, need);
-            else dense_t<T, true, EPI_SWIGLU_BF16>(d, st, need);
+            if (d.out_f32) dense_t<T, true, EPI_SWIGLU_F32>(d, st, op, io);
+            else dense_t<T, true, EPI_SWIGLU_BF16>(d, st, op, io);
             break;
-        case GEMM_LMHEAD: dense_t<T, false, EPI_LMHEAD>(d, st, need); break;
+        case GEMM_LMHEAD: dense_t<T, false, EPI_LMHEAD>(d, st, op, io); break;
+    }
+}
+
+static void gemm_op(const GemmDesc& d, hipStream_t st, DenseOp op, long* io) {
+    switch (d.dtype) {
+        case DT_F32: gemm_t<float>(d, st, op, io); break;
+        case DT_BF16: gemm_t<bf16_t>(d, st, op, io); break;
+        case DT_FP8: gemm_t<fp8_t>(d, st, op, io); break;
     }
 }
 
@@ -545,21 +626,20 @@ static void grouped_t(const GemmDesc& d, hipStream_t st) {
     }
 }
 
-void gemm(const GemmDesc& d, hipStream_t st) {
-    switch (d.dtype) {
-        case DT_F32: gemm_t<float>(d, st, nullptr); break;
-        case DT_BF16: gemm_t<bf16_t>(d, st, nullptr); break;
-        case DT_FP8: gemm_t<fp8_t>(d, st, nullptr); break;
-    }
+int gemm_main(const GemmDesc& d, hipStream_t st) {
+    long splits = 1;
+    gemm_op(d, st, OP_LAUNCH, &splits);
+    return (int)splits;
+}
+
+void gemm_splitk_finish(const GemmDesc& d, int splits, hipStream_t st) {
+    long s = splits;
+    if (splits > 1) gemm_op(d, st, OP_FINISH, &s);
 }
 
 long gemm_splitk_floats(const GemmDesc& d) {
     long need = 0;
-    switch (d.dtype) {
-        case DT_F32: gemm_t<float>(d, nullptr, &need); break;
-        case DT_BF16: gemm_t<bf16_t>(d, nullptr, &need); break;
-        case DT_FP8: gemm_t<fp8_t>(d, nullptr, &need); break;
-    }
+    gemm_op(d, nullptr, OP_NEED, &need);
     return need;
 }
 
@@ -571,6 +651,8 @@ void gemm_grouped(const GemmDesc& d, hipStream_t st) {
     }
 }
 
-int lm_head_tile_n() { return 64; }
+int gemm_variants() { return GEMM_VARIANTS; }
+
+int lm_head_tile_n(int M) { return M <= 64 ? CoreHs<bf16_t>::BN : CoreHw<bf16_t>::BN; }
 
 }  // namespace dlm

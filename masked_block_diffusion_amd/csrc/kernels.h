@@ -1,10 +1,33 @@
 // Host-side launchers of the gfx950 kernels.  Every launcher enqueues on the
 // given stream and returns immediately; shapes are validated by the caller.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dlm {
+
+// Kernel timing: while a LaunchTimer is armed on this thread, the next kernel
+// launched through launch() carries its start / stop events in its own
+// dispatch (hipExtLaunchKernelGGL), so the elapsed time is that kernel's
+// execution, without separate marker packets around it.
+struct LaunchTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool armed = false;
+};
+LaunchTimer*& launch_timer();
+
+template <typename... KArgs, typename... Args>
+inline void launch(void (*k)(KArgs...), dim3 grid, dim3 block, uint32_t shm, hipStream_t st, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    LaunchTimer* t = launch_timer();
+    if (t && t->armed) {
+        t->armed = false;
+        e0 = t->start;
+        e1 = t->stop;
+    }
+    hipExtLaunchKernelGGL(k, grid, block, shm, st, e0, e1, 0, args...);
+}
 
 enum DType { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
@@ -28,7 +51,7 @@ struct GemmDesc {
     const float* b2_scale = nullptr;
     int M = 0, N = 0, K = 0;
     void* C = nullptr; long ldc = 0;
-    // LM head reduction: partials [M, ceil(N / lm_head_tile_n())]
+    // LM head reduction: partials [M, ceil(N / lm_head_tile_n(M))]
     float* pmax = nullptr; float* psum = nullptr; int* pidx = nullptr;
     int mask_col = -1;
     float* logits = nullptr; long ld_logits = 0;
@@ -41,14 +64,24 @@ struct GemmDesc {
     int E = 0;
     // split-K (dense GEMMs): fp32 partials [splits][M][N] (x2 for SwiGLU)
     float* splitk = nullptr; long splitk_floats = 0;
+    // forced tile variant (1..gemm_variants(); bf16 store / SwiGLU only) and split factor; 0 = chosen by shape
+    int variant = 0;
+    int force_splits = 0;
 };
+int gemm_variants();
 
 // Dense and grouped GEMMs.  K * element size must be a multiple of 128 bytes.
-void gemm(const GemmDesc& d, hipStream_t st);
+// gemm_main launches the GEMM and returns its split-K factor; when that is
+// above 1, gemm_splitk_finish(d, splits) must follow on the same stream (it
+// sums the partials in split order and applies the epilogue).
+int gemm_main(const GemmDesc& d, hipStream_t st);
+void gemm_splitk_finish(const GemmDesc& d, int splits, hipStream_t st);
 void gemm_grouped(const GemmDesc& d, hipStream_t st);
 // fp32 partial space the dense GEMM d uses for split-K (0 if unsplit)
 long gemm_splitk_floats(const GemmDesc& d);
-int lm_head_tile_n();
+// vocab columns per LM-head tile (one partial per row and tile) for M rows;
+// the narrowest tile is used for M <= 64
+int lm_head_tile_n(int M);
 
 // Token ids of one forward: one flat array, or per-request canvases.
 struct IdSource {
@@ -71,20 +104,34 @@ struct SeqTab {
 void embed(const IdSource& ids, int rows, const void* table, int dtype, int d, int vocab,
            int mask_id, bool check_mask, float* x, int* err, hipStream_t st);
 
-// h = x / sqrt(mean(x^2) + eps) * g per row, written to every non-null output:
-// hf fp32, hb bf16, and (fp8 models) hq E4M3 codes with per-row scales hs
-// quantised from the bf16 value.
-void rmsnorm(const float* x, const float* g, int rows, int d, float eps, float* hf,
+// A GEMM result [rows, cols] as its consumer reads it: the direct fp32 output
+// (splits = 1, no scales) or split-K partials p[s * stride + row * cols + col],
+// s < splits, times a_scale[row] * b_scale[col] when the scales are set (fp8).
+struct Partials {
+    const float* p = nullptr;
+    int splits = 1;
+    long stride = 0;
+    const float* a_scale = nullptr;
+    const float* b_scale = nullptr;
+};
+
+// x += res (when res.p is set; the residual update of a split O / down
+// projection), then h = x / sqrt(mean(x^2) + eps) * g per row, written to every
+// non-null output: hf fp32, hb bf16, and (fp8 models) hq E4M3 codes with
+// per-row scales hs quantised from the bf16 value.  d <= rmsnorm_max_dim(),
+// d % 4 == 0.
+int rmsnorm_max_dim();
+void rmsnorm(float* x, const Partials& res, const float* g, int rows, int d, float eps, float* hf,
              uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st);
 
 // Per-row E4M3 quantisation of a bf16 matrix [rows, d]: s = amax / 448 (1 for a
 // zero row), q = e4m3(x / s).
 void quant_rows(const uint16_t* x, int rows, int d, uint8_t* q, float* s, hipStream_t st);
 
-// RoPE on Q and K of qkv (fp32 [rows, (Hq + 2 Hkv) * dh]) at absolute positions
-// T_r + i; Q -> q_out [rows, Hq * dh]; K, V -> cache slots T_r + i of layer l.
-// Element type of q_out and the cache: fp32 (f32 models) or bf16.
-void rope_kv(const float* qkv, int rows, const SeqTab& seqs, int layer, int n_layers, int hq,
+// RoPE on Q and K of qkv ([rows, (Hq + 2 Hkv) * dh], see Partials) at absolute
+// positions T_r + i; Q -> q_out [rows, Hq * dh]; K, V -> cache slots T_r + i of
+// layer l.  Element type of q_out and the cache: fp32 (f32 models) or bf16.
+void rope_kv(const Partials& qkv, int rows, const SeqTab& seqs, int layer, int n_layers, int hq,
              int hkv, int dh, float base, bool f32, void* q_out, hipStream_t st);
 
 // Attention of rows' queries (q [rows, Hq * dh]) over request r's cache slots
@@ -94,6 +141,7 @@ struct AttnWork {
     float* o_part;      // split-KV partial outputs
     float* ml_part;     // split-KV partial (max, sum)
     long capacity;      // floats available in o_part
+    LaunchTimer* merge_timer;   // timer for the split-KV merge kernel (nullable)
 };
 void attention(const void* q, const SeqTab& seqs, int layer, int n_layers, int hq, int hkv,
                int dh, bool causal, bool f32, void* out, const AttnWork& w, hipStream_t st);
@@ -112,9 +160,11 @@ void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, 
                int* inv, const RouteWork& w, hipStream_t st);
 int route_blocks(int n_assign);
 
-// x[r] += sum_s w[r, s] * y[inv[r * k + s]]   (y fp32 [A, d] in sorted order)
-void moe_combine(float* x, const float* y, const int* inv, const float* w, int rows, int k, int d,
-                 hipStream_t st);
+// x[r] += shared[r] + sum_s w[r, s] * y[inv[r * k + s]]   (y fp32 [A, d] in
+// sorted order; shared: the shared expert's down projection as Partials, or
+// nothing when shared.p is null)
+void moe_combine(float* x, const Partials& shared, const float* y, const int* inv, const float* w, int rows, int k,
+                 int d, hipStream_t st);
 
 // LM-head partials (max, sum exp, argmax) per (row, vocab tile) -> conf = 1/Z,
 // pred = lowest argmax.

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, i
 void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
                  float* logits_copy, hipStream_t st) {
     if (rows <= 0) return;
-    hipLaunchKernelGGL(router_topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, logits, rows, E, k, ids, w,
+    launch(router_topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, logits, rows, E, k, ids, w,
                        ids_copy, logits_copy);
 }
 
@@ -152,27 +152,33 @@ void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, 
                const RouteWork& w, hipStream_t st) {
     const int nb = route_blocks(n_assign);
     if (nb == 0) return;
-    hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank);
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(256), 0, st, w.hist, nb, E, GROUPED_BM, offs, tile_start);
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank,
+    launch(route_hist_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank);
+    launch(route_scan_kernel, dim3(1), dim3(256), 0, st, w.hist, nb, E, GROUPED_BM, offs, tile_start);
+    launch(route_scatter_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank,
                        sorted_assign, inv);
 }
 
 // ---------------------------------------------------------------- combine --
 
-__global__ __launch_bounds__(256) void moe_combine_kernel(float* x, const float* y, const int* inv, const float* w,
-                                                           int k, int d) {
+__global__ __launch_bounds__(256) void moe_combine_kernel(float* x, Partials shared, const float* y,
+                                                           const int* inv, const float* w, int k, int d) {
     const long r = blockIdx.x;
     for (int c = threadIdx.x; c < d; c += 256) {
         float acc = 0.f;
+        if (shared.p) {
+            const long off = r * d + c;
+            for (int s = 0; s < shared.splits; ++s) acc += shared.p[s * shared.stride + off];
+            if (shared.a_scale) acc *= shared.a_scale[r] * shared.b_scale[c];
+        }
         for (int s = 0; s < k; ++s) acc += w[r * k + s] * y[(long)inv[r * k + s] * d + c];
         x[r * d + c] += acc;
     }
 }
 
-void moe_combine(float* x, const float* y, const int* inv, const float* w, int rows, int k, int d, hipStream_t st) {
+void moe_combine(float* x, const Partials& shared, const float* y, const int* inv, const float* w, int rows, int k,
+                 int d, hipStream_t st) {
     if (rows <= 0) return;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3(rows), dim3(256), 0, st, x, y, inv, w, k, d);
+    launch(moe_combine_kernel, dim3(rows), dim3(256), 0, st, x, shared, y, inv, w, k, d);
 }
 
 }  // namespace dlm

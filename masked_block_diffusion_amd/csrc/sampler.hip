@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const float* pmax, const 
 void lm_merge(const float* pmax, const float* psum, const int* pidx, int rows, int n_tiles, float* conf, int* pred,
               hipStream_t st) {
     if (rows <= 0) return;
-    hipLaunchKernelGGL(lm_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, pmax, psum, pidx, rows, n_tiles,
+    launch(lm_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, pmax, psum, pidx, rows, n_tiles,
                        conf, pred);
 }
 
@@ -112,7 +112,7 @@ void commit(int32_t* const* canvases, int n_seqs, int C, const float* conf, cons
     if (n_seqs <= 0) return;
     CanvasTab tab;
     for (int i = 0; i < n_seqs; ++i) tab.c[i] = canvases[i];
-    hipLaunchKernelGGL(commit_kernel, dim3(n_seqs), dim3(256), 0, st, tab, C, conf, pred, mask_id, kind, k, thr,
+    launch(commit_kernel, dim3(n_seqs), dim3(256), 0, st, tab, C, conf, pred, mask_id, kind, k, thr,
                        (int)force_all, n_committed, n_masked);
 }
 

@@ -80,3 +80,127 @@ def test_quant_rows_rejects_bad_args():
     assert lib.dlm_op_quant_rows(None, 1, 1, None, None, None) == abi.DLM_E_ARG
     x = torch.zeros(4, dtype=torch.bfloat16, device="cuda")
     assert lib.dlm_op_quant_rows(x.data_ptr(), 0, 4, x.data_ptr(), x.data_ptr(), None) == abi.DLM_E_ARG
+
+
+def _bf16_tensor(shape, g):
+    return (torch.randn(*shape, generator=g) * 0.5).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("variant,splits", [(v, 0) for v in range(9)] + [(3, 2), (2, 4), (1, 3), (0, 5)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (37, 200, 1536), (256, 512, 2048), (300, 136, 256)])
+def test_gemm_variants_match_fp64(variant, splits, M, N, K):
+    """Every tile variant and split factor of the dense GEMM, ragged M / N,
+    against a float64 product of the same bf16 values (fp32 accumulation:
+    relative error bounded by K * 2^-24 of sum |a||b|)."""
+    import ctypes
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    g = torch.Generator().manual_seed(M * 1000 + N + K)
+    A, B, B2 = _bf16_tensor((M, K), g), _bf16_tensor((N, K), g), _bf16_tensor((N, K), g)
+    ref = A.double() @ B.double().T
+    ref2 = A.double() @ B2.double().T
+    bound = (A.double().abs() @ B.double().abs().T) * K * 2.0 ** -24 + 1e-30
+    bound2 = (A.double().abs() @ B2.double().abs().T) * K * 2.0 ** -24 + 1e-30
+    st = torch.cuda.current_stream().cuda_stream
+    for swiglu in (0, 1):
+        nws = lib.dlm_op_gemm_workspace(abi.DLM_BF16, swiglu, M, N, K, variant, splits)
+        ws = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+        C = torch.empty((M, N), dtype=torch.float32 if not swiglu else torch.bfloat16, device="cuda")
+        Ad, Bd, B2d = A.cuda(), B.cuda(), B2.cuda()
+        abi.check(lib.dlm_op_gemm(abi.DLM_BF16, swiglu, M, N, K, Ad.data_ptr(), Bd.data_ptr(), B2d.data_ptr(),
+                                  None, None, None, C.data_ptr(), ws.data_ptr(), ws.numel(), variant, splits,
+                                  None, st), "gemm")
+        torch.cuda.synchronize()
+        got = C.double().cpu()
+        if not swiglu:
+            assert torch.all((got - ref).abs() <= bound), f"max excess {((got - ref).abs() - bound).max()}"
+        else:
+            want = torch.nn.functional.silu(ref) * ref2
+            # the bf16 store rounds: half an ulp of the result, plus the propagated accumulation error
+            tol = want.abs() * 2.0 ** -8 + bound * (ref2.abs() + 1) + bound2 * (ref.abs() + 1) + 1e-6
+            assert torch.all((got - want).abs() <= tol), f"max excess {((got - want).abs() - tol).max()}"
+
+
+def test_gemm_f32_matches_fp64():
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    g = torch.Generator().manual_seed(7)
+    M, N, K = 32, 520, 128
+    A, B = torch.randn(M, K, generator=g), torch.randn(N, K, generator=g)
+    ref = A.double() @ B.double().T
+    bound = (A.double().abs() @ B.double().abs().T) * K * 2.0 ** -22
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    nws = lib.dlm_op_gemm_workspace(abi.DLM_F32, 0, M, N, K, 0, 0)
+    ws = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+    Ad, Bd = A.cuda(), B.cuda()          # keep both alive while the kernel runs
+    abi.check(lib.dlm_op_gemm(abi.DLM_F32, 0, M, N, K, Ad.data_ptr(), Bd.data_ptr(), None, None, None, None,
+                              C.data_ptr(), ws.data_ptr(), ws.numel(), 0, 0, None, st), "gemm")
+    torch.cuda.synchronize()
+    assert torch.all((C.double().cpu() - ref).abs() <= bound)
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(256, 320, 512, 0), (64, 128, 2560, 0), (37, 200, 768, 2),
+                                          (300, 64, 128, 0)])
+def test_gemm_fp8_matches_fp64(M, N, K, splits):
+    """E4M3 codes covering every finite value (subnormals, both zeros) with
+    per-row / per-column scales, against the oracle's decoding in float64.
+    Products of two E4M3 values are exact in fp32; the sum is fp32."""
+    from masked_block_diffusion_amd import abi
+    from oracle.numerics import e4m3_decode
+    lib = abi.load_library()
+    rng = np.random.default_rng(M + N + K)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    A = rng.choice(finite, size=(M, K)).astype(np.uint8)
+    B = rng.choice(finite, size=(N, K)).astype(np.uint8)
+    B2 = rng.choice(finite, size=(N, K)).astype(np.uint8)
+    sa = rng.uniform(0.5, 2.0, M).astype(np.float32)
+    sb = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    sb2 = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    Ad, Bd, B2d = e4m3_decode(A), e4m3_decode(B), e4m3_decode(B2)
+    raw = Ad @ Bd.T
+    ref = raw * sa[:, None].astype(np.float64) * sb[None, :].astype(np.float64)
+    bound = (np.abs(Ad) @ np.abs(Bd).T) * K * 2.0 ** -24 * sa[:, None] * sb[None, :] + np.abs(ref) * 2.0 ** -22
+    t = {k: torch.from_numpy(v).cuda() for k, v in dict(A=A, B=B, B2=B2, sa=sa, sb=sb, sb2=sb2).items()}
+    st = torch.cuda.current_stream().cuda_stream
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nws = lib.dlm_op_gemm_workspace(abi.DLM_FP8, 0, M, N, K, 0, splits)
+    ws = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+    abi.check(lib.dlm_op_gemm(abi.DLM_FP8, 0, M, N, K, t["A"].data_ptr(), t["B"].data_ptr(), t["B2"].data_ptr(),
+                              t["sa"].data_ptr(), t["sb"].data_ptr(), t["sb2"].data_ptr(), C.data_ptr(),
+                              ws.data_ptr(), ws.numel(), 0, splits, None, st), "gemm fp8")
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} differ; worst rel "
+                           f"{np.max(np.abs(got - ref) / (np.abs(ref) + 1e-30)):.3g}; "
+                           f"e.g. got {got[bad][:3]} want {ref[bad][:3]}")
+
+
+def test_gemm_fp8_small_integers_exact():
+    """E4M3 codes of small integers (1..16, both signs) with unit scales: every
+    partial sum is an integer below 2^24, so any summation order is exact."""
+    from masked_block_diffusion_amd import abi
+    from oracle.numerics import e4m3_decode, e4m3_encode
+    lib = abi.load_library()
+    rng = np.random.default_rng(5)
+    M, N, K = 300, 136, 512
+    vals = np.array([v for v in range(-16, 17) if v != 0 and abs(e4m3_decode(e4m3_encode(v))) == abs(v)], float)
+    A = e4m3_encode(rng.choice(vals, size=(M, K)))
+    B = e4m3_encode(rng.choice(vals, size=(N, K)))
+    ref = e4m3_decode(A) @ e4m3_decode(B).T
+    t = {k: torch.from_numpy(v).cuda() for k, v in dict(A=A, B=B).items()}
+    ones_m = torch.ones(M, dtype=torch.float32, device="cuda")
+    ones_n = torch.ones(N, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for variant_m in (M, 64, 256):                 # the three tile classes (prefill / small / canvas)
+        mm = min(M, variant_m)
+        C = torch.empty((mm, N), dtype=torch.float32, device="cuda")
+        nws = lib.dlm_op_gemm_workspace(abi.DLM_FP8, 0, mm, N, K, 0, 0)
+        ws = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+        abi.check(lib.dlm_op_gemm(abi.DLM_FP8, 0, mm, N, K, t["A"].data_ptr(), t["B"].data_ptr(), None,
+                                  ones_m.data_ptr(), ones_n.data_ptr(), None, C.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), 0, 0, None, st), "gemm fp8")
+        torch.cuda.synchronize()
+        got = C.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref[:mm]), f"M={mm}: {np.sum(got != ref[:mm])} differ"
