@@ -87,19 +87,20 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------- MFMA traits --
-// Per element type: K covered by one 16x16 MFMA, bytes one lane supplies per
-// operand, and the instruction.  Fragment layout of all three (16x16xK):
-// lane l supplies row (l % 16) of A / column (l % 16) of B, K elements
-// [ (l/16) * K/4, (l/16) * K/4 + K/4 ); the 4 fp32 results of lane l are
-// D[4 * (l/16) + i][l % 16], i = 0..3.
+// Per element type: K covered by one step of the 16x16 tile, bytes one lane
+// reads per operand and step, the register operand those bytes become, and
+// the multiply-accumulate.  bf16 / f32 (one MFMA 16x16xK): lane l supplies row
+// (l % 16) of A / column (l % 16) of B, K elements [(l/16) K/4, (l/16) K/4 +
+// K/4); the 4 fp32 results of lane l are D[4 (l/16) + i][l % 16], i = 0..3.
 
 template <typename T> struct Mfma;
 
 template <> struct Mfma<float> {
-    static constexpr int KSTEP = 4;            // elements per MFMA
+    static constexpr int KSTEP = 4;            // elements per step
     static constexpr int LANE_BYTES = 4;
     typedef float frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    __device__ __forceinline__ static frag load(const uint8_t* p) { return *(const frag*)p; }
+    __device__ __forceinline__ static f32x4 mac(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
 };
@@ -107,16 +108,40 @@ template <> struct Mfma<bf16_t> {
     static constexpr int KSTEP = 32;
     static constexpr int LANE_BYTES = 16;
     typedef bf16x8 frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    __device__ __forceinline__ static frag load(const uint8_t* p) { return *(const frag*)p; }
+    __device__ __forceinline__ static f32x4 mac(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
+
+// E4M3 operands are widened in registers to bf16 (exact: 4 exponent and 3
+// mantissa bits fit bf16's 8 and 7, subnormals included) and multiplied on
+// the bf16 MFMA, whose fp32 accumulation meets the fp32 rounding bound; the
+// fp8 MFMA's own 32-term sums measured about 2^-15 of sum|ab| off on this
+// chip, independent of K.  The bytes in HBM and LDS stay one per element.
+// A step covers K = 64: lane l reads codes k = 16 (l/16) .. 16 (l/16) + 15 of
+// the step and splits them into two bf16 fragments (the low and high 8);
+// A and B use the same assignment, so the two MFMAs add up all 64 products.
+__device__ __forceinline__ bf16x8 widen_e4m3x8(uint32_t w0, uint32_t w1) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 template <> struct Mfma<fp8_t> {
-    static constexpr int KSTEP = 32;
-    static constexpr int LANE_BYTES = 8;
-    typedef long frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+    static constexpr int KSTEP = 64;
+    static constexpr int LANE_BYTES = 16;
+    struct frag { bf16x8 lo, hi; };
+    __device__ __forceinline__ static frag load(const uint8_t* p) {
+        const u32x4 w = *(const u32x4*)p;
+        return frag{widen_e4m3x8(w.x, w.y), widen_e4m3x8(w.z, w.w)};
+    }
+    __device__ __forceinline__ static f32x4 mac(const frag& a, const frag& b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.lo, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
     }
 };
 

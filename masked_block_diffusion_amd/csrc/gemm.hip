@@ -73,7 +73,7 @@ struct Core {
     static constexpr bool TWO_B = DUAL;
     static constexpr int TM = BM / WM / 16;
     static constexpr int TN = BN / WN / 16;
-    static constexpr int KSB = Mfma<T>::KSTEP * (int)sizeof(T);   // bytes per MFMA k-step
+    static constexpr int KSB = Mfma<T>::KSTEP * (int)sizeof(T);   // K bytes per step
     static constexpr int LB = Mfma<T>::LANE_BYTES;
     static constexpr int ROWS = BM + BN * (DUAL ? 2 : 1);           // rows per stage
     static constexpr int STAGE = ROWS * BKB;
@@ -124,19 +124,6 @@ struct Core {
                                              0, 0);
     }
 
-    // One MFMA step into an fp32 accumulator.  fp8: the instruction starts
-    // from zero and its 32-term result is added on the vector ALU, so the
-    // running sum is kept in full fp32 (accumulating inside the fp8 MFMA
-    // measured far outside the fp32 rounding bound on this chip).
-    __device__ __forceinline__ static f32x4 mac(frag a, frag b, f32x4 c) {
-        if constexpr (sizeof(T) == 1) {
-            const f32x4 t = Mfma<T>::mma(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
-            return c + t;
-        } else {
-            return Mfma<T>::mma(a, b, c);
-        }
-    }
-
     __device__ __forceinline__ void compute(const uint8_t* stage) {
         const int lane = threadIdx.x % WAVE;
         const int wm = wave / WN, wn = wave % WN;
@@ -149,21 +136,21 @@ struct Core {
             const int phys = (((off >> 4) ^ sw) << 4) | (off & 15);
             frag af[TM], bf[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *(const frag*)(sa + i * 16 * BKB + phys);
+            for (int i = 0; i < TM; ++i) af[i] = Mfma<T>::load(sa + i * 16 * BKB + phys);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = *(const frag*)(sb + j * 16 * BKB + phys);
+            for (int j = 0; j < TN; ++j) bf[j] = Mfma<T>::load(sb + j * 16 * BKB + phys);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mac(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::mac(af[i], bf[j], acc[i][j]);
             if constexpr (DUAL) {
                 frag bf2[TN];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) bf2[j] = *(const frag*)(sb + (BN + j * 16) * BKB + phys);
+                for (int j = 0; j < TN; ++j) bf2[j] = Mfma<T>::load(sb + (BN + j * 16) * BKB + phys);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) acc2[i][j] = mac(af[i], bf2[j], acc2[i][j]);
+                    for (int j = 0; j < TN; ++j) acc2[i][j] = Mfma<T>::mac(af[i], bf2[j], acc2[i][j]);
             }
         }
     }
