@@ -8,9 +8,15 @@ second over the K timed steps, inputs already resident in HBM.
 
 Default workload: the dense 16-layer d=2048 bf16 model (16 Q / 4 KV heads x
 128, SwiGLU 8192, vocab 32768) with a 1024-token prefix and one 256-token
-canvas, 16 steps x 16 commits, then the append.  Weights and prompt are seeded
-synthetic draws (random init) generated on the host, so the CPU baseline reads
-the same bytes.
+canvas, 16 steps x 16 commits, then the append.  `--workload moe` runs the
+32-layer 26B-class MoE (128 experts top-8 x 768 + shared 2048, vocab 262144)
+with a 4096-token prefix and 4 canvases of 12 steps; `moe-fp8` the same model
+with E4M3 GEMMs and the confidence-threshold rule; `moe-batch32` 32 requests
+with prefixes of 512..4096 tokens denoised together.  Weights and prompts are
+seeded synthetic draws (random init).  Models up to a few billion parameters
+are drawn on the host and copied, so the CPU baseline reads the same bytes;
+the 26B-class ones are drawn on the GPU, and the CPU baseline reads a copy of
+the layers it samples.
 
 Also reported: ms per denoising step (denoise + commit, CUDA events on the
 library's stream), and the roofline of the dominant kernel of the denoising
@@ -48,34 +54,55 @@ def _workload_text(run) -> str:
             f"{rule}, append")
 
 
-def kernel_model(name: str, cfg, C: int, keys: int):
+def experts_touched(E: int, k: int, rows: int) -> float:
+    """Expected number of distinct experts a step's rows route to when each row
+    picks k of E experts: E (1 - (1 - k/E)^rows)."""
+    return E * (1.0 - (1.0 - k / E) ** rows)
+
+
+def kernel_model(name: str, cfg, rows: int, keys_per_req, experts_used=None):
     """Algorithmic (bytes, flops) of one launch of a denoising-step kernel over
-    a C-row canvas attending to `keys` keys.  Bytes: weights and activations
-    read once, outputs written once (x read and written for residual adds);
-    flops: 2 per multiply-add of the contraction."""
+    `rows` canvas rows (R requests x C) whose requests attend to
+    `keys_per_req` keys each.  Bytes: weights and activations read once,
+    outputs written once (x read and written for residual adds); flops: 2 per
+    multiply-add of the contraction.  Grouped expert GEMMs read the weights of
+    the experts the rows route to: `experts_used` (the mean number of distinct
+    experts per launch, counted from the routing), else the count expected
+    from independent uniform choices (`experts_touched`)."""
     d, F, dh = cfg.d_model, cfg.d_ffn, cfg.head_dim
     qd, kvd = cfg.n_q_heads * dh, cfg.n_kv_heads * dh
     nqkv = qd + 2 * kvd
     eb = 1 if cfg.dtype == "fp8" else (4 if cfg.dtype == "f32" else 2)
     ab = 4 if cfg.dtype == "f32" else 2          # stored activation element
+    M = rows
     if name == "gemm_qkv":
-        return nqkv * d * eb + C * d * eb + C * nqkv * 4, 2.0 * C * nqkv * d
+        return nqkv * d * eb + M * d * eb + M * nqkv * 4, 2.0 * M * nqkv * d
     if name == "gemm_o":
-        return d * qd * eb + C * qd * eb + 2 * C * d * 4, 2.0 * C * d * qd
+        return d * qd * eb + M * qd * eb + 2 * M * d * 4, 2.0 * M * d * qd
     if name == "gemm_gate_up":
-        return 2 * F * d * eb + C * d * eb + C * F * ab, 2.0 * C * 2 * F * d
+        return 2 * F * d * eb + M * d * eb + M * F * ab, 2.0 * M * 2 * F * d
     if name == "gemm_down":
-        return d * F * eb + C * F * eb + 2 * C * d * 4, 2.0 * C * d * F
+        return d * F * eb + M * F * eb + 2 * M * d * 4, 2.0 * M * d * F
     if name == "lm_head":
-        return cfg.vocab * d * eb + C * d * eb, 2.0 * C * cfg.vocab * d
+        return cfg.vocab * d * eb + M * d * eb, 2.0 * M * cfg.vocab * d
+    if name == "router":
+        wb = 4 if cfg.dtype == "f32" else 2
+        return cfg.n_experts * d * wb + M * d * wb + M * cfg.n_experts * 4, 2.0 * M * cfg.n_experts * d
+    if name in ("expert_gate_up", "expert_down") and cfg.ffn == "moe":
+        De, A = cfg.d_expert, M * cfg.top_k
+        used = experts_used if experts_used is not None else experts_touched(cfg.n_experts, cfg.top_k, M)
+        if name == "expert_gate_up":
+            return used * 2 * De * d * eb + A * d * eb + A * De * ab, 2.0 * A * 2 * De * d
+        return used * d * De * eb + A * De * eb + A * d * 4, 2.0 * A * d * De
     if name == "attention":
-        return (2 * keys * kvd * ab + 2 * C * qd * ab,
-                4.0 * C * cfg.n_q_heads * keys * dh)
+        keys = sum(keys_per_req)
+        return (2 * keys * kvd * ab + 2 * M * qd * ab,
+                4.0 * (M // len(keys_per_req)) * cfg.n_q_heads * keys * dh)
     return None
 
 
-def roofline(name, cfg, C, keys, avg_ms):
-    m = kernel_model(name, cfg, C, keys)
+def roofline(name, cfg, rows, keys_per_req, avg_ms, experts_used=None):
+    m = kernel_model(name, cfg, rows, keys_per_req, experts_used)
     if m is None or avg_ms <= 0:
         return None
     nbytes, flops = m
@@ -97,10 +124,21 @@ def roofline(name, cfg, C, keys, avg_ms):
     return out
 
 
-def cpu_baseline(run, weights_cpu, prefix_cpu):
-    """The oracle on the host, on a bounded sample of the same workload: prefill
-    of the full prompt, one denoising step with its commit, and one append;
-    the request time is extrapolated to the schedule's step count."""
+def _layer_of(name: str):
+    head = name.split(".", 1)[0]
+    return int(head) if head.isdigit() else None
+
+
+def cpu_baseline(run, weights, prefix_cpu, steps_per_canvas: float, sample_layers=None):
+    """The oracle on the host, on a bounded sample of the same workload and
+    weights: prefill of request 0's prompt, one denoising step with its commit,
+    and one append.  With `sample_layers` the sample model keeps only the
+    first layers (full width: embedding, those layers, LM head); the per-layer
+    time is scaled to the model's depth, the LM head (timed alone) counted
+    once per step.  The request time is extrapolated to the schedule's steps
+    and canvases, and to R requests (the oracle serves them one after another)."""
+    from dataclasses import replace
+
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -108,30 +146,52 @@ def cpu_baseline(run, weights_cpu, prefix_cpu):
     from oracle.model import OracleModel, OracleWeights
 
     cfg = run.model
-    om = OracleModel(cfg, OracleWeights(cfg, weights_cpu))
-    st = om.new_seq(run.capacity())
+    L = cfg.n_layers
+    Ls = L if sample_layers is None else min(sample_layers, L)
+    cfg_s = replace(cfg, n_layers=Ls)
+    host = {k: v.cpu() for k, v in weights.items() if _layer_of(k) is None or _layer_of(k) < Ls}
+    om = OracleModel(cfg_s, OracleWeights(cfg_s, host))
+    del host
+    C = run.canvas
+    st = om.new_seq(len(prefix_cpu) + C)
     t0 = time.perf_counter()
     om.prefill(st, prefix_cpu.numpy())
     t1 = time.perf_counter()
-    canvas = np.full(run.canvas, cfg.mask_id, dtype=np.int32)
+    canvas = np.full(C, cfg.mask_id, dtype=np.int32)
     conf, pred, _ = om.denoise(st, canvas)
     canvas, _ = osampler.commit(canvas, conf, pred, cfg.mask_id, run, 0)
     t2 = time.perf_counter()
     canvas[canvas == cfg.mask_id] = 0
     om.append(st, canvas)
     t3 = time.perf_counter()
-    per_req = (t1 - t0) + run.n_canvases * (run.n_steps * (t2 - t1) + (t3 - t2))
+    lm = 0.0
+    if Ls < L:
+        x = np.zeros((C, cfg.d_model))
+        x[:, 0] = 1.0
+        tl = time.perf_counter()
+        om.logits(x)
+        lm = time.perf_counter() - tl
+    scale = L / Ls
+    prefill_s = (t1 - t0) * scale
+    step_s = (t2 - t1 - lm) * scale + lm
+    append_s = (t3 - t2) * scale
+    per_req = prefill_s + run.n_canvases * (steps_per_canvas * step_s + append_s)
+    R = run.n_requests
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    what = (f"the whole {L}-layer model" if Ls == L else
+            f"{Ls} of {L} layers at full width (embedding, {'layers 0..' + str(Ls - 1) if Ls > 1 else 'layer 0'}, LM head "
+            f"{lm:.2f} s timed alone), layer time scaled x{scale:g}")
     return {
-        "value": run.canvas * run.n_canvases / per_req,
+        "value": R * C * run.n_canvases / (R * per_req),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle on the host ({threads} BLAS threads): prefill of the "
-                   f"{len(prefix_cpu)}-token prompt ({t1 - t0:.2f} s), one denoising step + commit "
-                   f"({t2 - t1:.2f} s) and one append ({t3 - t2:.2f} s) of the same workload and weights; "
-                   f"the request is extrapolated to {run.n_steps} steps per canvas"),
-        "s_per_denoise_step": t2 - t1,
+        "sample": (f"float64 numpy oracle on the host ({threads} BLAS threads), {what}: prefill of the "
+                   f"{len(prefix_cpu)}-token prompt of request 0 ({t1 - t0:.2f} s), one denoising step + commit "
+                   f"({t2 - t1:.2f} s) and one append ({t3 - t2:.2f} s) with the same weights; extrapolated to "
+                   f"{steps_per_canvas:g} steps x {run.n_canvases} canvas(es)"
+                   + (f" x {R} requests, each taken as long as request 0" if R > 1 else "")),
+        "s_per_denoise_step": step_s,
     }
 
 
@@ -140,7 +200,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="dense")
+    ap.add_argument("--workload", default="dense",
+                    help="dense (default), moe, moe-fp8, moe-batch32, tiny, or a reduced run name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -155,53 +216,76 @@ def main():
     from masked_block_diffusion_amd import DLM, Rule
     from masked_block_diffusion_amd import abi
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     run = synth.get_run(args.workload)
-    cfg, C = run.model, run.canvas
+    cfg, C, R = run.model, run.canvas, run.n_requests
+    big = cfg.n_params()["total"] > 4e9
     t = time.perf_counter()
-    w_cpu = synth.make_weights(cfg, seed=run.seed)
-    prefix_cpu = synth.make_inputs(run)[0]
-    print(f"[bench] weights generated in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
-    model = DLM(cfg, {k: v.cuda() for k, v in w_cpu.items()}, canvas=C)
+    weights = synth.make_weights(cfg, seed=run.seed, device="cuda" if big else "cpu")
+    prefixes_cpu = synth.make_inputs(run)
+    log(f"{cfg.name}: weights drawn on the {'GPU' if big else 'host'} in {time.perf_counter() - t:.1f} s")
+    model = DLM(cfg, weights if big else {k: v.cuda() for k, v in weights.items()}, canvas=C)
     cap = run.capacity()
-    seq = model.new_seq(cap)
-    ws = model.workspace(max(C, run.max_prefix), cap)
-    prefix = prefix_cpu.cuda()
+    seqs = [model.new_seq(cap) for _ in range(R)]
+    ws = model.workspace(max(R * C, run.max_prefix), cap)
+    prefixes = [p.cuda() for p in prefixes_cpu]
     rule = Rule.topk(C, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
-    conf = torch.empty(C, dtype=torch.float32, device="cuda")
-    pred = torch.empty(C, dtype=torch.int32, device="cuda")
-    n_masked = torch.empty(1, dtype=torch.int32, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * run.n_canvases)]
+    conf = torch.empty(R * C, dtype=torch.float32, device="cuda")
+    pred = torch.empty(R * C, dtype=torch.int32, device="cuda")
+    n_masked = torch.empty(R, dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * run.n_canvases)]
     all_ids = list(range(abi.DLM_K_COUNT))
 
-    def one_request(timed_ids):
-        seq.raw.T = 0
-        model.dlm_prefill(seq, prefix, ws)
+    moe = cfg.ffn == "moe"
+    L = cfg.n_layers
+    dbg_ids = torch.empty(L * R * C * max(1, cfg.top_k), dtype=torch.int32, device="cuda") if moe else None
+    used_per_launch = []     # distinct experts per (step, layer), MoE only
+
+    def one_request(timed_ids, count_experts=False):
+        for s, ids in zip(seqs, prefixes):
+            s.raw.T = 0
+            model.dlm_prefill(s, ids, ws)
         steps_run = 0
         for ci in range(run.n_canvases):
-            seq.canvas.fill_(cfg.mask_id)
+            for s in seqs:
+                s.canvas.fill_(cfg.mask_id)
             model.timing_enable(timed_ids)
-            ev[2 * ci].record()
-            for s in range(run.n_steps):
-                model.dlm_denoise_step([seq], conf, pred, ws)
-                model.dlm_commit([seq], conf, pred, rule, s, None, n_masked)
+            ev[4 * ci].record()
+            if count_experts:
+                model.dlm_debug_router(dbg_ids, None, L * R * C)
+            for st in range(run.n_steps):
+                model.dlm_denoise_step(seqs, conf, pred, ws)
+                if count_experts:
+                    hit = torch.zeros(L, cfg.n_experts, device="cuda")
+                    hit.scatter_(1, dbg_ids.view(L, -1).long(), 1.0)
+                    used_per_launch.append(hit.sum(1))
+                model.dlm_commit(seqs, conf, pred, rule, st, None, n_masked)
                 steps_run += 1
-                if run.rule == "threshold" and int(n_masked.cpu()[0]) == 0:
+                if run.rule == "threshold" and int(n_masked.max().cpu()) == 0:
                     break
-            ev[2 * ci + 1].record()
+            ev[4 * ci + 1].record()
+            if count_experts:
+                model.dlm_debug_router(None, None, 0)
             model.timing_enable([])
-            model.dlm_append_canvas([seq], ws)
+            ev[4 * ci + 2].record()
+            model.dlm_append_canvas(seqs, ws)
+            ev[4 * ci + 3].record()
         return steps_run
 
-    print(f"[bench] warmup {args.warmup} (+1 with every kernel timed)", file=sys.stderr, flush=True)
+    log(f"warmup {args.warmup} (+1 with every kernel timed)")
     for _ in range(args.warmup):
         one_request([])
     torch.cuda.synchronize()
     model.timing_read()
-    one_request(all_ids)
+    steps_full = one_request(all_ids, count_experts=moe)
     torch.cuda.synchronize()
     per_kernel = model.timing_read()
+    experts_used = float(torch.cat(used_per_launch).mean()) if used_per_launch else None
     dominant = max(per_kernel, key=lambda k: per_kernel[k][0])
     dom_id = [i for i in all_ids if model.lib.dlm_kernel_name(i).decode() == dominant][0]
+    log(f"dominant denoise kernel: {dominant}; timing {args.steps} requests")
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -211,16 +295,18 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kt = model.timing_read()
-    denoise_ms = sum(ev[2 * ci].elapsed_time(ev[2 * ci + 1]) for ci in range(run.n_canvases))
+    denoise_ms = sum(ev[4 * ci].elapsed_time(ev[4 * ci + 1]) for ci in range(run.n_canvases))
+    append_ms = sum(ev[4 * ci + 2].elapsed_time(ev[4 * ci + 3]) for ci in range(run.n_canvases))
     status = model.dlm_check_device_status()
     if status:
-        print(f"[bench] device error word {status}", file=sys.stderr)
+        log(f"device error word {status}")
         sys.exit(1)
     elapsed = t1 - t0
-    tokens = args.steps * C * run.n_canvases
+    tokens = args.steps * R * C * run.n_canvases
     steps_last = n_denoise // args.steps
     ms_k, n_k = kt.get(dominant, (0.0, 0))
-    keys = run.max_prefix + C
+    rows = R * C
+    keys = [len(p) + C * (run.n_canvases + 1) / 2 for p in prefixes_cpu]   # mean over the canvases
     step_ms = denoise_ms / max(1, steps_last)
     out = {
         "metric": METRIC,
@@ -237,28 +323,41 @@ def main():
         "data": "synthetic (seeded random-init weights and uniform random prompt ids)",
         "config": {
             "workload": _workload_text(run),
-            "global_batch": run.n_requests,
+            "global_batch": R,
             "seq_len": run.max_prefix + run.n_canvases * C,
             "canvas": C,
-            "prefix": run.max_prefix,
+            "prefix": run.max_prefix if R == 1 else [len(p) for p in prefixes_cpu],
             "denoise_steps_per_canvas": steps_last / run.n_canvases,
             "parallelism": "single GPU",
         },
         "ms_per_denoise_step": step_ms,
-        "decode_tokens_per_s": C * run.n_canvases / (denoise_ms * 1e-3) if denoise_ms else None,
-        "roofline": roofline(dominant, cfg, C, keys, ms_k / max(1, n_k)),
-        "denoise_step_kernels_ms": {k: round(v[0] / max(1, steps_last), 4) for k, v in
+        "decode_tokens_per_s": (R * C * run.n_canvases / ((denoise_ms + append_ms) * 1e-3)
+                                if denoise_ms else None),
+        "roofline": roofline(dominant, cfg, rows, keys, ms_k / max(1, n_k), experts_used),
+        "denoise_step_kernels_ms": {k: round(v[0] / max(1, steps_full), 4) for k, v in
                                     sorted(per_kernel.items(), key=lambda kv: -kv[1][0])},
     }
+    if experts_used is not None:
+        out["experts_used_per_layer_step"] = {
+            "mean": experts_used, "of": cfg.n_experts,
+            "first_step": float(used_per_launch[0].mean()), "last_step": float(used_per_launch[-1].mean()),
+            "uniform_expectation": experts_touched(cfg.n_experts, cfg.top_k, rows)}
     for name, (ms, n) in per_kernel.items():
-        r = roofline(name, cfg, C, keys, ms / max(1, n))
+        r = roofline(name, cfg, rows, keys, ms / max(1, n), experts_used)
         if r:
             out.setdefault("kernel_rooflines", {})[name] = {k: r[k] for k in ("bound", "frac", "hbm_gbs",
                                                                               "mfma_util_pct", "avg_launch_ms")}
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        del model
-        out["cpu_baseline"] = cpu_baseline(run, w_cpu, prefix_cpu)
+        log("cpu baseline (oracle sample)")
+        if big:
+            host = {k: v for k, v in weights.items() if _layer_of(k) is None or _layer_of(k) < 1}
+            del model, weights
+            torch.cuda.empty_cache()
+            out["cpu_baseline"] = cpu_baseline(run, host, prefixes_cpu[0], steps_last / run.n_canvases,
+                                               sample_layers=1)
+        else:
+            del model
+            out["cpu_baseline"] = cpu_baseline(run, weights, prefixes_cpu[0], steps_last / run.n_canvases)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))

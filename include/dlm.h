@@ -145,10 +145,15 @@ typedef struct {
 } dlm_weights;
 
 /* One request.  Host struct of non-owning device pointers.
- *   kv: KV cache, [n_layers][2 (K, V)][n_kv_heads][capacity][head_dim],
- *       bf16 (fp32 for DLM_F32 models); slot t holds the post-RoPE key and the
- *       value of absolute position t.
- *   capacity: tokens the cache holds.
+ *   kv: KV cache, bf16 (fp32 for DLM_F32 models), per layer and KV head a
+ *       key block then a value block: [n_layers][2][n_kv_heads][capacity *
+ *       head_dim] with the key block [capacity][head_dim] (row t: the
+ *       post-RoPE key of absolute position t) and the value block stored
+ *       transposed, [head_dim][capacity] (column t: the value of position t),
+ *       so attention reads consecutive positions of one value dimension.
+ *       Slots not yet written may hold anything; they are never used.
+ *   capacity: tokens the cache holds; a multiple of 8 (E_SHAPE otherwise), so
+ *       every transposed value row is 16-byte aligned.
  *   T: tokens cached so far (prefix plus appended canvases).
  *   canvas: device int32[C], the block being denoised ([MASK] = mask_id).
  *   page_table / page_size: reserved for a paged cache; must be NULL / 0. */

@@ -145,6 +145,28 @@ template <> struct Mfma<fp8_t> {
     }
 };
 
+// ------------------------------------------------- LDS-DMA pipelines --
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// s_waitcnt on vector-memory operations only: vmcnt <= N (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() would add a release
+// fence that drains every outstanding LDS-DMA load (all stages in flight);
+// here each wave has already waited for the stage it needs, so
+// the barrier only has to order LDS reads: lgkmcnt(0), s_barrier, and a
+// compiler memory clobber so no LDS access moves across it.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Error word bits (mirrors dlm.h).
 constexpr int DEVERR_TOKEN_RANGE = 1;
 constexpr int DEVERR_MASK_APPEND = 2;

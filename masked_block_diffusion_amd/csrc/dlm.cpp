@@ -255,6 +255,7 @@ dlm_status check_seq(const dlm_model* m, const dlm_seq* s, int extra, bool need_
     if (s->page_table || s->page_size) return fail(DLM_E_UNSUPPORTED, "seq %d: paged KV cache is not supported", idx);
     if (need_canvas && !s->canvas) return fail(DLM_E_ARG, "seq %d: canvas is NULL", idx);
     if (s->T < 0 || s->capacity < 0) return fail(DLM_E_ARG, "seq %d: negative T or capacity", idx);
+    if (s->capacity % 8 != 0) return fail(DLM_E_SHAPE, "seq %d: capacity %d is not a multiple of 8", idx, s->capacity);
     if ((long)s->T + extra > (long)s->capacity)
         return fail(DLM_E_CAPACITY, "seq %d: T %d + %d exceeds capacity %d", idx, s->T, extra, s->capacity);
     (void)m;

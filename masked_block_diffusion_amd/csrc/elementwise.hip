@@ -9,6 +9,8 @@
 // sums them in split order (applying the fp8 scales): RMSNorm adds the O- and
 // down-projection partials into the residual stream, RoPE sums the QKV
 // partials.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -80,32 +82,46 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
     const int r = blockIdx.x;          // one single-wave workgroup per row: every row on its own CU slot
     if (r >= rows) return;
     const int nc = d / 4;
+    const bool out = hf || hb;
     float* xr = x + (long)r * d;
-    f32x4 v[MAXC];
+    f32x4 v[MAXC], gg[MAXC];
     float ss = 0.f;
+    // every load of the row (x, pending partials, gains) is issued before the first use
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
         const int c = lane + WAVE * k;
         if (c < nc) {
             v[k] = *(const f32x4*)(xr + 4 * c);
-            if (res.p) {
-                v[k] += partial_sum4(res, r, 4 * c, d);
-                *(f32x4*)(xr + 4 * c) = v[k];
-            }
-            ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+            if (out) gg[k] = *(const f32x4*)(g + 4 * c);
         }
     }
-    if (!hf && !hb) return;                        // residual update only
+    if (res.p) {
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) {
+            const int c = lane + WAVE * k;
+            if (c < nc) v[k] += partial_sum4(res, r, 4 * c, d);
+        }
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) {
+            const int c = lane + WAVE * k;
+            if (c < nc) *(f32x4*)(xr + 4 * c) = v[k];
+        }
+    }
+    if (!out) return;                              // residual update only
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+        const int c = lane + WAVE * k;
+        if (c < nc) ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+    }
     const float den = sqrtf(wave_sum(ss) / (float)d + eps);
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
         const int c = lane + WAVE * k;
         if (c < nc) {
-            const f32x4 gg = *(const f32x4*)(g + 4 * c);
             f32x4 h;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = v[k][e] / den * gg[e];
+            for (int e = 0; e < 4; ++e) h[e] = v[k][e] / den * gg[k][e];
             if (hf) *(f32x4*)(hf + (long)r * d + 4 * c) = h;
             if (hb) {
                 uint64_t packed = 0;
@@ -122,18 +138,18 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
     }
     if (!hq) return;
     amax = wave_max(amax);
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
         const int c = lane + WAVE * k;
         if (c < nc) {
             uint32_t packed = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) packed |= (uint32_t)f32_to_e4m3(v[k][e] / s) << (8 * e);
+            for (int e = 0; e < 4; ++e) packed |= (uint32_t)f32_to_e4m3(v[k][e] / sc) << (8 * e);
             *(uint32_t*)(hq + (long)r * d + 4 * c) = packed;
         }
     }
-    if (lane == 0) hs[r] = s;
+    if (lane == 0) hs[r] = sc;
 }
 
 void rmsnorm(float* x, const Partials& res, const float* g, int rows, int d, float eps, float* hf, uint16_t* hb,
@@ -178,10 +194,55 @@ void quant_rows(const uint16_t* x, int rows, int d, uint8_t* q, float* s, hipStr
 // Rotate-half rotary embedding: for i < dh/2 the pair (v[i], v[i + dh/2]) is
 // rotated by pos * base^(-2i/dh).  The angle and its sine/cosine are formed in
 // double precision (positions reach several thousand), then applied in fp32.
+//
+// Cache layout per (layer, KV head): K is [capacity][dh] (a key per row), V is
+// stored transposed, [dh][capacity], so the attention kernel's P V operand
+// reads consecutive keys.  Blocks [0, rows) rotate Q and K of one token row;
+// the blocks after them each transpose V of up to 64 rows of one KV head
+// through LDS, so every wave writes 64 consecutive positions of one dh row.
+constexpr int VT_ROWS = 64;                // rows per V^T block
+constexpr int VT_COLS = 32;                // value dimensions per V^T block
 
 template <bool F32>
-__global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, int layer, int hq, int hkv, int dh,
-                                                      float base, void* q_out) {
+__global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, int rows, int layer, int hq,
+                                                      int hkv, int dh, float base, void* q_out) {
+    typedef typename std::conditional<F32, float, bf16_t>::type T;
+    constexpr int PITCH = VT_COLS + (F32 ? 1 : 2);   // conflict-free column reads
+    constexpr int PER_T = VT_ROWS * VT_COLS / NT;    // elements per thread
+    __shared__ T tile[VT_ROWS * PITCH];
+    const int ncols = (hq + 2 * hkv) * dh;
+    if ((int)blockIdx.x >= rows) {
+        const int nslice = dh / VT_COLS;
+        int vb = blockIdx.x - rows;
+        const int sl = vb % nslice; vb /= nslice;
+        const int kh = vb % hkv, r0 = (vb / hkv) * VT_ROWS;
+        const int nr = min(VT_ROWS, rows - r0);
+        const int col0 = (hq + hkv + kh) * dh + sl * VT_COLS;
+        float val[PER_T];
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int e = threadIdx.x + NT * i, rr = e / VT_COLS, d = e % VT_COLS;
+            val[i] = rr < nr ? partial_sum(qkv, r0 + rr, col0 + d, ncols) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int e = threadIdx.x + NT * i, rr = e / VT_COLS, d = e % VT_COLS;
+            if constexpr (F32) tile[rr * PITCH + d] = val[i];
+            else tile[rr * PITCH + d] = f32_to_bf16(val[i]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int e = threadIdx.x + NT * i, d = e / VT_ROWS, rr = e % VT_ROWS;
+            if (rr >= nr) continue;
+            const int r = r0 + rr, s = r / seqs.per_seq;
+            const int pos = seqs.T[s] + r % seqs.per_seq;
+            const long cap = seqs.cap[s];
+            T* vt = (T*)seqs.kv[s] + (((long)layer * 2 + 1) * hkv + kh) * cap * dh;
+            vt[(long)(sl * VT_COLS + d) * cap + pos] = tile[rr * PITCH + d];
+        }
+        return;
+    }
     const int r = blockIdx.x;
     const int s = r / seqs.per_seq, i = r % seqs.per_seq;
     const int pos = seqs.T[s] + i;
@@ -193,37 +254,24 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, 
     double sd, cd;
     sincos((double)pos * theta, &sd, &cd);
     const float sn = (float)sd, cs = (float)cd;
-    const int nh = hq + 2 * hkv;
-    const int ncols = nh * dh;
     const long cap = seqs.cap[s];
-    for (int h = hg; h < nh; h += ngroups) {
+    for (int h = hg; h < hq + hkv; h += ngroups) {
         const float a = partial_sum(qkv, r, h * dh + j, ncols);
         const float b = partial_sum(qkv, r, h * dh + j + half, ncols);
-        float ra = a, rb = b;
-        if (h < hq + hkv) {
-            ra = a * cs - b * sn;
-            rb = a * sn + b * cs;
-        }
+        const float ra = a * cs - b * sn;
+        const float rb = a * sn + b * cs;
+        T* dst;
         if (h < hq) {
-            const long o = ((long)r * hq + h) * dh;
-            if (F32) {
-                ((float*)q_out)[o + j] = ra;
-                ((float*)q_out)[o + j + half] = rb;
-            } else {
-                ((bf16_t*)q_out)[o + j] = f32_to_bf16(ra);
-                ((bf16_t*)q_out)[o + j + half] = f32_to_bf16(rb);
-            }
+            dst = (T*)q_out + ((long)r * hq + h) * dh;
         } else {
-            const int kind = h < hq + hkv ? 0 : 1;            // 0 = K, 1 = V
-            const int kh = h - hq - kind * hkv;
-            const long o = (((long)layer * 2 + kind) * hkv + kh) * cap * dh + (long)pos * dh;
-            if (F32) {
-                ((float*)seqs.kv[s])[o + j] = ra;
-                ((float*)seqs.kv[s])[o + j + half] = rb;
-            } else {
-                ((bf16_t*)seqs.kv[s])[o + j] = f32_to_bf16(ra);
-                ((bf16_t*)seqs.kv[s])[o + j + half] = f32_to_bf16(rb);
-            }
+            dst = (T*)seqs.kv[s] + (((long)layer * 2 + 0) * hkv + (h - hq)) * cap * dh + (long)pos * dh;
+        }
+        if constexpr (F32) {
+            dst[j] = ra;
+            dst[j + half] = rb;
+        } else {
+            dst[j] = f32_to_bf16(ra);
+            dst[j + half] = f32_to_bf16(rb);
         }
     }
 }
@@ -232,10 +280,11 @@ void rope_kv(const Partials& qkv, int rows, const SeqTab& seqs, int layer, int n
              float base, bool f32, void* q_out, hipStream_t st) {
     (void)n_layers;
     if (rows <= 0) return;
+    const dim3 grid(rows + (rows + VT_ROWS - 1) / VT_ROWS * hkv * (dh / VT_COLS));
     if (f32)
-        launch(rope_kv_kernel<true>, dim3(rows), dim3(NT), 0, st, qkv, seqs, layer, hq, hkv, dh, base, q_out);
+        launch(rope_kv_kernel<true>, grid, dim3(NT), 0, st, qkv, seqs, rows, layer, hq, hkv, dh, base, q_out);
     else
-        launch(rope_kv_kernel<false>, dim3(rows), dim3(NT), 0, st, qkv, seqs, layer, hq, hkv, dh, base, q_out);
+        launch(rope_kv_kernel<false>, grid, dim3(NT), 0, st, qkv, seqs, rows, layer, hq, hkv, dh, base, q_out);
 }
 
 }  // namespace dlm

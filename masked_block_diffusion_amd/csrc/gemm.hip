@@ -36,26 +36,6 @@ enum Epi { EPI_F32 = 0, EPI_BF16, EPI_ADD_F32, EPI_SWIGLU_BF16, EPI_SWIGLU_F32, 
 
 constexpr int BKB = 128;             // K bytes per stage row
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// s_waitcnt on vector-memory operations only: vmcnt <= N (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-
-// Workgroup barrier for the LDS ring.  __syncthreads() would add a release
-// fence that drains every outstanding LDS-DMA load (all stages in flight);
-// here each wave has already waited for the stage it needs (wait_stages), so
-// the barrier only has to order LDS reads: lgkmcnt(0), s_barrier, and a
-// compiler memory clobber so no LDS access moves across it.
-__device__ __forceinline__ void stage_barrier() {
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-    asm volatile("s_barrier" ::: "memory");
-}
-
 // Wait until at most p stages (of LPW loads each) are still outstanding.
 template <int LPW, int P>
 __device__ __forceinline__ void wait_stages(int p) {

@@ -160,18 +160,30 @@ void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, 
 
 // ---------------------------------------------------------------- combine --
 
+// One workgroup per token row; each thread owns 4 consecutive columns (d is a
+// multiple of 4): x += shared-expert output (split partials summed in order,
+// fp8 scales applied) + sum over the row's k slots of w * y[slot's sorted row].
 __global__ __launch_bounds__(256) void moe_combine_kernel(float* x, Partials shared, const float* y,
                                                            const int* inv, const float* w, int k, int d) {
     const long r = blockIdx.x;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        float acc = 0.f;
+    const float* wr = w + r * k;
+    const int* ir = inv + r * k;
+    for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         if (shared.p) {
             const long off = r * d + c;
-            for (int s = 0; s < shared.splits; ++s) acc += shared.p[s * shared.stride + off];
-            if (shared.a_scale) acc *= shared.a_scale[r] * shared.b_scale[c];
+            for (int s = 0; s < shared.splits; ++s) acc += *(const f32x4*)(shared.p + s * shared.stride + off);
+            if (shared.a_scale) acc = acc * shared.a_scale[r] * *(const f32x4*)(shared.b_scale + c);
         }
-        for (int s = 0; s < k; ++s) acc += w[r * k + s] * y[(long)inv[r * k + s] * d + c];
-        x[r * d + c] += acc;
+        f32x4 yv[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            if (s < k) yv[s] = *(const f32x4*)(y + (long)ir[s] * d + c);
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            if (s < k) acc += wr[s] * yv[s];
+        f32x4* xp = (f32x4*)(x + r * d + c);
+        *xp = *xp + acc;
     }
 }
 

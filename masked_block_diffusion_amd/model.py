@@ -37,15 +37,34 @@ def _stream() -> int:
 
 @dataclass
 class Seq:
-    """One request: its KV cache [L, 2, Hkv, capacity, dh], its canvas int32[C]
-    and the ABI struct pointing at both (T lives in the struct)."""
+    """One request: its KV cache [L, 2, Hkv, capacity * dh] (per layer and KV
+    head a key block [capacity, dh] and a value block stored transposed,
+    [dh, capacity]), its canvas int32[C] and the ABI struct pointing at both
+    (T lives in the struct)."""
     kv: torch.Tensor
     canvas: torch.Tensor
     raw: abi.dlm_seq
+    head_dim: int
 
     @property
     def T(self) -> int:
         return self.raw.T
+
+    @property
+    def capacity(self) -> int:
+        return self.raw.capacity
+
+    @property
+    def k(self) -> torch.Tensor:
+        """Keys, a view [L, Hkv, capacity, dh]."""
+        L, _, H, _ = self.kv.shape
+        return self.kv[:, 0].view(L, H, self.capacity, self.head_dim)
+
+    @property
+    def v(self) -> torch.Tensor:
+        """Values, a (strided) view [L, Hkv, capacity, dh] of the transposed block."""
+        L, _, H, _ = self.kv.shape
+        return self.kv[:, 1].view(L, H, self.head_dim, self.capacity).transpose(-1, -2)
 
 
 class DLM:
@@ -119,13 +138,16 @@ class DLM:
 
     # -------------------------------------------------------------- state --
     def new_seq(self, capacity: int) -> Seq:
+        """A request whose cache holds at least `capacity` tokens (rounded up to
+        a multiple of 64, the attention kernel's key tile)."""
         c = self.cfg
-        kv = torch.empty((c.n_layers, 2, c.n_kv_heads, capacity, c.head_dim), dtype=self.kv_dtype,
+        capacity = -(-capacity // 64) * 64
+        kv = torch.empty((c.n_layers, 2, c.n_kv_heads, capacity * c.head_dim), dtype=self.kv_dtype,
                          device=self.device)
         canvas = torch.full((self.C,), c.mask_id, dtype=torch.int32, device=self.device)
         raw = abi.dlm_seq(kv=kv.data_ptr(), capacity=capacity, T=0, canvas=canvas.data_ptr(),
                           page_table=None, page_size=0)
-        return Seq(kv, canvas, raw)
+        return Seq(kv, canvas, raw, c.head_dim)
 
     def workspace_bytes(self, max_rows: int, max_kv: int) -> int:
         return int(self.lib.dlm_workspace_bytes(self.handle, max_rows, max_kv))

@@ -26,17 +26,18 @@ RUNS = ["tiny", "dense-mini", "dense-mini-ragged", "moe-mini", "dense-mini-fp8",
         "moe-mini-batch"]
 
 
-def _kv_close(gkv, ost, T, dtype, what, lo=0):
-    """GPU cache [L, 2, Hkv, cap, dh] against the oracle's per-layer K/V over
-    slots [lo, T): relative RMS error per layer and kind (an intermediate tensor:
-    one near-tie router or fp8-code flip moves a few elements by a quantisation
-    step, which a max-abs bound would charge to the whole cache)."""
-    g = gkv.float().cpu().numpy()
+def _kv_close(gseq, ost, T, dtype, what, lo=0):
+    """GPU cache (keys and values as [L, Hkv, cap, dh] views) against the
+    oracle's per-layer K/V over slots [lo, T): relative RMS error per layer and
+    kind (an intermediate tensor: one near-tie router or fp8-code flip moves a
+    few elements by a quantisation step, which a max-abs bound would charge to
+    the whole cache)."""
+    g = [gseq.k.float().cpu().numpy(), gseq.v.float().cpu().numpy()]
     worst = 0.0
-    for l in range(g.shape[0]):
+    for l in range(g[0].shape[0]):
         for kind, ref in ((0, ost.k[l]), (1, ost.v[l])):
             o = ref[:, lo:T]
-            d = np.sqrt(np.mean((g[l, kind, :, lo:T] - o) ** 2))
+            d = np.sqrt(np.mean((g[kind][l, :, lo:T] - o) ** 2))
             s = np.sqrt(np.mean(o ** 2))
             worst = max(worst, d / s)
     assert worst <= LOGIT_TOL[dtype], f"{what}: KV relative RMS error {worst:.3g}"
@@ -49,8 +50,8 @@ def _load_cache(gseq, ost):
     T = ost.T
     k = np.stack([ost.k[l][:, :T] for l in range(len(ost.k))])
     v = np.stack([ost.v[l][:, :T] for l in range(len(ost.v))])
-    gseq.kv[:, 0, :, :T].copy_(torch.from_numpy(k).to(gseq.kv.dtype))
-    gseq.kv[:, 1, :, :T].copy_(torch.from_numpy(v).to(gseq.kv.dtype))
+    gseq.k[:, :, :T].copy_(torch.from_numpy(k).to(gseq.kv.dtype))
+    gseq.v[:, :, :T].copy_(torch.from_numpy(v).to(gseq.kv.dtype))
 
 
 @pytest.mark.parametrize("name", RUNS)
@@ -75,7 +76,7 @@ def test_lockstep_parity(name):
     torch.cuda.synchronize()
     for r in range(n):
         assert gseqs[r].T == ost[r].T
-        _kv_close(gseqs[r].kv, ost[r], ost[r].T, cfg.dtype, f"prefill request {r}")
+        _kv_close(gseqs[r], ost[r], ost[r].T, cfg.dtype, f"prefill request {r}")
 
     rule = Rule.topk(C, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
     sched = osampler.topk_schedule(C, run.n_steps)
@@ -142,7 +143,7 @@ def test_lockstep_parity(name):
         torch.cuda.synchronize()
         for r in range(n):
             assert gseqs[r].T == ost[r].T
-            _kv_close(gseqs[r].kv, ost[r], ost[r].T, cfg.dtype, f"append canvas {ci} request {r}",
+            _kv_close(gseqs[r], ost[r], ost[r].T, cfg.dtype, f"append canvas {ci} request {r}",
                       lo=ost[r].T - C)
     assert gm.dlm_check_device_status() == 0
     print(f"[parity] run={name} max rel logit err {totals.logit_err:.3g}; exempt tokens "
