@@ -203,7 +203,16 @@ def main():
     ap.add_argument("--workload", default="dense",
                     help="dense (default), moe, moe-fp8, moe-batch32, tiny, or a reduced run name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for runs under a profiler: no per-kernel event timing (no roofline), "
+                         "no expert counting, no CPU baseline")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="with --profile: one canvas of this many denoising steps per request")
     args = ap.parse_args()
+    if args.profile:
+        args.no_cpu_baseline = True
+    elif args.profile_steps:
+        ap.error("--profile-steps needs --profile")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
@@ -220,6 +229,9 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     run = synth.get_run(args.workload)
+    if args.profile_steps:
+        from dataclasses import replace
+        run = replace(run, n_canvases=1, n_steps=args.profile_steps)
     cfg, C, R = run.model, run.canvas, run.n_requests
     big = cfg.n_params()["total"] > 4e9
     t = time.perf_counter()
@@ -279,19 +291,22 @@ def main():
         one_request([])
     torch.cuda.synchronize()
     model.timing_read()
-    steps_full = one_request(all_ids, count_experts=moe)
-    torch.cuda.synchronize()
-    per_kernel = model.timing_read()
-    experts_used = float(torch.cat(used_per_launch).mean()) if used_per_launch else None
-    dominant = max(per_kernel, key=lambda k: per_kernel[k][0])
-    dom_id = [i for i in all_ids if model.lib.dlm_kernel_name(i).decode() == dominant][0]
+    if args.profile:
+        steps_full, per_kernel, experts_used, dominant, dom_ids = 1, {}, None, None, []
+    else:
+        steps_full = one_request(all_ids, count_experts=moe)
+        torch.cuda.synchronize()
+        per_kernel = model.timing_read()
+        experts_used = float(torch.cat(used_per_launch).mean()) if used_per_launch else None
+        dominant = max(per_kernel, key=lambda k: per_kernel[k][0])
+        dom_ids = [i for i in all_ids if model.lib.dlm_kernel_name(i).decode() == dominant]
     log(f"dominant denoise kernel: {dominant}; timing {args.steps} requests")
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     n_denoise = 0
     for _ in range(args.steps):
-        n_denoise += one_request([dom_id])
+        n_denoise += one_request(dom_ids)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kt = model.timing_read()
@@ -333,7 +348,7 @@ def main():
         "ms_per_denoise_step": step_ms,
         "decode_tokens_per_s": (R * C * run.n_canvases / ((denoise_ms + append_ms) * 1e-3)
                                 if denoise_ms else None),
-        "roofline": roofline(dominant, cfg, rows, keys, ms_k / max(1, n_k), experts_used),
+        "roofline": roofline(dominant, cfg, rows, keys, ms_k / max(1, n_k), experts_used) if dominant else None,
         "denoise_step_kernels_ms": {k: round(v[0] / max(1, steps_full), 4) for k, v in
                                     sorted(per_kernel.items(), key=lambda kv: -kv[1][0])},
     }

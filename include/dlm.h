@@ -88,7 +88,8 @@ typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_FP8 = 2 } dlm_dtype;
 typedef enum { DLM_FFN_DENSE = 0, DLM_FFN_MOE = 1 } dlm_ffn_kind;
 
 /* Model shape.  Constraints checked by dlm_create: head_dim in {32, 64, 128};
- * n_q_heads a multiple of n_kv_heads; d_model, d_ffn, d_expert multiples of 32
+ * n_q_heads a multiple of n_kv_heads; (n_q_heads + n_kv_heads) * head_dim
+ * <= 8192; d_model, d_ffn, d_expert multiples of 32
  * (f32) / 64 (bf16) / 128 (fp8) elements; top_k <= n_experts <= 256,
  * top_k <= 16; 0 <= mask_id < vocab; canvas in [1, 1024]; d_model <= 4096. */
 typedef struct {

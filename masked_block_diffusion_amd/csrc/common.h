@@ -71,7 +71,9 @@ __device__ __forceinline__ fp8_t f32_to_e4m3(float f) {
     return (fp8_t)(sign | code);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware exp2 and reciprocal (each within ~1 ulp);
+// z -> -inf gives -0, z -> +inf gives z.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------ reductions --
 
@@ -99,7 +101,9 @@ template <> struct Mfma<float> {
     static constexpr int KSTEP = 4;            // elements per step
     static constexpr int LANE_BYTES = 4;
     typedef float frag;
-    __device__ __forceinline__ static frag load(const uint8_t* p) { return *(const frag*)p; }
+    typedef float raw;                         // what a lane reads from LDS
+    __device__ __forceinline__ static raw load(const uint8_t* p) { return *(const raw*)p; }
+    __device__ __forceinline__ static frag widen(raw r) { return r; }
     __device__ __forceinline__ static f32x4 mac(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
@@ -108,7 +112,9 @@ template <> struct Mfma<bf16_t> {
     static constexpr int KSTEP = 32;
     static constexpr int LANE_BYTES = 16;
     typedef bf16x8 frag;
-    __device__ __forceinline__ static frag load(const uint8_t* p) { return *(const frag*)p; }
+    typedef bf16x8 raw;
+    __device__ __forceinline__ static raw load(const uint8_t* p) { return *(const raw*)p; }
+    __device__ __forceinline__ static frag widen(raw r) { return r; }
     __device__ __forceinline__ static f32x4 mac(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -135,8 +141,9 @@ template <> struct Mfma<fp8_t> {
     static constexpr int KSTEP = 64;
     static constexpr int LANE_BYTES = 16;
     struct frag { bf16x8 lo, hi; };
-    __device__ __forceinline__ static frag load(const uint8_t* p) {
-        const u32x4 w = *(const u32x4*)p;
+    typedef u32x4 raw;                         // 16 codes
+    __device__ __forceinline__ static raw load(const uint8_t* p) { return *(const raw*)p; }
+    __device__ __forceinline__ static frag widen(raw w) {
         return frag{widen_e4m3x8(w.x, w.y), widen_e4m3x8(w.z, w.w)};
     }
     __device__ __forceinline__ static f32x4 mac(const frag& a, const frag& b, f32x4 c) {

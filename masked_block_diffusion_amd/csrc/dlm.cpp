@@ -207,6 +207,9 @@ dlm_status check_config(const dlm_config* c) {
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
         return fail(DLM_E_SHAPE, "head_dim %d not in {32, 64, 128}", c->head_dim);
     if (c->n_q_heads % c->n_kv_heads) return fail(DLM_E_SHAPE, "n_q_heads %% n_kv_heads != 0");
+    if (c->head_dim >= 32 && (c->n_q_heads + c->n_kv_heads) * c->head_dim > 8192)
+        return fail(DLM_E_SHAPE, "(n_q_heads + n_kv_heads) * head_dim %d exceeds 8192",
+                    (c->n_q_heads + c->n_kv_heads) * c->head_dim);
     if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DLM_E_ARG, "mask_id outside [0, vocab)");
     if (c->dtype < DLM_F32 || c->dtype > DLM_FP8) return fail(DLM_E_DTYPE, "unknown dtype %d", c->dtype);
     if (c->ffn != DLM_FFN_DENSE && c->ffn != DLM_FFN_MOE) return fail(DLM_E_ARG, "unknown ffn kind %d", c->ffn);

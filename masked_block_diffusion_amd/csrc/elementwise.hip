@@ -18,16 +18,8 @@ namespace dlm {
 
 constexpr int NT = 256;
 
-// Value of output element (row, col) of a GEMM, from its direct fp32 output
-// (splits == 1, already scaled) or from its split-K partials.
-__device__ __forceinline__ float partial_sum(const Partials& p, int row, int col, int ncols) {
-    const long off = (long)row * ncols + col;
-    float v = 0.f;
-    for (int s = 0; s < p.splits; ++s) v += p.p[s * p.stride + off];
-    if (p.a_scale) v *= p.a_scale[row] * p.b_scale[col];
-    return v;
-}
-
+// Partials of GEMM output rows: the direct fp32 output (splits == 1, already
+// scaled) or split-K partials [splits][rows][cols], summed in split order.
 __device__ __forceinline__ f32x4 partial_sum4(const Partials& p, int row, int col, int ncols) {
     const long off = (long)row * ncols + col;
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -96,10 +88,37 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
         }
     }
     if (res.p) {
+        // split by split (fixed order); each split's loads of the whole row
+        // are issued together, so a row costs one round trip per split
+        f32x4 acc[MAXC];
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < res.splits; ++sp) {
+            const float* pr = res.p + sp * res.stride + (long)r * d;
+            f32x4 t[MAXC];
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k) {
+                const int c = lane + WAVE * k;
+                if (c < nc) t[k] = *(const f32x4*)(pr + 4 * c);
+            }
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k) {
+                const int c = lane + WAVE * k;
+                if (c < nc) acc[k] += t[k];
+            }
+        }
+        if (res.a_scale) {
+            const float sa = res.a_scale[r];
+#pragma unroll
+            for (int k = 0; k < MAXC; ++k) {
+                const int c = lane + WAVE * k;
+                if (c < nc) acc[k] = acc[k] * sa * *(const f32x4*)(res.b_scale + 4 * c);
+            }
+        }
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
             const int c = lane + WAVE * k;
-            if (c < nc) v[k] += partial_sum4(res, r, 4 * c, d);
+            if (c < nc) v[k] += acc[k];
         }
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
@@ -220,9 +239,24 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, 
         const int col0 = (hq + hkv + kh) * dh + sl * VT_COLS;
         float val[PER_T];
 #pragma unroll
-        for (int i = 0; i < PER_T; ++i) {
-            const int e = threadIdx.x + NT * i, rr = e / VT_COLS, d = e % VT_COLS;
-            val[i] = rr < nr ? partial_sum(qkv, r0 + rr, col0 + d, ncols) : 0.f;
+        for (int i = 0; i < PER_T; ++i) val[i] = 0.f;
+        for (int sp = 0; sp < qkv.splits; ++sp) {
+            const float* pr = qkv.p + sp * qkv.stride + (long)r0 * ncols + col0;
+            float t[PER_T];
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int e = threadIdx.x + NT * i, rr = e / VT_COLS, d = e % VT_COLS;
+                if (rr < nr) t[i] = pr[(long)rr * ncols + d];
+            }
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) val[i] += t[i];
+        }
+        if (qkv.a_scale) {
+#pragma unroll
+            for (int i = 0; i < PER_T; ++i) {
+                const int e = threadIdx.x + NT * i, rr = e / VT_COLS, d = e % VT_COLS;
+                if (rr < nr) val[i] *= qkv.a_scale[r0 + rr] * qkv.b_scale[col0 + d];
+            }
         }
 #pragma unroll
         for (int i = 0; i < PER_T; ++i) {
@@ -250,14 +284,50 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, 
     const int j = threadIdx.x % half;        // pair index
     const int hg = threadIdx.x / half;       // head lane group
     const int ngroups = NT / half;
+    const int nh = hq + hkv;                 // rotated heads: Q, then K
+    // every head's pair is loaded before the first is used (one round trip)
+    constexpr int MAXIT = 16;                // ceil(nh / ngroups) <= 16 for the supported shapes
+    float av[MAXIT], bv[MAXIT];
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) av[it] = bv[it] = 0.f;
+    for (int sp = 0; sp < qkv.splits; ++sp) {
+        const float* pr = qkv.p + sp * qkv.stride + (long)r * ncols + j;
+        float ta[MAXIT], tb[MAXIT];
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+            const int h = hg + it * ngroups;
+            if (h < nh) {
+                ta[it] = pr[h * dh];
+                tb[it] = pr[h * dh + half];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+            av[it] += ta[it];
+            bv[it] += tb[it];
+        }
+    }
+    if (qkv.a_scale) {
+        const float sa = qkv.a_scale[r];
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+            const int h = hg + it * ngroups;
+            if (h < nh) {
+                av[it] *= sa * qkv.b_scale[h * dh + j];
+                bv[it] *= sa * qkv.b_scale[h * dh + j + half];
+            }
+        }
+    }
     const double theta = pow((double)base, -2.0 * (double)j / (double)dh);
     double sd, cd;
     sincos((double)pos * theta, &sd, &cd);
     const float sn = (float)sd, cs = (float)cd;
     const long cap = seqs.cap[s];
-    for (int h = hg; h < hq + hkv; h += ngroups) {
-        const float a = partial_sum(qkv, r, h * dh + j, ncols);
-        const float b = partial_sum(qkv, r, h * dh + j + half, ncols);
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+        const int h = hg + it * ngroups;
+        if (h >= nh) continue;
+        const float a = av[it], b = bv[it];
         const float ra = a * cs - b * sn;
         const float rb = a * sn + b * cs;
         T* dst;

@@ -47,7 +47,12 @@ __device__ __forceinline__ void wait_stages(int p) {
     }
 }
 
-template <typename T, int BM_, int BN_, int WM_, int WN_, bool DUAL, int NS>
+// KW_ k-groups: 4 * KW_ waves share the tile and the LDS ring; k-group g
+// computes k-steps g, g + KW, ... of every stage, and the groups' accumulators
+// are added through LDS before the epilogue.  Two k-groups put two waves on
+// each SIMD, which doubles the LDS fragment bandwidth a SIMD can draw (one
+// wave reads at most ~27 B per clock from LDS).
+template <typename T, int BM_, int BN_, int WM_, int WN_, bool DUAL, int NS, int KW_ = 1>
 struct Core {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr bool TWO_B = DUAL;
@@ -58,18 +63,25 @@ struct Core {
     static constexpr int ROWS = BM + BN * (DUAL ? 2 : 1);           // rows per stage
     static constexpr int STAGE = ROWS * BKB;
     static constexpr int LDS_BYTES = NS * STAGE;
-    static constexpr int LPW = ROWS / 32;                           // 1-KB loads per wave per stage
+    static constexpr int KW = KW_;
+    static constexpr int NWAVES = 4 * KW;
+    static constexpr int THREADS = WAVE * NWAVES;
+    static constexpr int LPW = ROWS / 32 / KW;                      // 1-KB loads per wave per stage
+    static constexpr int KS = BKB / KSB;                            // MFMA k-steps per stage
+    static constexpr int KSW = KS / KW;                             // ... per k-group
     static constexpr int PART = TM * TN * 4;
     typedef typename Mfma<T>::frag frag;
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile");
-    static_assert(WM * WN == 4, "4 waves");
-    static_assert(ROWS % 32 == 0, "stage rows");
+    static_assert(WM * WN == 4, "4 waves per k-group");
+    static_assert(ROWS % (32 * KW) == 0 && KS % KW == 0, "stage rows / k-steps");
     static_assert((NS - 2) * LPW < 64, "vmcnt");
 
     const uint8_t* src[LPW];     // this lane's source (row + swizzled chunk) per load
     f32x4 acc[TM][TN];
     f32x4 acc2[DUAL ? TM : 1][DUAL ? TN : 1];
-    int wave;
+    int wave;                    // 0 .. NWAVES - 1
+    int pos;                     // wave within the k-group: (wm, wn) = (pos / WN, pos % WN)
+    int kg;                      // k-group
 
     // rowptr(R) -> address of stage row R (A rows, then B, then B2), always a
     // readable row (rows outside the matrix are clamped by the caller: they
@@ -77,6 +89,8 @@ struct Core {
     template <class F>
     __device__ __forceinline__ void init(F rowptr) {
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+        pos = wave % 4;
+        kg = wave / 4;
         const int lane = threadIdx.x % WAVE;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
@@ -104,38 +118,69 @@ struct Core {
                                              0, 0);
     }
 
-    __device__ __forceinline__ void compute(const uint8_t* stage) {
+    // Fragments of one stage as read from LDS (fp8 codes are widened at use).
+    typedef typename Mfma<T>::raw raw;
+    struct Frags {
+        raw a[KSW][TM], b[KSW][TN], b2[KSW][DUAL ? TN : 1];
+    };
+    // Register double-buffering of fragments when both sets, their widened
+    // copies (fp8) and the accumulators fit a wave's registers (512 with one
+    // wave per SIMD, 256 with two).
+    static constexpr int FRAG_REGS = KSW * (TM + TN * (DUAL ? 2 : 1)) * 4;
+    static constexpr int ACC_REGS = TM * TN * 4 * (DUAL ? 2 : 1);
+    static constexpr bool DB =
+        2 * FRAG_REGS + (sizeof(T) == 1 ? 2 * FRAG_REGS : 0) + ACC_REGS <= (KW == 1 ? 400 : 190);
+    static_assert(KW == 1 || WAVE * 4 * ACC_REGS * 4 <= LDS_BYTES, "k-group exchange fits the LDS ring");
+
+    __device__ __forceinline__ void read(Frags& f, const uint8_t* stage) const {
         const int lane = threadIdx.x % WAVE;
-        const int wm = wave / WN, wn = wave % WN;
+        const int wm = pos / WN, wn = pos % WN;
         const int sw = lane & 7;                       // rows of a fragment are 16-aligned: row & 7 == lane & 7
         const uint8_t* sa = stage + (wm * (BM / WM) + lane % 16) * BKB;
         const uint8_t* sb = stage + (BM + wn * (BN / WN) + lane % 16) * BKB;
 #pragma unroll
-        for (int s = 0; s < BKB / KSB; ++s) {
-            const int off = s * KSB + (lane / 16) * LB;
+        for (int ss = 0; ss < KSW; ++ss) {
+            const int off = (ss * KW + kg) * KSB + (lane / 16) * LB;
             const int phys = (((off >> 4) ^ sw) << 4) | (off & 15);
-            frag af[TM], bf[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = Mfma<T>::load(sa + i * 16 * BKB + phys);
+            for (int i = 0; i < TM; ++i) f.a[ss][i] = Mfma<T>::load(sa + i * 16 * BKB + phys);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = Mfma<T>::load(sb + j * 16 * BKB + phys);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::mac(af[i], bf[j], acc[i][j]);
+            for (int j = 0; j < TN; ++j) f.b[ss][j] = Mfma<T>::load(sb + j * 16 * BKB + phys);
             if constexpr (DUAL) {
-                frag bf2[TN];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) bf2[j] = Mfma<T>::load(sb + (BN + j * 16) * BKB + phys);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc2[i][j] = Mfma<T>::mac(af[i], bf2[j], acc2[i][j]);
+                for (int j = 0; j < TN; ++j) f.b2[ss][j] = Mfma<T>::load(sb + (BN + j * 16) * BKB + phys);
             }
         }
     }
 
-    // Accumulates K stages [kt0, kt1).
+    __device__ __forceinline__ void mma(const Frags& f) {
+#pragma unroll
+        for (int s = 0; s < KSW; ++s) {
+            frag af[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = Mfma<T>::widen(f.a[s][i]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const frag bf = Mfma<T>::widen(f.b[s][j]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) acc[i][j] = Mfma<T>::mac(af[i], bf, acc[i][j]);
+            }
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const frag bf = Mfma<T>::widen(f.b2[s][j]);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) acc2[i][j] = Mfma<T>::mac(af[i], bf, acc2[i][j]);
+                }
+            }
+        }
+    }
+
+    // Accumulates K stages [kt0, kt1).  Fragments are double-buffered in
+    // registers: after stage t+1's barrier its fragment reads are issued, then
+    // stage t's MFMAs (from the other register set), so LDS latency hides
+    // under the MFMAs; the slot of stage t (already in registers everywhere)
+    // is refilled with stage t + NS.
     __device__ __forceinline__ void run(uint8_t* smem, int kt0, int kt1) {
         zero();
         const int n = kt1 - kt0;
@@ -143,11 +188,88 @@ struct Core {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
             if (s < n) load_stage(smem, kt0 + s, s);
-        for (int t = 0; t < n; ++t) {
-            wait_stages<LPW, NS - 2>(min(NS - 2, n - 1 - t));
+        if constexpr (!DB) {
+            Frags f;
+            for (int t = 0; t < n; ++t) {
+                wait_stages<LPW, NS - 2>(min(NS - 2, n - 1 - t));
+                stage_barrier();
+                if (t + NS - 1 < n) load_stage(smem, kt0 + t + NS - 1, (t + NS - 1) % NS);
+                read(f, smem + (t % NS) * STAGE);
+                mma(f);
+                constexpr int NREAD = KSW * (TM + TN * (DUAL ? 2 : 1));
+                constexpr int NMFMA = KSW * TM * TN * (DUAL ? 2 : 1) * (sizeof(T) == 1 ? 2 : 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+            }
+            return;
+        }
+        Frags f0, f1;
+        wait_stages<LPW, NS - 2>(min(NS - 2, n - 1));
+        stage_barrier();
+        read(f0, smem);
+        if (NS - 1 < n) load_stage(smem, kt0 + NS - 1, NS - 1);
+        // one stage: stage t is in `cur`; stage t + 1 (< n) is read into `nxt`
+        auto step = [&](int t, Frags& cur, Frags& nxt) {
+            wait_stages<LPW, NS - 2>(min(NS - 2, n - 2 - t));
             stage_barrier();
-            if (t + NS - 1 < n) load_stage(smem, kt0 + t + NS - 1, (t + NS - 1) % NS);
-            compute(smem + (t % NS) * STAGE);
+            if (t + NS < n) load_stage(smem, kt0 + t + NS, (t + NS) % NS);
+            read(nxt, smem + ((t + 1) % NS) * STAGE);
+            mma(cur);
+            // keep the reads as one group ahead of the MFMAs through scheduling
+            constexpr int NREAD = KSW * (TM + TN * (DUAL ? 2 : 1));
+            constexpr int NMFMA = KSW * TM * TN * (DUAL ? 2 : 1) * (sizeof(T) == 1 ? 2 : 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+        };
+        int t = 0;
+        for (; t + 2 < n; t += 2) {
+            step(t, f0, f1);
+            step(t + 1, f1, f0);
+        }
+        if (t + 1 < n) {
+            step(t, f0, f1);
+            mma(f1);
+        } else {
+            mma(f0);
+        }
+    }
+
+    // Adds every k-group's accumulators into k-group 0 through LDS (the ring is
+    // free: run() ended with all loads waited for); true for the waves that
+    // then hold the tile's result.  Fixed order: group 0 + group 1.
+    __device__ __forceinline__ bool reduce(uint8_t* smem) {
+        if constexpr (KW == 1) {
+            return true;
+        } else {
+            const int lane = threadIdx.x % WAVE;
+            float* x = (float*)smem + (long)pos * ACC_REGS * WAVE + lane;   // [pos][reg][lane]
+            __syncthreads();
+            if (kg == 1) {
+                int r = 0;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            x[(r++) * WAVE] = acc[i][j][v];
+                            if constexpr (DUAL) x[(r++) * WAVE] = acc2[i][j][v];
+                        }
+            }
+            __syncthreads();
+            if (kg == 0) {
+                int r = 0;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            acc[i][j][v] += x[(r++) * WAVE];
+                            if constexpr (DUAL) acc2[i][j][v] += x[(r++) * WAVE];
+                        }
+            }
+            return kg == 0;
         }
     }
 };
@@ -195,7 +317,7 @@ template <class C, bool FP8, int EPI>
 __device__ __forceinline__ void epilogue(C& c, const EpiArgs& e, int m0, int n0, int mlim, int N, const int* gather,
                                          int gather_div, int ntile) {
     const int lane = threadIdx.x % WAVE;
-    const int wm = c.wave / C::WN, wn = c.wave % C::WN;
+    const int wm = c.pos / C::WN, wn = c.pos % C::WN;
     const int rbase = m0 + wm * (C::BM / C::WM) + 4 * (lane / 16);
     const int cbase = n0 + wn * (C::BN / C::WN) + lane % 16;
     if constexpr (EPI == EPI_LMHEAD) {
@@ -265,7 +387,7 @@ __device__ __forceinline__ void epilogue(C& c, const EpiArgs& e, int m0, int n0,
 template <class C>
 __device__ __forceinline__ void store_partial(C& c, float* part, float* part2, int m0, int n0, int M, int N) {
     const int lane = threadIdx.x % WAVE;
-    const int wm = c.wave / C::WN, wn = c.wave % C::WN;
+    const int wm = c.pos / C::WN, wn = c.pos % C::WN;
     const int rbase = m0 + wm * (C::BM / C::WM) + 4 * (lane / 16);
     const int cbase = n0 + wn * (C::BN / C::WN) + lane % 16;
 #pragma unroll
@@ -296,7 +418,7 @@ struct DenseArgs {
 // Workgroup order: ((n-tile * splits + split) * m-tiles + m-tile), remapped so
 // each XCD runs a contiguous range of it.
 template <class C, typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs a) {
+__global__ __launch_bounds__(C::THREADS) void gemm_dense_kernel(DenseArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
     const int mt_n = (a.M + C::BM - 1) / C::BM, nt_n = (a.N + C::BN - 1) / C::BN;
     const int lin = xcd_remap(blockIdx.x, mt_n * nt_n * a.splits);
@@ -319,6 +441,7 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs a) {
     const int nkt = (int)((long)a.K * sizeof(T) / BKB);
     const int per = (nkt + a.splits - 1) / a.splits;
     c.run(smem, split * per, min(nkt, (split + 1) * per));
+    if (!c.reduce(smem)) return;
     if (a.splits > 1) {
         const long mn = (long)a.M * a.N;
         store_partial(c, a.part + split * mn, a.part + (a.splits + split) * mn, m0, n0, a.M, a.N);
@@ -355,7 +478,7 @@ struct GroupedArgs {
 };
 
 template <class C, typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs a) {
+__global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
     const int nt_n = (a.N + C::BN - 1) / C::BN;
     const int lin = xcd_remap(blockIdx.x, a.max_mtiles * nt_n);
@@ -387,6 +510,7 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs a) {
         return B + (long)r * a.ldb;
     });
     c.run(smem, 0, (int)((long)a.K * sizeof(T) / BKB));
+    if (!c.reduce(smem)) return;
     EpiArgs e = a.e;
     if constexpr (sizeof(T) == 1) {
         e.b_scale = a.b_scale + (long)ex * a.bs_stride;
@@ -399,8 +523,8 @@ __global__ __launch_bounds__(256) void gemm_grouped_kernel(GroupedArgs a) {
 
 // Tile shapes (BM, BN, WM, WN, stages):
 //   small M (<= 64; the tiny model, short canvases)     32 x 64,  waves 1x4, 4 stages
-//   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2, 4 stages
-//     (SwiGLU pair: 128 x 64 x 2 weights if N >= 4096, else 64 x 32 x 2)
+//   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2 x 2 k-groups, 6 stages
+//     (SwiGLU pair: 128 x 64 x 2 weights, 2 k-groups, if N >= 4096, else 64 x 32 x 2)
 //   prefill M                                           128 x 128, waves 2x2, 4 stages
 //   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128, waves 4x1
 //   grouped (experts)                                   GROUPED_BM x 64, waves 1x4, 4 stages
@@ -471,7 +595,7 @@ static int launch_dense(const GemmDesc& d, hipStream_t st) {
     a.e = make_epi(d, C::BN);
     const int grid = ((d.M + C::BM - 1) / C::BM) * ((d.N + C::BN - 1) / C::BN) * a.splits;
     if (grid == 0) return 1;
-    launch((gemm_dense_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
+    launch((gemm_dense_kernel<C, T, EPI>), dim3(grid), dim3(C::THREADS), 0, st, a);
     return a.splits;
 }
 
@@ -497,7 +621,7 @@ static void launch_grouped(const GemmDesc& d, hipStream_t st) {
     a.e = make_epi(d, C::BN);
     const int grid = a.max_mtiles * ((d.N + C::BN - 1) / C::BN);
     if (d.M == 0 || grid == 0) return;
-    launch((gemm_grouped_kernel<C, T, EPI>), dim3(grid), dim3(256), 0, st, a);
+    launch((gemm_grouped_kernel<C, T, EPI>), dim3(grid), dim3(C::THREADS), 0, st, a);
 }
 
 // Tile variants a caller may force (GemmDesc::variant, the GEMM test entry
@@ -513,10 +637,14 @@ static bool with_variant(int v, F f) {
         case 6: f(Core<T, 64, 32, 2, 2, DUAL, 4>{}); return true;
         case 7: f(Core<T, 32, 64, 1, 4, DUAL, 4>{}); return true;
         case 8: f(Core<T, 64, 64, 2, 2, DUAL, 6>{}); return true;
+        case 9: f(Core<T, 128, 64, 2, 2, DUAL, 4, 2>{}); return true;
+        case 10: f(Core<T, 64, 64, 2, 2, DUAL, 4, 2>{}); return true;
+        case 11: f(Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>{}); return true;
+        case 12: f(Core<T, 64, DUAL ? 32 : 64, 2, 2, DUAL, DUAL ? 4 : 6, 2>{}); return true;
         default: return false;
     }
 }
-constexpr int GEMM_VARIANTS = 8;
+constexpr int GEMM_VARIANTS = 12;
 
 template <bool DUAL, int EPI, typename T, class F>
 static void with_core(const GemmDesc& d, F f) {
@@ -530,13 +658,14 @@ static void with_core(const GemmDesc& d, F f) {
         if (d.M <= 64) f(CoreS<T, DUAL>{});
         else if (d.M <= 256) {
             // measured on the canvas shapes (M = 256) with weights streamed
-            // from HBM: 64 x 64 tiles for the projections; a SwiGLU pair gets
-            // 128 x 64 tiles when wide, 64 x 32 when narrow
+            // from HBM: 64 x 64 tiles, 6 stages, two k-groups for the
+            // projections; a SwiGLU pair gets 128 x 64 tiles with two k-groups
+            // when wide, 64 x 32 when narrow
             if constexpr (DUAL) {
-                if (d.N >= 4096) f(Core<T, 128, 64, 2, 2, true, 4>{});
+                if (d.N >= 4096) f(Core<T, 128, 64, 2, 2, true, 4, 2>{});
                 else f(Core<T, 64, 32, 2, 2, true, 4>{});
             } else {
-                f(CoreM<T, false>{});
+                f(Core<T, 64, 64, 2, 2, false, 6, 2>{});
             }
         } else f(CoreL<T, DUAL>{});
     }
