@@ -38,6 +38,14 @@ def test_fullsize_moe_two_layers():
     lockstep(_two_layers(synth.get_run("moe")), "moe (full width, 2 layers)", max_steps=2)
 
 
+def test_fullsize_moe_fp8_one_layer():
+    """fp8 kernels at full width where one layer keeps a flipped activation
+    code from reaching the other rows through attention."""
+    run = replace(synth.get_run("moe-fp8"), n_canvases=1)
+    run = replace(run, model=replace(run.model, n_layers=1))
+    lockstep(run, "moe-fp8 (full width, 1 layer)", max_steps=2)
+
+
 @pytest.mark.xfail(strict=False, reason=(
     "fp8 per-token activation codes decided on near-ties cascade: under relative noise of 1e-7 to 1e-5 "
     "(fp32 rounding and accumulation) the float64 oracle's own logits move by 0.29 to 0.45 against a "
