@@ -240,7 +240,12 @@ def main():
     log(f"{cfg.name}: weights drawn on the {'GPU' if big else 'host'} in {time.perf_counter() - t:.1f} s")
     model = DLM(cfg, weights if big else {k: v.cuda() for k, v in weights.items()}, canvas=C)
     cap = run.capacity()
-    seqs = [model.new_seq(cap) for _ in range(R)]
+    if R > 1:     # independent requests: each cache in 64-token pages of one shared pool
+        from masked_block_diffusion_amd import KVPool
+        pool = KVPool(model, R * (-(-cap // 64)))
+        seqs = [model.new_seq(cap, pool) for _ in range(R)]
+    else:
+        seqs = [model.new_seq(cap) for _ in range(R)]
     ws = model.workspace(max(R * C, run.max_prefix), cap)
     prefixes = [p.cuda() for p in prefixes_cpu]
     rule = Rule.topk(C, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
@@ -344,6 +349,7 @@ def main():
             "prefix": run.max_prefix if R == 1 else [len(p) for p in prefixes_cpu],
             "denoise_steps_per_canvas": steps_last / run.n_canvases,
             "parallelism": "single GPU",
+            "kv_cache": "paged, 64-token pages of one pool" if R > 1 else "contiguous per request",
         },
         "ms_per_denoise_step": step_ms,
         "decode_tokens_per_s": (R * C * run.n_canvases / ((denoise_ms + append_ms) * 1e-3)

@@ -146,18 +146,30 @@ typedef struct {
 } dlm_weights;
 
 /* One request.  Host struct of non-owning device pointers.
- *   kv: KV cache, bf16 (fp32 for DLM_F32 models), per layer and KV head a
- *       key block then a value block: [n_layers][2][n_kv_heads][capacity *
- *       head_dim] with the key block [capacity][head_dim] (row t: the
- *       post-RoPE key of absolute position t) and the value block stored
- *       transposed, [head_dim][capacity] (column t: the value of position t),
- *       so attention reads consecutive positions of one value dimension.
- *       Slots not yet written may hold anything; they are never used.
+ *   kv: KV cache, bf16 (fp32 for DLM_F32 models).
+ *     Contiguous (page_table NULL): per layer and KV head a key block then a
+ *       value block: [n_layers][2][n_kv_heads][capacity * head_dim], the key
+ *       block [capacity][head_dim] (row t: the post-RoPE key of absolute
+ *       position t), the value block stored transposed, [head_dim][capacity]
+ *       (column t: the value of position t), so attention reads consecutive
+ *       positions of one value dimension.
+ *     Paged (page_table set): kv is the base of a pool of 64-token pages;
+ *       position t lives in page page_table[t / 64] at slot t % 64.  A page
+ *       holds all layers and heads of its tokens, [n_layers][2][n_kv_heads]
+ *       [64 * head_dim], keys [64][head_dim] and transposed values
+ *       [head_dim][64]; page p starts p * n_layers * 2 * n_kv_heads * 64 *
+ *       head_dim elements after kv.  Requests may share a pool; the pages of
+ *       one request must be distinct and not used by another request in the
+ *       same call.
+ *     Slots not yet written may hold anything; they are never used.
  *   capacity: tokens the cache holds; a multiple of 8 (E_SHAPE otherwise), so
- *       every transposed value row is 16-byte aligned.
+ *       every transposed value row is 16-byte aligned; paged: a multiple of
+ *       64, the table then has capacity / 64 entries.
  *   T: tokens cached so far (prefix plus appended canvases).
  *   canvas: device int32[C], the block being denoised ([MASK] = mask_id).
- *   page_table / page_size: reserved for a paged cache; must be NULL / 0. */
+ *   page_table: device int32[capacity / 64] page indices into the pool, or
+ *       NULL; page_size: 64 with a page table (E_UNSUPPORTED otherwise), 0
+ *       without one (E_ARG otherwise). */
 typedef struct {
     void*          kv;
     int32_t        capacity;

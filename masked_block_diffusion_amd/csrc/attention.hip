@@ -5,8 +5,8 @@
 // prefix.  Prefill ("causal") mode: the query at position p sees keys [0, p].
 // Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
 //
-// Cache layout per (layer, KV head): K [capacity][dh], V transposed
-// [dh][capacity] (written so by the RoPE / cache-write kernel).
+// Cache: per (layer, KV head) keys as rows and values transposed, contiguous
+// or in 64-token pages (kvcache.h); a 64-key tile is one KV block (one page).
 //
 // bf16 kernel (flash-style, online softmax in fp32):
 //   * A workgroup owns one KV head of one request, 128 "query rows" (pairs of
@@ -27,7 +27,8 @@
 //   * Long key ranges are split across workgroups (split-KV); partial (max,
 //     sum, unnormalised O) are merged by a second kernel in fixed split order.
 //   * Keys past the end of the range are never read from memory the caller
-//     has not written: their K rows are fetched from key 0 (and masked), and
+//     has not written: their K rows are fetched from the tile's first key (and
+//     masked), and
 //     V^T chunks reaching past the end are zeroed in LDS by the lane that
 //     fetched them (unwritten cache slots may hold any bit pattern, and 0 * NaN
 //     would poison the sum).
@@ -35,6 +36,7 @@
 // fp32 throughout.
 #include "common.h"
 #include "kernels.h"
+#include "kvcache.h"
 
 namespace dlm {
 
@@ -102,9 +104,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int per = a.seqs.per_seq;
     const int T = a.seqs.T[sq];
     const int n_keys = T + per;
-    const long cap = a.seqs.cap[sq];
-    const bf16_t* kbase = (const bf16_t*)a.seqs.kv[sq] + (((long)a.layer * 2 + 0) * a.hkv + kvh) * cap * DH;
-    const bf16_t* vbase = (const bf16_t*)a.seqs.kv[sq] + (((long)a.layer * 2 + 1) * a.hkv + kvh) * cap * DH;
 
     // this lane's two query rows (one per 16-row block)
     const int nq = per * a.group;
@@ -155,18 +154,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             lchunk[j] = p ^ (d % S::VCH);
         }
     }
+    // tile t is KV block t of the cache (one page when paged); keys at or past
+    // kend are fetched from the tile's first key / first chunk instead
     auto issue = [&](int tile, int slot) {
         const int k0 = tile * KT;
+        const KVBlock<const bf16_t> kb = kv_block<const bf16_t>(a.seqs, sq, a.layer, a.hkv, kvh, DH, tile);
         uint8_t* st = smem + slot * S::STAGE;
 #pragma unroll
         for (int j = 0; j < S::LPT; ++j) {
             const bf16_t* src;
             if (j < S::KLPT) {
                 const int key = k0 + lrow[j];
-                src = kbase + (long)(key < kend ? key : 0) * DH + lchunk[j] * 8;
+                src = kb.k + (long)(key < kend ? lrow[j] : 0) * DH + lchunk[j] * 8;
             } else {
                 const int kc = k0 + 8 * lchunk[j];
-                src = vbase + (long)lrow[j] * cap + (kc < kend ? kc : 0);
+                src = kb.vt + (long)lrow[j] * kb.vstride + (kc < kend ? 8 * lchunk[j] : 0);
             }
             __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(st + (j * 4 + wave) * 1024), 16, 0, 0);
         }
@@ -356,9 +358,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, SeqTab seq
     const int T = seqs.T[sq];
     const int pos = T + i;
     const int kvh = h / (hq / hkv);
-    const long cap = seqs.cap[sq];
-    const float* kb = (const float*)seqs.kv[sq] + (((long)layer * 2 + 0) * hkv + kvh) * cap * DH;
-    const float* vtb = (const float*)seqs.kv[sq] + (((long)layer * 2 + 1) * hkv + kvh) * cap * DH;
     const int kend = causal ? pos + 1 : T + per;
     float qv[DH], o[DH];
 #pragma unroll
@@ -367,17 +366,20 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, SeqTab seq
         o[c] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
+    KVBlock<const float> b{};
     for (int k = 0; k < kend; ++k) {
+        if (k % KV_PAGE == 0) b = kv_block<const float>(seqs, sq, layer, hkv, kvh, DH, k / KV_PAGE);
+        const int i = k % KV_PAGE;
         float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < DH; ++c) s += qv[c] * kb[(long)k * DH + c];
+        for (int c = 0; c < DH; ++c) s += qv[c] * b.k[(long)i * DH + c];
         s *= scale;
         const float mn = fmaxf(m, s);
         const float al = expf(m - mn);
         const float p = expf(s - mn);
         l = l * al + p;
 #pragma unroll
-        for (int c = 0; c < DH; ++c) o[c] = o[c] * al + p * vtb[(long)c * cap + k];
+        for (int c = 0; c < DH; ++c) o[c] = o[c] * al + p * b.vt[(long)c * b.vstride + i];
         m = mn;
     }
 #pragma unroll

@@ -255,7 +255,11 @@ dlm_status check_weights(const dlm_config* c, const dlm_weights* w) {
 dlm_status check_seq(const dlm_model* m, const dlm_seq* s, int extra, bool need_canvas, int idx) {
     if (!s) return fail(DLM_E_ARG, "seq %d is NULL", idx);
     if (!s->kv) return fail(DLM_E_ARG, "seq %d: kv is NULL", idx);
-    if (s->page_table || s->page_size) return fail(DLM_E_UNSUPPORTED, "seq %d: paged KV cache is not supported", idx);
+    if (s->page_table && s->page_size != KV_PAGE)
+        return fail(DLM_E_UNSUPPORTED, "seq %d: page_size %d (pages hold %d tokens)", idx, s->page_size, KV_PAGE);
+    if (!s->page_table && s->page_size) return fail(DLM_E_ARG, "seq %d: page_size without page_table", idx);
+    if (s->page_table && s->capacity % KV_PAGE)
+        return fail(DLM_E_SHAPE, "seq %d: paged capacity %d is not a multiple of %d", idx, s->capacity, KV_PAGE);
     if (need_canvas && !s->canvas) return fail(DLM_E_ARG, "seq %d: canvas is NULL", idx);
     if (s->T < 0 || s->capacity < 0) return fail(DLM_E_ARG, "seq %d: negative T or capacity", idx);
     if (s->capacity % 8 != 0) return fail(DLM_E_SHAPE, "seq %d: capacity %d is not a multiple of 8", idx, s->capacity);
@@ -518,10 +522,13 @@ dlm_status build_tab(dlm_model* m, dlm_seq* const* seqs, int n_seqs, int extra, 
         dlm_status s = check_seq(m, seqs[i], extra, need_canvas, i);
         if (s) return s;
         tab.kv[i] = seqs[i]->kv;
+        tab.pt[i] = seqs[i]->page_table;
         tab.T[i] = seqs[i]->T;
         tab.cap[i] = seqs[i]->capacity;
         max_kv = std::max(max_kv, seqs[i]->T + extra);
     }
+    const dlm_config& c = m->cfg;
+    tab.page_elems = (long)c.n_layers * 2 * c.n_kv_heads * KV_PAGE * c.head_dim;
     tab.n = n_seqs;
     tab.per_seq = extra;
     return DLM_OK;

@@ -13,6 +13,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kvcache.h"
 
 namespace dlm {
 
@@ -214,9 +215,10 @@ void quant_rows(const uint16_t* x, int rows, int d, uint8_t* q, float* s, hipStr
 // rotated by pos * base^(-2i/dh).  The angle and its sine/cosine are formed in
 // double precision (positions reach several thousand), then applied in fp32.
 //
-// Cache layout per (layer, KV head): K is [capacity][dh] (a key per row), V is
-// stored transposed, [dh][capacity], so the attention kernel's P V operand
-// reads consecutive keys.  Blocks [0, rows) rotate Q and K of one token row;
+// Cache layout (kvcache.h): per (layer, KV head) K as rows [token][dh] and V
+// transposed [dh][token], contiguous or in 64-token pages, so the attention
+// kernel's P V operand reads consecutive keys.  Blocks [0, rows) rotate Q and
+// K of one token row;
 // the blocks after them each transpose V of up to 64 rows of one KV head
 // through LDS, so every wave writes 64 consecutive positions of one dh row.
 constexpr int VT_ROWS = 64;                // rows per V^T block
@@ -271,9 +273,8 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, 
             if (rr >= nr) continue;
             const int r = r0 + rr, s = r / seqs.per_seq;
             const int pos = seqs.T[s] + r % seqs.per_seq;
-            const long cap = seqs.cap[s];
-            T* vt = (T*)seqs.kv[s] + (((long)layer * 2 + 1) * hkv + kh) * cap * dh;
-            vt[(long)(sl * VT_COLS + d) * cap + pos] = tile[rr * PITCH + d];
+            const KVBlock<T> b = kv_block<T>(seqs, s, layer, hkv, kh, dh, pos / KV_PAGE);
+            b.vt[(long)(sl * VT_COLS + d) * b.vstride + pos % KV_PAGE] = tile[rr * PITCH + d];
         }
         return;
     }
@@ -322,7 +323,6 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, 
     double sd, cd;
     sincos((double)pos * theta, &sd, &cd);
     const float sn = (float)sd, cs = (float)cd;
-    const long cap = seqs.cap[s];
 #pragma unroll
     for (int it = 0; it < MAXIT; ++it) {
         const int h = hg + it * ngroups;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NT) void rope_kv_kernel(Partials qkv, SeqTab seqs, 
         if (h < hq) {
             dst = (T*)q_out + ((long)r * hq + h) * dh;
         } else {
-            dst = (T*)seqs.kv[s] + (((long)layer * 2 + 0) * hkv + (h - hq)) * cap * dh + (long)pos * dh;
+            dst = kv_block<T>(seqs, s, layer, hkv, h - hq, dh, pos / KV_PAGE).k + (long)(pos % KV_PAGE) * dh;
         }
         if constexpr (F32) {
             dst[j] = ra;

@@ -559,8 +559,8 @@ static int splits_for(const GemmDesc& d) {
     // a SwiGLU split would need its own epilogue kernel (the nonlinearity
     // needs the full sums): never split it
     // tiles of two k-groups already put 8 waves on a CU: splitting them
-    // measured slower from 128 tiles up
-    if (C::TWO_B || tiles >= (C::KW > 1 ? 128 : SPLIT_TARGET_WG * 3 / 4) || d.M > 256) return 1;
+    // measured slower from 160 tiles up (faster at 128)
+    if (C::TWO_B || tiles >= (C::KW > 1 ? 160 : SPLIT_TARGET_WG * 3 / 4) || d.M > 256) return 1;
     int s = (int)((SPLIT_TARGET_WG + tiles - 1) / tiles);
     s = std::min(s, std::max(1, nkt / 4));
     s = std::min(s, 2);

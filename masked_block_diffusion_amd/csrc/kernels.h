@@ -91,12 +91,18 @@ struct IdSource {
 };
 
 // Requests of one forward: KV cache base, cached tokens T and capacity.
+// Tokens per KV page (the attention kernel's key tile).
+constexpr int KV_PAGE = 64;
+
+// The requests of one forward and their caches (layout in kvcache.h).
 struct SeqTab {
-    void* kv[MAX_SEQS];
+    void* kv[MAX_SEQS];          // contiguous cache, or the page pool's base
+    const int* pt[MAX_SEQS];     // page table (device), NULL for a contiguous cache
     int T[MAX_SEQS];
-    int cap[MAX_SEQS];   // capacity (tokens) of each request's cache
+    int cap[MAX_SEQS];           // capacity (tokens) of each request's cache
+    long page_elems;             // elements per page: n_layers * 2 * n_kv_heads * KV_PAGE * head_dim
     int n;
-    int per_seq;         // rows per request in this forward
+    int per_seq;                 // rows per request in this forward
 };
 
 // x[r] = float(embed[id_r]); ids outside [0, vocab) set DEVERR_TOKEN_RANGE

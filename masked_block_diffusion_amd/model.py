@@ -35,16 +35,23 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+KV_PAGE = 64   # tokens per KV page
+
+
 @dataclass
 class Seq:
-    """One request: its KV cache [L, 2, Hkv, capacity * dh] (per layer and KV
-    head a key block [capacity, dh] and a value block stored transposed,
-    [dh, capacity]), its canvas int32[C] and the ABI struct pointing at both
-    (T lives in the struct)."""
+    """One request: its canvas int32[C], its KV cache and the ABI struct
+    pointing at both (T lives in the struct).  Contiguous cache: `kv` is
+    [L, 2, Hkv, capacity * dh], per layer and KV head a key block [capacity,
+    dh] and a value block stored transposed, [dh, capacity].  Paged cache:
+    `kv` is the pool [pages, L, 2, Hkv, 64 * dh] and `pages` the request's page
+    indices (int32, device), token t in page pages[t // 64] at slot t % 64."""
     kv: torch.Tensor
     canvas: torch.Tensor
     raw: abi.dlm_seq
     head_dim: int
+    pages: Optional[torch.Tensor] = None
+    pool: Optional["KVPool"] = None
 
     @property
     def T(self) -> int:
@@ -54,17 +61,58 @@ class Seq:
     def capacity(self) -> int:
         return self.raw.capacity
 
-    @property
-    def k(self) -> torch.Tensor:
-        """Keys, a view [L, Hkv, capacity, dh]."""
-        L, _, H, _ = self.kv.shape
-        return self.kv[:, 0].view(L, H, self.capacity, self.head_dim)
+    def read_kv(self):
+        """(keys, values), each [L, Hkv, capacity, dh] (a copy when paged)."""
+        dh = self.head_dim
+        if self.pages is None:
+            L, _, H, _ = self.kv.shape
+            k = self.kv[:, 0].view(L, H, self.capacity, dh)
+            v = self.kv[:, 1].view(L, H, dh, self.capacity).transpose(-1, -2)
+            return k, v
+        pg = self.kv[self.pages.long()]                              # [P, L, 2, H, 64 * dh]
+        P, L, _, H, _ = pg.shape
+        k = pg[:, :, 0].reshape(P, L, H, KV_PAGE, dh).permute(1, 2, 0, 3, 4).reshape(L, H, P * KV_PAGE, dh)
+        v = pg[:, :, 1].reshape(P, L, H, dh, KV_PAGE).permute(1, 2, 0, 4, 3).reshape(L, H, P * KV_PAGE, dh)
+        return k, v
 
-    @property
-    def v(self) -> torch.Tensor:
-        """Values, a (strided) view [L, Hkv, capacity, dh] of the transposed block."""
-        L, _, H, _ = self.kv.shape
-        return self.kv[:, 1].view(L, H, self.head_dim, self.capacity).transpose(-1, -2)
+    def write_kv(self, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Stores keys / values [L, Hkv, n, dh] into token slots [0, n)."""
+        n, dh = k.shape[2], self.head_dim
+        if self.pages is None:
+            ck, cv = self.read_kv()
+            ck[:, :, :n].copy_(k)
+            cv[:, :, :n].copy_(v)
+            return
+        L, H = k.shape[0], k.shape[1]
+        for b in range((n + KV_PAGE - 1) // KV_PAGE):
+            lo, hi = b * KV_PAGE, min(n, (b + 1) * KV_PAGE)
+            page = self.kv[int(self.pages[b])]                       # [L, 2, H, 64 * dh]
+            pk = page[:, 0].view(L, H, KV_PAGE, dh)
+            pv = page[:, 1].view(L, H, dh, KV_PAGE)
+            pk[:, :, : hi - lo].copy_(k[:, :, lo:hi])
+            pv[:, :, :, : hi - lo].copy_(v[:, :, lo:hi].transpose(-1, -2))
+
+
+class KVPool:
+    """A device pool of 64-token KV pages shared by requests, with a free list
+    on the host.  A page holds all layers and heads of its tokens:
+    [L, 2, Hkv, 64 * dh] (keys [64, dh], values transposed [dh, 64])."""
+
+    def __init__(self, model: "DLM", n_pages: int):
+        c = model.cfg
+        self.model = model
+        self.kv = torch.empty((n_pages, c.n_layers, 2, c.n_kv_heads, KV_PAGE * c.head_dim),
+                              dtype=model.kv_dtype, device=model.device)
+        self.free = list(range(n_pages))
+
+    def alloc(self, n: int, order=None) -> torch.Tensor:
+        if n > len(self.free):
+            raise MemoryError(f"KV pool has {len(self.free)} free pages, {n} requested")
+        take = [self.free.pop(0 if order is None else order(len(self.free))) for _ in range(n)]
+        return torch.tensor(take, dtype=torch.int32, device=self.model.device)
+
+    def release(self, pages: torch.Tensor) -> None:
+        self.free.extend(int(p) for p in pages.cpu())
 
 
 class DLM:
@@ -137,17 +185,24 @@ class DLM:
         return W
 
     # -------------------------------------------------------------- state --
-    def new_seq(self, capacity: int) -> Seq:
+    def new_seq(self, capacity: int, pool: Optional[KVPool] = None, order=None) -> Seq:
         """A request whose cache holds at least `capacity` tokens (rounded up to
-        a multiple of 64, the attention kernel's key tile)."""
+        a multiple of 64, the attention kernel's key tile): its own contiguous
+        cache, or pages from `pool` (`order(n_free)` picks which free page to
+        take next; the default takes them in order)."""
         c = self.cfg
-        capacity = -(-capacity // 64) * 64
-        kv = torch.empty((c.n_layers, 2, c.n_kv_heads, capacity * c.head_dim), dtype=self.kv_dtype,
-                         device=self.device)
+        capacity = -(-capacity // KV_PAGE) * KV_PAGE
         canvas = torch.full((self.C,), c.mask_id, dtype=torch.int32, device=self.device)
-        raw = abi.dlm_seq(kv=kv.data_ptr(), capacity=capacity, T=0, canvas=canvas.data_ptr(),
-                          page_table=None, page_size=0)
-        return Seq(kv, canvas, raw, c.head_dim)
+        if pool is None:
+            kv = torch.empty((c.n_layers, 2, c.n_kv_heads, capacity * c.head_dim), dtype=self.kv_dtype,
+                             device=self.device)
+            raw = abi.dlm_seq(kv=kv.data_ptr(), capacity=capacity, T=0, canvas=canvas.data_ptr(),
+                              page_table=None, page_size=0)
+            return Seq(kv, canvas, raw, c.head_dim)
+        pages = pool.alloc(capacity // KV_PAGE, order)
+        raw = abi.dlm_seq(kv=pool.kv.data_ptr(), capacity=capacity, T=0, canvas=canvas.data_ptr(),
+                          page_table=pages.data_ptr(), page_size=KV_PAGE)
+        return Seq(pool.kv, canvas, raw, c.head_dim, pages, pool)
 
     def workspace_bytes(self, max_rows: int, max_kv: int) -> int:
         return int(self.lib.dlm_workspace_bytes(self.handle, max_rows, max_kv))

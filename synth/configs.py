@@ -164,7 +164,7 @@ RUNS = {
                                 n_steps=48, threshold=0.5),
     "moe-mini-batch": RunConfig("moe-mini-batch", MOE_BF16_MINI, canvas=64, n_requests=4,
                                 prefix_len=(20, 150), n_canvases=1, rule="topk",
-                                n_steps=12, page_size=16),
+                                n_steps=12),
 }
 
 

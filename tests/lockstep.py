@@ -9,6 +9,8 @@ prefill and after every append: the new KV slots within the dtype's tolerance.
 
 `max_steps` stops a canvas early: both sides then fill its remaining masked
 positions with the oracle's predictions, so the append is still compared.
+`paged` gives every request its cache as pages of one shared pool, drawn in
+a shuffled order (so neighbouring tokens of a request sit in unrelated pages).
 `sample` lists the requests the oracle follows; the GPU still runs the whole
 batch (the launch shapes of the full workload), the other requests evolve on
 the GPU alone and are checked by the properties that hold for any request:
@@ -25,12 +27,12 @@ from tests.parity import LOGIT_TOL, StepReport, compare_commit, compare_logits, 
 
 
 def _kv_close(gseq, ost, T, dtype, what, lo=0):
-    """GPU cache (keys and values as [L, Hkv, cap, dh] views) against the
-    oracle's per-layer K/V over slots [lo, T): relative RMS error per layer and
-    kind (an intermediate tensor: one near-tie router or fp8-code flip moves a
-    few elements by a quantisation step, which a max-abs bound would charge to
-    the whole cache)."""
-    g = [gseq.k.float().cpu().numpy(), gseq.v.float().cpu().numpy()]
+    """GPU cache (keys and values as [L, Hkv, cap, dh], gathered from pages when
+    paged) against the oracle's per-layer K/V over slots [lo, T): relative RMS
+    error per layer and kind (an intermediate tensor: one near-tie router or
+    fp8-code flip moves a few elements by a quantisation step, which a max-abs
+    bound would charge to the whole cache)."""
+    g = [t.float().cpu().numpy() for t in gseq.read_kv()]
     worst = 0.0
     for l in range(g[0].shape[0]):
         for kind, ref in ((0, ost.k[l]), (1, ost.v[l])):
@@ -48,20 +50,19 @@ def _load_cache(gseq, ost):
     T = ost.T
     k = np.stack([ost.k[l][:, :T] for l in range(len(ost.k))])
     v = np.stack([ost.v[l][:, :T] for l in range(len(ost.v))])
-    gseq.k[:, :, :T].copy_(torch.from_numpy(k).to(gseq.kv.dtype))
-    gseq.v[:, :, :T].copy_(torch.from_numpy(v).to(gseq.kv.dtype))
+    gseq.write_kv(torch.from_numpy(k).to(gseq.kv.dtype).cuda(), torch.from_numpy(v).to(gseq.kv.dtype).cuda())
 
 
 
-def lockstep(run, label, max_steps=None, sample=None, weights=None):
-    from masked_block_diffusion_amd import DLM, Rule
+def lockstep(run, label, max_steps=None, sample=None, weights=None, paged=False):
+    from masked_block_diffusion_amd import DLM, KVPool, Rule
 
     cfg = run.model
     C, n = run.canvas, run.n_requests
     sample = list(range(n)) if sample is None else list(sample)
     steps = run.n_steps if max_steps is None else min(run.n_steps, max_steps)
     print(f"[parity] run={label} dtype={cfg.dtype} ffn={cfg.ffn} L={cfg.n_layers} d={cfg.d_model} "
-          f"V={cfg.vocab} C={C} requests={n} sampled={sample} steps/canvas={steps}", flush=True)
+          f"V={cfg.vocab} C={C} requests={n} sampled={sample} steps/canvas={steps} paged={paged}", flush=True)
     w = synth.make_weights(cfg, seed=run.seed) if weights is None else weights
     om = OracleModel(cfg, OracleWeights(cfg, w))
     gm = DLM(cfg, {k: v.cuda() for k, v in w.items()}, canvas=C)
@@ -69,7 +70,13 @@ def lockstep(run, label, max_steps=None, sample=None, weights=None):
     prefixes = synth.make_inputs(run)
     cap = run.capacity()
     ost = {r: om.new_seq(cap) for r in sample}
-    gseqs = [gm.new_seq(cap) for _ in range(n)]
+    if paged:
+        per = -(-cap // 64)
+        pool = KVPool(gm, n * per + 3)
+        rng = np.random.default_rng(7)
+        gseqs = [gm.new_seq(cap, pool, order=lambda nf: int(rng.integers(nf))) for _ in range(n)]
+    else:
+        gseqs = [gm.new_seq(cap) for _ in range(n)]
     ws = gm.workspace(max(n * C, max(len(p) for p in prefixes)), cap)
     for r in range(n):
         if r in ost:

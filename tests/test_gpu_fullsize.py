@@ -9,7 +9,8 @@ canvas lengths, so every kernel runs its real grid and tile choice):
     26B weights in float64): prefill of the 4096-token prompt, the first
     denoising steps, the append -- in bf16, and in fp8 with the threshold rule;
   * the 32-request batch (prefixes of 512..4096 tokens, 8192 canvas rows per
-    step) at full width, two layers: the GPU runs the whole batch, the oracle
+    step, every request's cache in 64-token pages of one pool) at full width,
+    two layers: the GPU runs the whole batch, the oracle
     follows two of the requests (requests never interact, so each can be
     computed alone); the others are checked by the commit properties.
 
@@ -59,4 +60,4 @@ def test_fullsize_batch32_two_layers():
     lengths = synth.prefix_lengths(run)
     sample = [min(range(len(lengths)), key=lambda r: lengths[r]),      # shortest and longest prompts
               max(range(len(lengths)), key=lambda r: lengths[r])]
-    lockstep(run, "moe-batch32 (full width, 2 layers)", max_steps=2, sample=sample)
+    lockstep(run, "moe-batch32 (full width, 2 layers, paged)", max_steps=2, sample=sample, paged=True)

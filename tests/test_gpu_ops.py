@@ -204,3 +204,31 @@ def test_gemm_fp8_small_integers_exact():
         torch.cuda.synchronize()
         got = C.cpu().numpy().astype(np.float64)
         assert np.array_equal(got, ref[:mm]), f"M={mm}: {np.sum(got != ref[:mm])} differ"
+
+
+def test_paged_cache_validation():
+    """Page tables need 64-token pages and a capacity of whole pages; a page
+    size without a table is an argument error."""
+    import synth
+    from masked_block_diffusion_amd import DLM, KVPool, abi
+    run = synth.get_run("tiny")
+    gm = DLM(run.model, {k: v.cuda() for k, v in synth.make_weights(run.model).items()}, canvas=run.canvas)
+    pool = KVPool(gm, 4)
+    seq = gm.new_seq(128, pool)
+    ids = synth.make_inputs(run)[0].cuda()
+    ws = gm.workspace(len(ids), 128)
+    for page_size, cap, status in ((16, 128, abi.DLM_E_UNSUPPORTED), (64, 96, abi.DLM_E_SHAPE)):
+        seq.raw.page_size, seq.raw.capacity = page_size, cap
+        with pytest.raises(abi.DLMError) as e:
+            gm.dlm_prefill(seq, ids, ws)
+        assert e.value.status == status
+    seq.raw.page_size, seq.raw.capacity = 64, 128
+    plain = gm.new_seq(128)
+    plain.raw.page_size = 64
+    with pytest.raises(abi.DLMError) as e:
+        gm.dlm_prefill(plain, ids, ws)
+    assert e.value.status == abi.DLM_E_ARG
+    gm.dlm_prefill(seq, ids, ws)
+    torch.cuda.synchronize()
+    assert seq.T == len(ids)
+    gm.close()

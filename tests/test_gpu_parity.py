@@ -3,7 +3,7 @@ tests/lockstep.py for what is compared at every step).
 
 Runs: the tiny fp32 model at its full size, and reduced bf16/fp8, dense/MoE,
 single- and multi-request variants whose vocabulary, canvas and prefix sizes
-are not multiples of any kernel tile.  The full-size workloads are in
+are not multiples of any kernel tile; three of them again with paged caches.  The full-size workloads are in
 tests/test_gpu_fullsize.py.
 """
 import pytest
@@ -20,3 +20,10 @@ RUNS = ["tiny", "dense-mini", "dense-mini-ragged", "moe-mini", "dense-mini-fp8",
 @pytest.mark.parametrize("name", RUNS)
 def test_lockstep_parity(name):
     lockstep(synth.get_run(name), name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dense-mini-ragged", "moe-mini-batch"])
+def test_lockstep_parity_paged(name):
+    """The same runs with every request's cache in 64-token pages of one pool,
+    taken in a shuffled order."""
+    lockstep(synth.get_run(name), name + " (paged)", paged=True)
