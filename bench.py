@@ -206,11 +206,13 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="for runs under a profiler: no per-kernel event timing (no roofline), "
                          "no expert counting, no CPU baseline")
+    ap.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="with --profile: one canvas of this many denoising steps per request")
     args = ap.parse_args()
     if args.profile:
         args.no_cpu_baseline = True
+        args.no_graphs = True
     elif args.profile_steps:
         ap.error("--profile-steps needs --profile")
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -222,7 +224,7 @@ def main():
     import torch
 
     import synth
-    from masked_block_diffusion_amd import DLM, Rule
+    from masked_block_diffusion_amd import DLM, CanvasSteps, Rule
     from masked_block_diffusion_amd import abi
 
     def log(msg):
@@ -260,7 +262,9 @@ def main():
     dbg_ids = torch.empty(L * R * C * max(1, cfg.top_k), dtype=torch.int32, device="cuda") if moe else None
     used_per_launch = []     # distinct experts per (step, layer), MoE only
 
-    def one_request(timed_ids, count_experts=False):
+    graph_cache = {}
+
+    def one_request(timed_ids, count_experts=False, graphs=False):
         for s, ids in zip(seqs, prefixes):
             s.raw.T = 0
             model.dlm_prefill(s, ids, ws)
@@ -268,11 +272,22 @@ def main():
         for ci in range(run.n_canvases):
             for s in seqs:
                 s.canvas.fill_(cfg.mask_id)
+            cg = None
+            if graphs:
+                cg = graph_cache.get(ci)
+                if cg is None or not cg.valid_for(seqs):
+                    cg = graph_cache[ci] = CanvasSteps(model, seqs, conf, pred, rule, ws, None, n_masked)
             model.timing_enable(timed_ids)
             ev[4 * ci].record()
             if count_experts:
                 model.dlm_debug_router(dbg_ids, None, L * R * C)
             for st in range(run.n_steps):
+                if cg is not None:
+                    cg.replay(st)
+                    steps_run += 1
+                    if run.rule == "threshold" and int(n_masked.max().cpu()) == 0:
+                        break
+                    continue
                 model.dlm_denoise_step(seqs, conf, pred, ws)
                 if count_experts:
                     hit = torch.zeros(L, cfg.n_experts, device="cuda")
@@ -358,6 +373,25 @@ def main():
         "denoise_step_kernels_ms": {k: round(v[0] / max(1, steps_full), 4) for k, v in
                                     sorted(per_kernel.items(), key=lambda kv: -kv[1][0])},
     }
+    if not args.no_graphs:
+        # the same requests with the step loop replayed from per-step HIP graphs
+        # (captured in an untimed request; see CanvasSteps)
+        log(f"graph replay: capture, then {args.steps} timed requests")
+        one_request([], graphs=True)
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        g_steps = 0
+        for _ in range(args.steps):
+            g_steps += one_request([], graphs=True)
+        torch.cuda.synchronize()
+        g1 = time.perf_counter()
+        g_denoise = sum(ev[4 * ci].elapsed_time(ev[4 * ci + 1]) for ci in range(run.n_canvases))
+        out["graph_replay"] = {
+            "value": tokens / (g1 - g0), "unit": "tokens/s",
+            "ms_per_step": 1e3 * (g1 - g0) / args.steps,
+            "ms_per_denoise_step": g_denoise / max(1, g_steps // args.steps),
+            "note": "step loop (denoise + commit) replayed from per-step HIP graphs; prefill and append direct",
+        }
     if experts_used is not None:
         out["experts_used_per_layer_step"] = {
             "mean": experts_used, "of": cfg.n_experts,

@@ -558,9 +558,12 @@ static int splits_for(const GemmDesc& d) {
     }
     // a SwiGLU split would need its own epilogue kernel (the nonlinearity
     // needs the full sums): never split it
-    // tiles of two k-groups already put 8 waves on a CU: splitting them
-    // measured slower from 160 tiles up (faster at 128)
-    if (C::TWO_B || tiles >= (C::KW > 1 ? 160 : SPLIT_TARGET_WG * 3 / 4) || d.M > 256) return 1;
+    // tiles of two k-groups already put 8 waves on a CU: splitting a plain
+    // store measured slower from 160 tiles up; a residual add still gains
+    // (split partials are plain stores summed by the next kernel, where the
+    // unsplit epilogue reads and rewrites the fp32 stream)
+    const long no_split = (C::KW > 1 && EPI != EPI_ADD_F32) ? 160 : SPLIT_TARGET_WG * 3 / 4;
+    if (C::TWO_B || tiles >= no_split || d.M > 256) return 1;
     int s = (int)((SPLIT_TARGET_WG + tiles - 1) / tiles);
     s = std::min(s, std::max(1, nkt / 4));
     s = std::min(s, 2);

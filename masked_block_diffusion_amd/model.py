@@ -286,6 +286,36 @@ class DLM:
             pass
 
 
+class CanvasSteps:
+    """The denoising steps of a canvas as HIP graphs, one per step: step s is
+    dlm_denoise_step then dlm_commit(step=s) over `seqs` with the given
+    outputs, rule and workspace, captured on torch's capture stream and
+    replayed with `replay(s)`.  A graph repeats its launches exactly: the
+    requests' T, cache and canvas pointers, the workspace and the outputs are
+    fixed at capture, so the graphs serve every canvas that starts with the
+    same T in the same buffers (the canvas contents and the cache values may
+    differ).  Capturing runs nothing."""
+
+    def __init__(self, model: "DLM", seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor, rule: "Rule",
+                 ws: torch.Tensor, n_committed: Optional[torch.Tensor] = None,
+                 n_masked: Optional[torch.Tensor] = None):
+        self.T = [s.T for s in seqs]
+        self.graphs = []
+        self._keep = (seqs, conf, pred, rule, ws, n_committed, n_masked)
+        for step in range(rule.n_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                model.dlm_denoise_step(seqs, conf, pred, ws)
+                model.dlm_commit(seqs, conf, pred, rule, step, n_committed, n_masked)
+            self.graphs.append(g)
+
+    def valid_for(self, seqs: Sequence[Seq]) -> bool:
+        return [s.T for s in seqs] == self.T
+
+    def replay(self, step: int) -> None:
+        self.graphs[step].replay()
+
+
 class Rule:
     """A commit rule (top-k schedule or confidence threshold) in ABI form."""
 
@@ -310,26 +340,41 @@ class Rule:
 
 
 def generate(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], rule: Rule,
-             n_canvases: int, ws: torch.Tensor, on_step=None):
+             n_canvases: int, ws: torch.Tensor, on_step=None, graphs: Optional[dict] = None):
     """Prefill each request, then for each canvas: reset to [MASK], denoise and
     commit until the schedule ends (for the threshold rule, until nothing is
     masked in any request), append.  Returns the finished canvases
-    [n_canvases][n_seqs, C] (device int32) and the steps run per canvas."""
+    [n_canvases][n_seqs, C] (device int32) and the steps run per canvas.
+
+    `graphs`: a dict (kept by the caller across calls) turns the step loop into
+    replays of per-step HIP graphs, captured on first use for each canvas
+    index (see CanvasSteps); None runs every step as direct calls."""
     n = len(seqs)
     C = model.C
     for s, ids in zip(seqs, prefixes):
         model.dlm_prefill(s, ids, ws)
-    conf = torch.empty(n * C, dtype=torch.float32, device=model.device)
-    pred = torch.empty(n * C, dtype=torch.int32, device=model.device)
-    n_masked = torch.empty(n, dtype=torch.int32, device=model.device)
+    conf = graphs.setdefault("conf", torch.empty(n * C, dtype=torch.float32, device=model.device)) \
+        if graphs is not None else torch.empty(n * C, dtype=torch.float32, device=model.device)
+    pred = graphs.setdefault("pred", torch.empty(n * C, dtype=torch.int32, device=model.device)) \
+        if graphs is not None else torch.empty(n * C, dtype=torch.int32, device=model.device)
+    n_masked = graphs.setdefault("n_masked", torch.empty(n, dtype=torch.int32, device=model.device)) \
+        if graphs is not None else torch.empty(n, dtype=torch.int32, device=model.device)
     outs, steps = [], []
     for ci in range(n_canvases):
         for s in seqs:
             s.canvas.fill_(model.cfg.mask_id)
+        cg = None
+        if graphs is not None:
+            cg = graphs.get(ci)
+            if cg is None or not cg.valid_for(seqs):
+                cg = graphs[ci] = CanvasSteps(model, seqs, conf, pred, rule, ws, None, n_masked)
         st = 0
         for st in range(rule.n_steps):
-            model.dlm_denoise_step(seqs, conf, pred, ws)
-            model.dlm_commit(seqs, conf, pred, rule, st, None, n_masked)
+            if cg is not None:
+                cg.replay(st)
+            else:
+                model.dlm_denoise_step(seqs, conf, pred, ws)
+                model.dlm_commit(seqs, conf, pred, rule, st, None, n_masked)
             if on_step is not None:
                 on_step(ci, st, conf, pred)
             if rule.kind == "threshold" and int(n_masked.cpu().max()) == 0:
