@@ -164,6 +164,17 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// Wait until at most p stages (of LPW loads each) are still outstanding.
+template <int LPW, int P>
+__device__ __forceinline__ void wait_stages(int p) {
+    if constexpr (P <= 0) {
+        wait_vm<0>();
+    } else {
+        if (p >= P) wait_vm<P * LPW>();
+        else wait_stages<LPW, P - 1>(p);
+    }
+}
+
 // Workgroup barrier for the LDS ring.  __syncthreads() would add a release
 // fence that drains every outstanding LDS-DMA load (all stages in flight);
 // here each wave has already waited for the stage it needs, so

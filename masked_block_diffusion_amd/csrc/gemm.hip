@@ -36,17 +36,6 @@ enum Epi { EPI_F32 = 0, EPI_BF16, EPI_ADD_F32, EPI_SWIGLU_BF16, EPI_SWIGLU_F32, 
 
 constexpr int BKB = 128;             // K bytes per stage row
 
-// Wait until at most p stages (of LPW loads each) are still outstanding.
-template <int LPW, int P>
-__device__ __forceinline__ void wait_stages(int p) {
-    if constexpr (P <= 0) {
-        wait_vm<0>();
-    } else {
-        if (p >= P) wait_vm<P * LPW>();
-        else wait_stages<LPW, P - 1>(p);
-    }
-}
-
 // KW_ k-groups: 4 * KW_ waves share the tile and the LDS ring; k-group g
 // computes k-steps g, g + KW, ... of every stage, and the groups' accumulators
 // are added through LDS before the epilogue.  Two k-groups put two waves on
@@ -480,10 +469,20 @@ struct GroupedArgs {
 template <class C, typename T, int EPI>
 __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+    // Only the first mtiles = tile_start[E] m-tiles exist (the grid is sized
+    // for the most there can be).  The mtiles * nt_n live tiles are dealt to the 8 XCDs
+    // (blockIdx % 8) in equal contiguous ranges, so each XCD streams the same
+    // share of expert weights; inside a range the m-tiles of one weight tile
+    // are adjacent and share that XCD's L2.
     const int nt_n = (a.N + C::BN - 1) / C::BN;
-    const int lin = xcd_remap(blockIdx.x, a.max_mtiles * nt_n);
-    const int nt = lin / a.max_mtiles, mt = lin % a.max_mtiles;
-    if (mt >= a.tile_start[a.E]) return;
+    const int mtiles = a.tile_start[a.E];
+    const int live = mtiles * nt_n;
+    const int per = (live + 7) / 8;
+    const int slot = blockIdx.x / 8;
+    if (slot >= per) return;
+    const int lin = (blockIdx.x % 8) * per + slot;
+    if (lin >= live) return;
+    const int nt = lin / mtiles, mt = lin % mtiles;
     // expert owning m-tile mt: last e with tile_start[e] <= mt
     int lo = 0, hi = a.E - 1;
     while (lo < hi) {
@@ -624,7 +623,8 @@ static void launch_grouped(const GemmDesc& d, hipStream_t st) {
     a.offs = d.offs; a.tile_start = d.tile_start; a.E = d.E; a.N = d.N; a.K = d.K;
     a.max_mtiles = (d.M + C::BM - 1) / C::BM + d.E;
     a.e = make_epi(d, C::BN);
-    const int grid = a.max_mtiles * ((d.N + C::BN - 1) / C::BN);
+    // a multiple of 8 covers the 8 equal XCD ranges of any live tile count
+    const int grid = (a.max_mtiles * ((d.N + C::BN - 1) / C::BN) + 7) / 8 * 8;
     if (d.M == 0 || grid == 0) return;
     launch((gemm_grouped_kernel<C, T, EPI>), dim3(grid), dim3(C::THREADS), 0, st, a);
 }
