@@ -37,7 +37,7 @@ constexpr int MAX_SEQS = 64;
 
 // m-tile rows of the grouped (per-expert) GEMMs; the routing scan computes
 // each expert's first m-tile for this tile height.
-constexpr int GROUPED_BM = 32;
+constexpr int GROUPED_BM = 64;
 
 // C[M, N] (op)= A[M, K] * B[N, K]^T.  Leading dimensions in elements.
 struct GemmDesc {
