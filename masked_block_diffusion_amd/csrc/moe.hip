@@ -160,37 +160,42 @@ void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, 
 
 // ---------------------------------------------------------------- combine --
 
-// One workgroup per token row; each thread owns 4 consecutive columns (d is a
-// multiple of 4): x += shared-expert output (split partials summed in order,
-// fp8 scales applied) + sum over the row's k slots of w * y[slot's sorted row].
+// One workgroup per (token row, 1024-column chunk); each thread owns 4
+// consecutive columns (d is a multiple of 4) and issues all of its loads
+// before the arithmetic: x += shared-expert output (split partials summed in
+// order, fp8 scales applied) + sum over the row's k slots of w * y[slot's
+// sorted row].
+constexpr int COMBINE_COLS = 1024;
 __global__ __launch_bounds__(256) void moe_combine_kernel(float* x, Partials shared, const float* y,
                                                            const int* inv, const float* w, int k, int d) {
     const long r = blockIdx.x;
+    const int c = blockIdx.y * COMBINE_COLS + 4 * threadIdx.x;
+    if (c >= d) return;
     const float* wr = w + r * k;
     const int* ir = inv + r * k;
-    for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (shared.p) {
-            const long off = r * d + c;
-            for (int s = 0; s < shared.splits; ++s) acc += *(const f32x4*)(shared.p + s * shared.stride + off);
-            if (shared.a_scale) acc = acc * shared.a_scale[r] * *(const f32x4*)(shared.b_scale + c);
-        }
-        f32x4 yv[16];
+    f32x4 yv[16];
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
-            if (s < k) yv[s] = *(const f32x4*)(y + (long)ir[s] * d + c);
-#pragma unroll
-        for (int s = 0; s < 16; ++s)
-            if (s < k) acc += wr[s] * yv[s];
-        f32x4* xp = (f32x4*)(x + r * d + c);
-        *xp = *xp + acc;
+    for (int s = 0; s < 16; ++s)
+        if (s < k) yv[s] = *(const f32x4*)(y + (long)ir[s] * d + c);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (shared.p) {
+        const long off = r * d + c;
+        for (int s = 0; s < shared.splits; ++s) acc += *(const f32x4*)(shared.p + s * shared.stride + off);
+        if (shared.a_scale) acc = acc * shared.a_scale[r] * *(const f32x4*)(shared.b_scale + c);
     }
+    f32x4* xp = (f32x4*)(x + r * d + c);
+    const f32x4 x0 = *xp;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        if (s < k) acc += wr[s] * yv[s];
+    *xp = x0 + acc;
 }
 
 void moe_combine(float* x, const Partials& shared, const float* y, const int* inv, const float* w, int rows, int k,
                  int d, hipStream_t st) {
     if (rows <= 0) return;
-    launch(moe_combine_kernel, dim3(rows), dim3(256), 0, st, x, shared, y, inv, w, k, d);
+    launch(moe_combine_kernel, dim3(rows, (d + COMBINE_COLS - 1) / COMBINE_COLS), dim3(256), 0, st, x, shared, y, inv, w, k,
+           d);
 }
 
 }  // namespace dlm
