@@ -219,6 +219,85 @@ def cpu_baseline(run, weights, prefix_cpu, steps_per_canvas: float, sample_layer
     }
 
 
+def ar_sweep(args):
+    """Committed tokens/s of autoregressive decoding (a block size of one: one
+    row per request and pass, one token per pass) and of block diffusion (the
+    workload's canvas and schedule), for each request count R, on the same
+    model, weights and kernels.  Prefills are excluded on both sides; each
+    side is timed after an untimed warmup (8 AR tokens; one canvas)."""
+    import torch
+
+    import synth
+    from masked_block_diffusion_amd import DLM, Rule, ar_decode, generate  # noqa: F401
+
+    def log(msg):
+        print(f"[ar-sweep] {msg}", file=sys.stderr, flush=True)
+
+    run = synth.get_run(args.workload)
+    cfg, C, P = run.model, run.canvas, run.max_prefix
+    big = cfg.n_params()["total"] > 4e9
+    weights = synth.make_weights(cfg, seed=run.seed, device="cuda" if big else "cpu")
+    weights = weights if big else {k: v.cuda() for k, v in weights.items()}
+    ar_model = DLM(cfg, weights, canvas=1)
+    df_model = DLM(cfg, weights, canvas=C)
+    rule = Rule.topk(C, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
+    N = args.ar_tokens
+    rows = []
+    for R in [int(x) for x in args.ar_requests.split(",")]:
+        prompts = [synth.prefix_ids(run, r, P).cuda() for r in range(R)]
+        # AR: prefill P - 1 tokens, 8 untimed tokens, then N timed
+        cap = P + 8 + N
+        seqs = [ar_model.new_seq(cap) for _ in range(R)]
+        ws = ar_model.workspace(max(R, P), cap)
+        for s, ids in zip(seqs, prompts):
+            ar_model.dlm_prefill(s, ids[:-1], ws)
+        warm = ar_decode(ar_model, seqs, prompts, 8, ws, prefilled=True)
+        last = [warm[r, -1:] for r in range(R)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ar_decode(ar_model, seqs, last, N, ws, prefilled=True)
+        torch.cuda.synchronize()
+        t_ar = time.perf_counter() - t0
+        del seqs, ws
+        # block diffusion: prefill P, one untimed canvas, one timed canvas (steps + commits + append)
+        cap = P + 2 * C
+        seqs = [df_model.new_seq(cap) for _ in range(R)]
+        ws = df_model.workspace(max(R * C, P), cap)
+        conf = torch.empty(R * C, dtype=torch.float32, device="cuda")
+        pred = torch.empty(R * C, dtype=torch.int32, device="cuda")
+        n_masked = torch.empty(R, dtype=torch.int32, device="cuda")
+        for s, ids in zip(seqs, prompts):
+            df_model.dlm_prefill(s, ids, ws)
+
+        def canvas():
+            for s in seqs:
+                s.canvas.fill_(cfg.mask_id)
+            for st in range(rule.n_steps):
+                df_model.dlm_denoise_step(seqs, conf, pred, ws)
+                df_model.dlm_commit(seqs, conf, pred, rule, st, None, n_masked)
+                if rule.kind == "threshold" and int(n_masked.cpu().max()) == 0:
+                    break
+            df_model.dlm_append_canvas(seqs, ws)
+        canvas()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        canvas()
+        torch.cuda.synchronize()
+        t_df = time.perf_counter() - t0
+        del seqs, ws
+        torch.cuda.empty_cache()
+        row = {"requests": R, "ar_tokens_per_s": R * N / t_ar, "ar_ms_per_pass": 1e3 * t_ar / N,
+               "diffusion_tokens_per_s": R * C / t_df, "diffusion_ms_per_canvas": 1e3 * t_df}
+        row["diffusion_over_ar"] = row["diffusion_tokens_per_s"] / row["ar_tokens_per_s"]
+        log(json.dumps({k: round(v, 3) if isinstance(v, float) else v for k, v in row.items()}))
+        rows.append(row)
+    cross = next((r["requests"] for r in rows if r["diffusion_over_ar"] < 1.0), None)
+    print(json.dumps({"metric": "committed tokens/s, AR decoding vs block diffusion", "unit": "tokens/s",
+                      "n_gpus": 1, "workload": _workload_text(run), "ar_tokens_timed": N,
+                      "data": "synthetic (seeded random-init weights and uniform random prompt ids)",
+                      "dtype": cfg.dtype, "sweep": rows, "first_requests_where_ar_wins": cross}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +312,12 @@ def main():
     ap.add_argument("--no-graphs", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="with --profile: one canvas of this many denoising steps per request")
+    ap.add_argument("--ar-sweep", action="store_true",
+                    help="autoregressive decoding (one-row canvas, one token per pass) against block "
+                         "diffusion over request counts --ar-requests, on the same weights and kernels; "
+                         "prints its own JSON line")
+    ap.add_argument("--ar-requests", default="1,2,4,8,16,32,64")
+    ap.add_argument("--ar-tokens", type=int, default=64, help="tokens per request timed in AR mode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only a plain 256 MiB device copy, four times (the reference kernel that scales the "
                          "HBM byte counters)")
@@ -246,6 +331,8 @@ def main():
         torch.cuda.synchronize()
         print("copied 4 x 256 MiB", flush=True)
         return
+    if args.ar_sweep:
+        return ar_sweep(args)
     if args.profile:
         args.no_cpu_baseline = True
         args.no_graphs = True

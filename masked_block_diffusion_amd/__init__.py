@@ -7,4 +7,4 @@ wraps the calls over torch tensors.  There is no fallback path: when the
 library is missing the binding raises.
 """
 from .abi import DLMError, load_library  # noqa: F401
-from .model import DLM, CanvasSteps, KVPool, Rule, Seq, generate  # noqa: F401
+from .model import DLM, CanvasSteps, KVPool, Rule, Seq, ar_decode, generate  # noqa: F401

