@@ -67,12 +67,14 @@ void embed(const IdSource& ids, int rows, const void* table, int dtype, int d, i
 // (d <= 4 * 64 * MAXC).  x += residual partials (if any), then
 // h = x / sqrt(mean(x^2) + eps) * g.
 
-constexpr int MAXC = 16;
+constexpr int RN_T = 256;    // threads per row (4 waves)
+constexpr int MAXC = 4;       // float4 per thread: d <= 4 * RN_T * MAXC
 
-__global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, const float* g, int rows, int d,
+__global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, const float* g, int rows, int d,
                                                         float eps, float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
-    const int lane = threadIdx.x;
-    const int r = blockIdx.x;          // one single-wave workgroup per row: every row on its own CU slot
+    __shared__ float red[RN_T / WAVE];
+    const int lane = threadIdx.x;      // thread of the row (4 waves per row)
+    const int r = blockIdx.x;
     if (r >= rows) return;
     const int nc = d / 4;
     const bool out = hf || hb;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
     // every load of the row (x, pending partials, gains) is issued before the first use
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
-        const int c = lane + WAVE * k;
+        const int c = lane + RN_T * k;
         if (c < nc) {
             v[k] = *(const f32x4*)(xr + 4 * c);
             if (out) gg[k] = *(const f32x4*)(g + 4 * c);
@@ -99,12 +101,12 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
             f32x4 t[MAXC];
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
-                const int c = lane + WAVE * k;
+                const int c = lane + RN_T * k;
                 if (c < nc) t[k] = *(const f32x4*)(pr + 4 * c);
             }
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
-                const int c = lane + WAVE * k;
+                const int c = lane + RN_T * k;
                 if (c < nc) acc[k] += t[k];
             }
         }
@@ -112,32 +114,37 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
             const float sa = res.a_scale[r];
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
-                const int c = lane + WAVE * k;
+                const int c = lane + RN_T * k;
                 if (c < nc) acc[k] = acc[k] * sa * *(const f32x4*)(res.b_scale + 4 * c);
             }
         }
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
-            const int c = lane + WAVE * k;
+            const int c = lane + RN_T * k;
             if (c < nc) v[k] += acc[k];
         }
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) {
-            const int c = lane + WAVE * k;
+            const int c = lane + RN_T * k;
             if (c < nc) *(f32x4*)(xr + 4 * c) = v[k];
         }
     }
     if (!out) return;                              // residual update only
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
-        const int c = lane + WAVE * k;
+        const int c = lane + RN_T * k;
         if (c < nc) ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
     }
-    const float den = sqrtf(wave_sum(ss) / (float)d + eps);
+    // row sums across the four waves, added in wave order
+    ss = wave_sum(ss);
+    if (lane % WAVE == 0) red[lane / WAVE] = ss;
+    __syncthreads();
+    ss = (red[0] + red[1]) + (red[2] + red[3]);
+    const float den = sqrtf(ss / (float)d + eps);
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
-        const int c = lane + WAVE * k;
+        const int c = lane + RN_T * k;
         if (c < nc) {
             f32x4 h;
 #pragma unroll
@@ -158,10 +165,14 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
     }
     if (!hq) return;
     amax = wave_max(amax);
+    __syncthreads();                   // every wave has read red[] above
+    if (lane % WAVE == 0) red[lane / WAVE] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
-        const int c = lane + WAVE * k;
+        const int c = lane + RN_T * k;
         if (c < nc) {
             uint32_t packed = 0;
 #pragma unroll
@@ -175,10 +186,10 @@ __global__ __launch_bounds__(WAVE) void rmsnorm_kernel(float* x, Partials res, c
 void rmsnorm(float* x, const Partials& res, const float* g, int rows, int d, float eps, float* hf, uint16_t* hb,
              uint8_t* hq, float* hs, hipStream_t st) {
     if (rows <= 0) return;
-    launch(rmsnorm_kernel, dim3(rows), dim3(WAVE), 0, st, x, res, g, rows, d, eps, hf, hb, hq, hs);
+    launch(rmsnorm_kernel, dim3(rows), dim3(RN_T), 0, st, x, res, g, rows, d, eps, hf, hb, hq, hs);
 }
 
-int rmsnorm_max_dim() { return 4 * WAVE * MAXC; }
+int rmsnorm_max_dim() { return 4 * RN_T * MAXC; }
 
 // ------------------------------------------------------------- quant_rows --
 
