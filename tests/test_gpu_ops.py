@@ -49,11 +49,17 @@ def _bf16_rows():
     return np.array(out, dtype=np.uint16)
 
 
-def test_quant_rows_exhaustive_bf16():
+@pytest.mark.parametrize("pad8", [False, True], ids=["odd-width", "width-multiple-of-8"])
+def test_quant_rows_exhaustive_bf16(pad8):
+    """Both quantiser paths: rows of odd width (element loop) and rows padded
+    with zeros to a multiple of 8 (16-byte chunks kept in registers); zero
+    padding changes no row maximum and quantises to code 0."""
     import ctypes
     from masked_block_diffusion_amd import abi
     lib = abi.load_library()
     bits = _bf16_rows()
+    if pad8:
+        bits = np.pad(bits, ((0, 0), (0, (-bits.shape[1]) % 8)))
     rows, d = bits.shape
     x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
     q = torch.empty((rows, d), dtype=torch.uint8, device="cuda")
