@@ -240,7 +240,7 @@ def ar_sweep(args):
     weights = weights if big else {k: v.cuda() for k, v in weights.items()}
     ar_model = DLM(cfg, weights, canvas=1)
     df_model = DLM(cfg, weights, canvas=C)
-    rule = Rule.topk(C, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
+    rule = Rule.for_run(run)
     N = args.ar_tokens
     rows = []
     for R in [int(x) for x in args.ar_requests.split(",")]:
@@ -373,7 +373,7 @@ def main():
         seqs = [model.new_seq(cap) for _ in range(R)]
     ws = model.workspace(max(R * C, run.max_prefix), cap)
     prefixes = [p.cuda() for p in prefixes_cpu]
-    rule = Rule.topk(C, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
+    rule = Rule.for_run(run)
     conf = torch.empty(R * C, dtype=torch.float32, device="cuda")
     pred = torch.empty(R * C, dtype=torch.int32, device="cuda")
     n_masked = torch.empty(R, dtype=torch.int32, device="cuda")

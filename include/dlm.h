@@ -185,13 +185,21 @@ typedef struct {
  *   DLM_COMMIT_THRESHOLD: commit every masked position with confidence >=
  *     threshold; if there is none, the single most confident one; at step
  *     n_steps - 1, every masked position.
- * k_per_step: HOST array of n_steps entries (TOPK only). */
+ * k_per_step: HOST array of n_steps entries (TOPK only).
+ * edit_threshold: token editing (T2T; What changes, the LLaDA2.1 item: the
+ *   model may revise tokens it already wrote; the pages give no rule, this is
+ *   its plainest form).  When > 0, every position that held a token before the
+ *   step, whose prediction differs from it and whose confidence is >=
+ *   edit_threshold, is rewritten with the prediction.  0 turns editing off
+ *   (mask -> token only).  Edits never touch or write mask_id, so the masked
+ *   counts follow the commit rule alone. */
 typedef enum { DLM_COMMIT_TOPK = 0, DLM_COMMIT_THRESHOLD = 1 } dlm_commit_kind;
 typedef struct {
     int32_t        kind;
     int32_t        n_steps;
     const int32_t* k_per_step;
     float          threshold;
+    float          edit_threshold;
 } dlm_commit_rule;
 
 typedef struct dlm_model dlm_model;
@@ -229,12 +237,15 @@ dlm_status dlm_denoise_step(dlm_model* model, dlm_seq* const* seqs, int32_t n_se
                             void* ws, size_t ws_bytes, void* stream);
 
 /* Applies the commit rule at step `step` (0-based) to each request's canvas,
- * in place: only positions that hold mask_id are written, always with their
- * prediction (never with mask_id).  Ranking: higher confidence first, equal
- * confidence -> lower position first.
- *   n_committed [n_seqs] int32 (device, out, nullable): positions written;
+ * in place: positions that hold mask_id are written per the rule (and, with
+ * rule->edit_threshold > 0, earlier tokens per the editing rule), always with
+ * their prediction (never with mask_id).  Ranking: higher confidence first,
+ * equal confidence -> lower position first.
+ *   n_committed [n_seqs] int32 (device, out, nullable): positions written
+ *               (commits plus edits);
  *   n_masked    [n_seqs] int32 (device, out, nullable): positions still masked.
- * E_ARG if step is outside [0, rule->n_steps). */
+ * E_ARG if step is outside [0, rule->n_steps) or edit_threshold is negative or
+ * not finite. */
 dlm_status dlm_commit(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
                       const float* conf, const int32_t* pred, const dlm_commit_rule* rule,
                       int32_t step, int32_t* n_committed, int32_t* n_masked, void* stream);

@@ -98,7 +98,7 @@ class dlm_seq(ctypes.Structure):
 class dlm_commit_rule(ctypes.Structure):
     _fields_ = [
         ("kind", c_int32), ("n_steps", c_int32), ("k_per_step", POINTER(c_int32)),
-        ("threshold", c_float),
+        ("threshold", c_float), ("edit_threshold", c_float),
     ]
 
 

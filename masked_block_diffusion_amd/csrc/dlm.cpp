@@ -657,6 +657,8 @@ dlm_status dlm_commit(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, const 
     } else {
         return fail(DLM_E_ARG, "unknown commit rule %d", rule->kind);
     }
+    if (!(rule->edit_threshold >= 0.f) || !std::isfinite(rule->edit_threshold))
+        return fail(DLM_E_ARG, "edit_threshold must be finite and >= 0");
     int32_t* canv[DLM_MAX_SEQS];
     for (int i = 0; i < n_seqs; ++i) {
         if (!seqs[i] || !seqs[i]->canvas) return fail(DLM_E_ARG, "seq %d: canvas is NULL", i);
@@ -665,7 +667,7 @@ dlm_status dlm_commit(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, const 
     {
         Timed t(m, DLM_K_COMMIT, (hipStream_t)stream);
         commit(canv, n_seqs, m->cfg.canvas, conf, pred, m->cfg.mask_id, kind, k, rule->threshold, force,
-               n_committed, n_masked, (hipStream_t)stream);
+               rule->edit_threshold, n_committed, n_masked, (hipStream_t)stream);
     }
     return hip_status("dlm_commit");
 }

@@ -180,9 +180,11 @@ void lm_merge(const float* pmax, const float* psum, const int* pidx, int rows, i
 
 // Commit (one workgroup per request).  kind 0: top-k with k; kind 1: threshold
 // (all masked with conf >= thr, at least the most confident one); force_all:
-// every masked position.
+// every masked position.  edit_thr > 0: token editing -- every position that
+// held a token, whose prediction differs and whose conf >= edit_thr, takes its
+// prediction.  n_committed counts commits plus edits.
 void commit(int32_t* const* canvases, int n_seqs, int C, const float* conf, const int* pred,
-            int mask_id, int kind, int k, float thr, bool force_all, int* n_committed,
+            int mask_id, int kind, int k, float thr, bool force_all, float edit_thr, int* n_committed,
             int* n_masked, hipStream_t st);
 
 }  // namespace dlm

@@ -66,7 +66,7 @@ constexpr int CMAX = 1024;
 
 __global__ __launch_bounds__(256) void commit_kernel(CanvasTab tab, int C, const float* conf, const int* pred,
                                                       int mask_id, int kind, int k, float thr, int force_all,
-                                                      int* n_committed, int* n_masked) {
+                                                      float edit_thr, int* n_committed, int* n_masked) {
     __shared__ float sc[CMAX];
     __shared__ int sm[CMAX];
     __shared__ int cnt[2];
@@ -82,7 +82,14 @@ __global__ __launch_bounds__(256) void commit_kernel(CanvasTab tab, int C, const
     __syncthreads();
     int my_commit = 0, my_left = 0;
     for (int j = threadIdx.x; j < C; j += 256) {
-        if (!sm[j]) continue;
+        if (!sm[j]) {
+            // token editing: an earlier token whose prediction moved with enough confidence
+            if (edit_thr > 0.f && pr[j] != canvas[j] && sc[j] >= edit_thr) {
+                canvas[j] = pr[j];
+                ++my_commit;
+            }
+            continue;
+        }
         const float cj = sc[j];
         int rank = 0;
         for (int i = 0; i < C; ++i)
@@ -108,12 +115,12 @@ __global__ __launch_bounds__(256) void commit_kernel(CanvasTab tab, int C, const
 }
 
 void commit(int32_t* const* canvases, int n_seqs, int C, const float* conf, const int* pred, int mask_id, int kind,
-            int k, float thr, bool force_all, int* n_committed, int* n_masked, hipStream_t st) {
+            int k, float thr, bool force_all, float edit_thr, int* n_committed, int* n_masked, hipStream_t st) {
     if (n_seqs <= 0) return;
     CanvasTab tab;
     for (int i = 0; i < n_seqs; ++i) tab.c[i] = canvases[i];
     launch(commit_kernel, dim3(n_seqs), dim3(256), 0, st, tab, C, conf, pred, mask_id, kind, k, thr,
-                       (int)force_all, n_committed, n_masked);
+                       (int)force_all, edit_thr, n_committed, n_masked);
 }
 
 }  // namespace dlm

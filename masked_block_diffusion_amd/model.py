@@ -317,26 +317,37 @@ class CanvasSteps:
 
 
 class Rule:
-    """A commit rule (top-k schedule or confidence threshold) in ABI form."""
+    """A commit rule (top-k schedule or confidence threshold) in ABI form;
+    edit_threshold > 0 adds token editing (earlier tokens whose prediction
+    moved with confidence >= edit_threshold take the prediction)."""
 
     def __init__(self, kind: str, n_steps: int, k_per_step: Optional[Sequence[int]] = None,
-                 threshold: float = 0.5):
+                 threshold: float = 0.5, edit_threshold: float = 0.0):
         self.kind, self.n_steps = kind, n_steps
+        self.edit_threshold = edit_threshold
         self._k = (ctypes.c_int32 * n_steps)(*(k_per_step or [0] * n_steps))
         self.raw = abi.dlm_commit_rule(
             kind=abi.DLM_COMMIT_TOPK if kind == "topk" else abi.DLM_COMMIT_THRESHOLD,
             n_steps=n_steps, k_per_step=ctypes.cast(self._k, ctypes.POINTER(ctypes.c_int32)),
-            threshold=threshold)
+            threshold=threshold, edit_threshold=edit_threshold)
 
     @staticmethod
-    def topk(canvas: int, n_steps: int) -> "Rule":
+    def topk(canvas: int, n_steps: int, edit_threshold: float = 0.0) -> "Rule":
         """Commit C // S per step, one more on the first C % S steps."""
         base, extra = divmod(canvas, n_steps)
-        return Rule("topk", n_steps, [base + (1 if s < extra else 0) for s in range(n_steps)])
+        return Rule("topk", n_steps, [base + (1 if s < extra else 0) for s in range(n_steps)],
+                    edit_threshold=edit_threshold)
 
     @staticmethod
-    def threshold(n_steps: int, thr: float) -> "Rule":
-        return Rule("threshold", n_steps, None, thr)
+    def threshold(n_steps: int, thr: float, edit_threshold: float = 0.0) -> "Rule":
+        return Rule("threshold", n_steps, None, thr, edit_threshold)
+
+    @staticmethod
+    def for_run(run) -> "Rule":
+        """The rule of a workload definition (its schedule, threshold and edit threshold)."""
+        if run.rule == "topk":
+            return Rule.topk(run.canvas, run.n_steps, run.edit_threshold)
+        return Rule.threshold(run.n_steps, run.threshold, run.edit_threshold)
 
 
 def generate(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], rule: Rule,

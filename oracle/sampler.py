@@ -14,10 +14,21 @@
     every masked position whose confidence reaches the threshold, at least the
     single most confident one, and every remaining position at the last step.
   * Ties in confidence rank go to the lower position.
+  * Token editing (T2T; "Diffusion LLMs: what changes...", the LLaDA2.1 item:
+    besides mask -> token commits the model may revise tokens it already
+    wrote).  The pages give no rule; the plainest reading, used here: with an
+    edit threshold tau > 0, every position that held a token before the step
+    whose prediction differs from that token and whose confidence is at least
+    tau is rewritten with the prediction, from the same forward pass as the
+    step's commits.  Edits touch no [MASK] position and write no [MASK], so
+    the masked count follows the commit rule exactly; tau = 0 turns editing
+    off (mask -> token only, never reverted).
 
 Pins: hand-built confidence vectors with known answers, and the invariants
 (mask -> token only, counts per step equal the schedule, counts sum to C, no
-[MASK] after the last step) in tests/test_oracle_sampler.py.
+[MASK] after the last step; with editing: the masked counts are those of the
+commit rule alone, edits only rewrite earlier tokens with their prediction at
+confidence >= tau) in tests/test_oracle_sampler.py.
 """
 from __future__ import annotations
 
@@ -69,13 +80,31 @@ def commit_threshold(canvas: np.ndarray, conf: np.ndarray, pred: np.ndarray, mas
     return out, np.sort(chosen)
 
 
+def edit_tokens(before: np.ndarray, conf: np.ndarray, pred: np.ndarray, mask_id: int,
+                tau: float) -> np.ndarray:
+    """Positions edited at this step: held a token before it, the prediction
+    differs from that token, confidence >= tau (tau > 0; none for tau = 0)."""
+    if not tau > 0.0:
+        return np.zeros(0, dtype=np.int64)
+    held = before != mask_id
+    return np.nonzero(held & (pred != before) & (conf >= tau))[0].astype(np.int64)
+
+
 def commit(canvas, conf, pred, mask_id, run, step):
+    """The step's commits, plus token edits when the run has an edit
+    threshold.  Returns (new canvas, committed positions)."""
     if run.rule == "topk":
         k = topk_schedule(run.canvas, run.n_steps)[step]
-        return commit_topk(canvas, conf, pred, mask_id, k)
-    if run.rule == "threshold":
-        return commit_threshold(canvas, conf, pred, mask_id, run.threshold, step, run.n_steps)
-    raise ValueError(run.rule)
+        out, chosen = commit_topk(canvas, conf, pred, mask_id, k)
+    elif run.rule == "threshold":
+        out, chosen = commit_threshold(canvas, conf, pred, mask_id, run.threshold, step, run.n_steps)
+    else:
+        raise ValueError(run.rule)
+    edited = edit_tokens(canvas, conf, pred, mask_id, getattr(run, "edit_threshold", 0.0))
+    if len(edited):
+        out = out.copy()
+        out[edited] = pred[edited]
+    return out, chosen
 
 
 def generate(model, run, prefix_ids, capacity=None, on_step=None):

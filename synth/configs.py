@@ -85,6 +85,7 @@ class RunConfig:
     threshold: float = 0.5
     page_size: int = 64               # KV page size in tokens (paged layout)
     seed: int = 0
+    edit_threshold: float = 0.0       # token editing (T2T): > 0 rewrites earlier tokens (0: off)
 
     @property
     def max_prefix(self) -> int:
@@ -165,6 +166,16 @@ RUNS = {
     "moe-mini-batch": RunConfig("moe-mini-batch", MOE_BF16_MINI, canvas=64, n_requests=4,
                                 prefix_len=(20, 150), n_canvases=1, rule="topk",
                                 n_steps=12),
+    # token editing on the tiny model: the threshold sits inside the spread of its
+    # confidences (~1/V), so some earlier tokens are rewritten and some are not
+    "tiny-t2t": RunConfig("tiny-t2t", TINY_DENSE_F32, canvas=32, n_requests=1,
+                          prefix_len=(64, 64), n_canvases=2, rule="topk", n_steps=8,
+                          edit_threshold=0.0040),
+    # the dense model with editing on wherever the prediction moved (timing of the
+    # edit pass; random-init confidences are ~1/V)
+    "dense-t2t": RunConfig("dense-t2t", DENSE_BF16, canvas=256, n_requests=1,
+                           prefix_len=(1024, 1024), n_canvases=1, rule="topk", n_steps=16,
+                           edit_threshold=1e-6),
 }
 
 

@@ -103,17 +103,36 @@ def compare_logits(gpu: np.ndarray, oracle: np.ndarray, mask_id: int, dtype: str
 def compare_commit(before: np.ndarray, gpu_after: np.ndarray, oracle_after: np.ndarray,
                    oracle_conf: np.ndarray, oracle_logits: np.ndarray, mask_id: int,
                    rule: str, k: int, threshold: float, forced: bool, rep: StepReport,
-                   exempt_rows: Set[int] = frozenset(), logit_err: float = 0.0) -> None:
+                   exempt_rows: Set[int] = frozenset(), logit_err: float = 0.0,
+                   edit_threshold: float = 0.0) -> None:
     """One request's canvas before and after the commit, on both sides.
-    logit_err: the step's measured max |gpu - oracle| logit difference."""
+    logit_err: the step's measured max |gpu - oracle| logit difference.
+    edit_threshold > 0: token editing is on, and the earlier tokens are
+    compared like the commits (the edit decision is exempt where the oracle's
+    confidence is within the margin of the threshold or its argmax is a
+    near-tie)."""
     rank_m = max(MARGIN, 4.0 * logit_err)
     thr_m = max(MARGIN, 2.0 * logit_err)
     tok_m = max(MARGIN, 2.0 * logit_err)
     rep.rank_margin = max(rep.rank_margin, rank_m)
     masked = before == mask_id
-    # positions that were not masked never change
-    if np.any(gpu_after[~masked] != before[~masked]):
-        rep.problems.append("commit changed a non-masked position")
+    if not edit_threshold > 0.0:
+        # positions that were not masked never change
+        if np.any(gpu_after[~masked] != before[~masked]):
+            rep.problems.append("commit changed a non-masked position")
+    else:
+        held = ~masked
+        lc_e = np.log(np.maximum(oracle_conf, 1e-300))
+        amb = held & ((np.abs(lc_e - np.log(edit_threshold)) <= thr_m) | (top2_margin(oracle_logits) <= tok_m))
+        for r in exempt_rows:
+            amb[r] = True
+        g_ed = held & (gpu_after != before)
+        o_ed = held & (oracle_after != before)
+        if np.any((g_ed != o_ed) & ~amb):
+            rep.problems.append(f"edit sets differ at decisive positions {np.nonzero((g_ed != o_ed) & ~amb)[0][:10].tolist()}")
+        if np.any(g_ed & o_ed & ~amb & (gpu_after != oracle_after)):
+            rep.problems.append("edited tokens differ")
+        rep.exempt_tokens += int((amb & (g_ed | o_ed)).sum())
     g_set = masked & (gpu_after != mask_id)
     o_set = masked & (oracle_after != mask_id)
     lc = np.log(np.maximum(oracle_conf, 1e-300))

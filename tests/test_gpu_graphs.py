@@ -25,7 +25,7 @@ def _setup(name, paged=False):
     seqs = [gm.new_seq(cap, pool) for _ in range(run.n_requests)]
     prefixes = [p.cuda() for p in synth.make_inputs(run)]
     ws = gm.workspace(max(run.n_requests * run.canvas, max(len(p) for p in prefixes)), cap)
-    rule = Rule.topk(run.canvas, run.n_steps) if run.rule == "topk" else Rule.threshold(run.n_steps, run.threshold)
+    rule = Rule.for_run(run)
     return run, gm, seqs, prefixes, ws, rule
 
 

@@ -14,7 +14,7 @@ from tests.lockstep import lockstep
 pytestmark = pytest.mark.gpu
 
 RUNS = ["tiny", "dense-mini", "dense-mini-ragged", "moe-mini", "dense-mini-fp8", "moe-mini-fp8",
-        "moe-mini-batch"]
+        "moe-mini-batch", "tiny-t2t"]
 
 
 @pytest.mark.parametrize("name", RUNS)

@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from oracle.model import OracleModel, OracleWeights
-from oracle.sampler import (commit_threshold, commit_topk, generate, rank_masked,
+from oracle.sampler import (commit, commit_threshold, commit_topk, edit_tokens, generate, rank_masked,
                             topk_schedule)
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")))
@@ -107,3 +107,53 @@ def test_pages_figures_pin_tokens_per_pass():
     assert topk_schedule(256, GOLDEN["steps_budget"]["avg_steps"]) == [22] * 4 + [21] * 8
     cp = GOLDEN["compute_per_token"]
     assert abs(cp["diffusion_gflop_per_token"] / cp["ar_gflop_per_token"] - cp["ratio"]) < 0.1
+
+
+def test_edit_tokens_hand_built():
+    """Token editing: only positions that held a token, only where the
+    prediction differs, only at confidence >= tau (inclusive); tau = 0 is off."""
+    before = np.array([5, M, 6, 7, 8, M])
+    pred = np.array([9, 1, 6, 3, 4, 2])
+    conf = np.array([0.9, 0.99, 0.95, 0.2, 0.8, 0.1])
+    assert edit_tokens(before, conf, pred, M, 0.8).tolist() == [0, 4]   # 2: same token; 3: 0.2 < 0.8
+    assert edit_tokens(before, conf, pred, M, 0.85).tolist() == [0]
+    assert edit_tokens(before, conf, pred, M, 0.0).tolist() == []
+    run = synth.configs.RunConfig("e", None, canvas=6, n_requests=1, prefix_len=(1, 1), n_canvases=1,
+                                  rule="topk", n_steps=2, edit_threshold=0.8)
+    out, chosen = commit(before, conf, pred, M, run, 0)
+    # commits: the 3 most confident masked positions of 2 (both); edits: 0 and 4
+    assert sorted(chosen.tolist()) == [1, 5]
+    assert out.tolist() == [9, 1, 6, 7, 4, 2]
+
+
+@pytest.mark.parametrize("rule,steps", [("topk", 8), ("threshold", 6)])
+def test_editing_invariants(rule, steps):
+    """With editing on, the masked counts per step are those of the commit rule
+    alone (edits neither fill nor create [MASK]), every change to an earlier
+    token is its prediction at confidence >= tau, and the schedule still ends
+    with no [MASK]; tau above every confidence reduces to mask -> token only."""
+    run, om = _tiny_run(rule, steps)
+    tau = 0.021                                   # inside the tiny model's confidence spread
+    run_e = replace(run, edit_threshold=tau)
+    prefix = np.arange(9) % 40
+    seen = {"edits": 0}
+
+    def check(ci, s, before, conf, pred, after):
+        held = before != run.model.mask_id
+        changed = before != after
+        # the commit rule alone decides every masked position
+        ref, _ = commit(before, conf, pred, run.model.mask_id, run, s)
+        assert np.array_equal(after[~held], ref[~held])
+        assert not np.any(after == run.model.mask_id) or np.sum(after == run.model.mask_id) == np.sum(ref == run.model.mask_id)
+        ed = changed & held
+        assert np.all(after[ed] == pred[ed]) and np.all(conf[ed] >= tau)
+        keep = held & (pred != before) & (conf < tau)
+        assert np.all(after[keep] == before[keep])
+        seen["edits"] += int(ed.sum())
+
+    outs, _, _ = generate(om, run_e, prefix, on_step=check)
+    assert all(not np.any(c == run.model.mask_id) for c in outs)
+    assert seen["edits"] > 0, "the threshold should let some edits through"
+    outs_hi, _, _ = generate(om, replace(run, edit_threshold=2.0), prefix)
+    outs_off, _, _ = generate(om, run, prefix)
+    assert all(np.array_equal(a, b) for a, b in zip(outs_hi, outs_off))
