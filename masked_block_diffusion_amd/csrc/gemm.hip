@@ -525,7 +525,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2 x 2 k-groups, 6 stages
 //     (SwiGLU pair: 128 x 64 x 2 weights, 2 k-groups, if N >= 4096, else 64 x 32 x 2)
 //   prefill M                                           128 x 128, waves 2x2, 4 stages
-//   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128, waves 4x1
+//   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128 (two k-groups), waves 4x1
 //   grouped (experts)                                   SwiGLU pair GROUPED_BM x 64 x 2, else GROUPED_BM x 128;
 //                                                       waves 2x2, 3 stages
 // The canvas choices come from a sweep of every variant and split factor on
@@ -539,7 +539,7 @@ template <typename T, bool DUAL>
 using CoreW = std::conditional_t<DUAL, Core<T, 128, 64, 2, 2, true, 4>, Core<T, 256, 64, 4, 1, false, 3>>;
 template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4>;
 template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
-template <typename T> using CoreHw = Core<T, 256, 128, 4, 1, false, 3>;
+template <typename T> using CoreHw = Core<T, 256, 128, 4, 1, false, 3, 2>;
 // Expert tiles: 64 rows (about what one expert gets from a 256-row canvas at
 // top-8 of 128) and 3 stages, from a sweep over routings that touch 32 to 69
 // experts; wider weight tiles for the narrow-K down projection.
