@@ -40,10 +40,15 @@
  *     caches, canvases, outputs, workspace).  Pointers marked "device" must be
  *     device memory of the current HIP device; "host" pointers are read before
  *     the call returns.  The library never frees caller memory.  It owns only
- *     its host handle and one 4-byte device error word per model.
+ *     its host handle, one 4-byte device error word per model and, for MoE
+ *     models, one HIP stream (default priority) with two events.
  *   - Streams: all GPU work is enqueued on `stream` (a hipStream_t; NULL is the
- *     null stream).  No entry point synchronises except dlm_check_device_status
- *     and dlm_timing_read.  One model handle serves one stream at a time.
+ *     null stream) -- for MoE models each layer's shared expert runs on the
+ *     model's own stream, forked from `stream` by an event and joined back into
+ *     it before its result is used, so all work still starts after earlier work
+ *     on `stream` and finishes before later work on it.  No entry point
+ *     synchronises except dlm_check_device_status and dlm_timing_read.  One
+ *     model handle serves one stream at a time.
  *   - Errors: arguments are validated on the host before anything is enqueued;
  *     on failure the call returns a negative dlm_status, enqueues nothing and
  *     changes no state, and dlm_last_error() describes the failure.  Faults only
@@ -111,10 +116,13 @@ typedef struct {
     float   rope_base;
 } dlm_config;
 
-/* Per-layer weights, all device pointers, row-major [out, in] (a GEMM computes
+/* Per-layer weights, all device pointers.  Shapes are [out, in] (a GEMM computes
  * y = x W^T).  Element type: fp32 for DLM_F32, bf16 for DLM_BF16, OCP E4M3FN
  * codes (uint8) for DLM_FP8 projections.  "_s" pointers are the fp8 per-output-
  * channel fp32 scales (W = code * s[out]); NULL for other dtypes.
+ * Layout: the projections (wqkv, wo, w_gate, w_up, w_down, we_gate, we_up,
+ * we_down and lm_head) are in the tiled layout dlm_pack_weight writes from the
+ * row-major matrix (per expert for we_*); w_router and embed are row-major.
  *   wqkv   [(Hq + 2 Hkv) * dh, d]  rows: Q heads, then K heads, then V heads
  *   wo     [d, Hq * dh]
  *   w_gate, w_up [F, d]; w_down [d, F]     F = d_ffn (dense FFN or shared expert)
@@ -144,6 +152,24 @@ typedef struct {
     const void*  lm_head;  const float* lm_head_s;
     const dlm_layer_weights* layers;
 } dlm_weights;
+
+/* Tiled weight layout.  Layout only -- the values are the row-major projection
+ * matrices of the transformer described above, rearranged so that a GEMM's
+ * K stage over 16 consecutive output rows is one contiguous 2 KB run (weights
+ * stream from HBM in whole DRAM pages rather than one 128-byte line per row).
+ * For a [N, K] matrix of eb-byte elements (eb = 4, 2, 1 for DLM_F32, DLM_BF16,
+ * DLM_FP8), nkt = K * eb / 128: the 128 bytes of row n holding k-bytes
+ * [128 kt, 128 kt + 128) sit at byte ((n / 16) * nkt + kt) * 2048 + (n % 16) * 128.
+ * N is padded to a multiple of 16 with zero rows; `batch` matrices (the experts
+ * of a layer) follow one another.
+ * dlm_packed_weight_bytes: bytes of the packed output (0 on invalid arguments).
+ * dlm_pack_weight: src device [batch, N, K] row-major, dst device (caller-
+ * allocated, dlm_packed_weight_bytes long, not overlapping src); enqueued on
+ * `stream`.  E_DTYPE for an unknown dtype, E_ARG for null or overlapping
+ * pointers or batch / N / K < 1, E_SHAPE unless K * eb is a multiple of 128. */
+size_t dlm_packed_weight_bytes(int32_t dtype, int32_t batch, int32_t N, int32_t K);
+dlm_status dlm_pack_weight(int32_t dtype, int32_t batch, int32_t N, int32_t K, const void* src, void* dst,
+                           void* stream);
 
 /* One request.  Host struct of non-owning device pointers.
  *   kv: KV cache, bf16 (fp32 for DLM_F32 models).
@@ -284,12 +310,15 @@ dlm_status dlm_op_quant_rows(const void* x, int32_t rows, int32_t d, void* q, fl
  * b2_scale[n] for B2 -- device fp32 arrays, required for DLM_FP8 only).
  *   swiglu = 0: C fp32 [M, N].
  *   swiglu = 1: C = silu(A B^T) * (A B2^T), bf16 (fp32 for DLM_F32) [M, N].
- * variant: tile shape, 0 = the one the model would pick, 1..8 forced (bf16
- * only); splits: split-K factor, 0 = the model's choice.  ws / ws_bytes: room
+ * variant: tile shape, 0 = the one the model would pick, 1..12 forced (bf16
+ * only), optionally or-ed with DLM_GEMM_B_TILED: B (and B2) are then in the
+ * tiled weight layout of dlm_pack_weight; splits: split-K factor, 0 = the
+ * model's choice.  ws / ws_bytes: room
  * for split-K partials (see dlm_op_gemm_workspace).  ms (host, nullable): when
  * set, the GEMM kernel is timed with events in its dispatch, the call
  * synchronises and writes the kernel's duration.  E_SHAPE unless K * element
- * size is a multiple of 128 bytes; E_ARG for a variant outside 0..8. */
+ * size is a multiple of 128 bytes; E_ARG for a variant outside 0..12. */
+#define DLM_GEMM_B_TILED 0x100
 dlm_status dlm_op_gemm(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
                        const void* B2, const float* a_scale, const float* b_scale, const float* b2_scale, void* C,
                        void* ws, size_t ws_bytes, int32_t variant, int32_t splits, float* ms, void* stream);

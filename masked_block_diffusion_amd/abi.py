@@ -52,8 +52,9 @@ EXPORTS = [
     "dlm_create", "dlm_destroy", "dlm_workspace_bytes", "dlm_prefill", "dlm_denoise_step",
     "dlm_commit", "dlm_append_canvas", "dlm_check_device_status", "dlm_last_error",
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
-    "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace",
+    "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace", "dlm_packed_weight_bytes", "dlm_pack_weight",
 ]
+DLM_GEMM_B_TILED = 0x100
 
 
 class dlm_config(ctypes.Structure):
@@ -133,6 +134,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_op_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, P, P, P, P, P, P, P, P,
                                   c_size_t, c_int32, c_int32, POINTER(c_float), P]),
         "dlm_op_gemm_workspace": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
+        "dlm_packed_weight_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+        "dlm_pack_weight": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

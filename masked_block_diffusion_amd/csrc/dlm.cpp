@@ -55,6 +55,11 @@ struct dlm_model {
     std::vector<dlm_layer_weights> layers;
     int* d_err = nullptr;
     int device = 0;
+    // MoE models: the shared expert runs on a second stream of the library's
+    // own (default priority), forked from and joined back into the caller's
+    // stream with these events, so it overlaps the routing chain
+    hipStream_t side = nullptr;
+    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     int32_t* dbg_router = nullptr;   // test hook: per-layer router choices
     float* dbg_router_logits = nullptr;
     int64_t dbg_cap = 0;             // (layer, row) pairs the hook buffers hold
@@ -116,7 +121,7 @@ struct Timed {
 
 struct Plan {
     size_t x, hA, hb, hq, hs, qkv, q, ao, aoq, aos, fi, fiq, fis, rl, tid, tw, offs, tstart, sorted, inv,
-        hist, lrank, ei, eiq, eis, y, pmax, psum, pidx, opart, mlpart, splitk, total;
+        hist, lrank, ei, eiq, eis, y, pmax, psum, pidx, opart, mlpart, splitk, splitk2, total;
     long splitk_floats;
 };
 
@@ -192,6 +197,7 @@ Plan plan(const dlm_config& c, int rows, int max_kv) {
     p.mlpart = take(af / (c.head_dim + 2) * 2 * 4);
     p.splitk_floats = splitk_need(c, rows);
     p.splitk = take(std::max(1L, p.splitk_floats) * 4);
+    p.splitk2 = moe ? take(std::max(1L, p.splitk_floats) * 4) : p.splitk;   // the shared expert's own
     p.total = off;
     return p;
 }
@@ -351,15 +357,20 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
         pending = Partials();
     };
     auto opA = [&](const void* bf, const void* q8) { return fp8 ? q8 : bf; };
-    auto dense = [&](int id, GemmDesc g, bool consumed = false) {
-        g.splitk = at<float>(ws, p.splitk);
+    // a GEMM on stream s with split-K partials in region `part`
+    auto dense_on = [&](hipStream_t s, size_t part, int id, GemmDesc g, bool consumed) {
+        g.splitk = at<float>(ws, part);
         g.splitk_floats = p.splitk_floats;
-        return run_gemm(m, id, g, st, consumed);
+        return run_gemm(m, id, g, s, consumed);
+    };
+    auto dense = [&](int id, GemmDesc g, bool consumed = false) { return dense_on(st, p.splitk, id, g, consumed); };
+    auto quant_on = [&](hipStream_t s, const void* src, int rows, int cols, uint8_t* qd8, float* sc) {
+        if (!fp8) return;
+        Timed t(m, DLM_K_QUANT, s);
+        quant_rows((const uint16_t*)src, rows, cols, qd8, sc, s);
     };
     auto quant = [&](const void* src, int rows, int cols, uint8_t* qd8, float* sc) {
-        if (!fp8) return;
-        Timed t(m, DLM_K_QUANT, st);
-        quant_rows((const uint16_t*)src, rows, cols, qd8, sc, st);
+        quant_on(st, src, rows, cols, qd8, sc);
     };
 
     for (int l = 0; l < c.n_layers; ++l) {
@@ -370,7 +381,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             GemmDesc g;
             g.dtype = gdt; g.epi = GEMM_STORE_F32;
             g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
-            g.B = L.wqkv; g.ldb = d; g.b_scale = L.wqkv_s;
+            g.B = L.wqkv; g.ldb = d; g.b_tiled = true; g.b_scale = L.wqkv_s;
             g.M = R; g.N = nqkv; g.K = d;
             g.C = qkv; g.ldc = nqkv;
             qkv_res = dense(DLM_K_GEMM_QKV, g, true);
@@ -398,24 +409,46 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             g.dtype = gdt; g.epi = GEMM_ADD_F32;
             g.A = opA(ao, fp8 ? at<uint8_t>(ws, p.aoq) : nullptr); g.lda = qd;
             g.a_scale = fp8 ? at<float>(ws, p.aos) : nullptr;
-            g.B = L.wo; g.ldb = qd; g.b_scale = L.wo_s;
+            g.B = L.wo; g.ldb = qd; g.b_tiled = true; g.b_scale = L.wo_s;
             g.M = R; g.N = d; g.K = qd;
             g.C = x; g.ldc = d;
             pending = dense(DLM_K_GEMM_O, g, true);
         }
         norm(L.ffn_norm);
-        // dense SwiGLU FFN, or the MoE's shared expert
-        {
+        // dense SwiGLU FFN (the gate/up half), or the MoE's shared expert
+        auto ffn_gate_up = [&](hipStream_t s, size_t part) {
             GemmDesc g;
             g.dtype = gdt; g.epi = GEMM_SWIGLU; g.out_f32 = f32;
             g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
-            g.B = L.w_gate; g.B2 = L.w_up; g.ldb = d; g.b_scale = L.w_gate_s; g.b2_scale = L.w_up_s;
+            g.B = L.w_gate; g.B2 = L.w_up; g.ldb = d; g.b_tiled = true;
+            g.b_scale = L.w_gate_s; g.b2_scale = L.w_up_s;
             g.M = R; g.N = c.d_ffn; g.K = d; g.C = fi; g.ldc = c.d_ffn;
-            dense(DLM_K_GEMM_GATE_UP, g);
-        }
-        quant(fi, R, c.d_ffn, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr, fp8 ? at<float>(ws, p.fis) : nullptr);
+            dense_on(s, part, DLM_K_GEMM_GATE_UP, g, false);
+            quant_on(s, fi, R, c.d_ffn, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr, fp8 ? at<float>(ws, p.fis) : nullptr);
+        };
+        // ... and its down half: x += result, or (consumed) split partials for the next reader
+        auto ffn_down = [&](hipStream_t s, size_t part) {
+            GemmDesc g;
+            g.dtype = gdt; g.epi = GEMM_ADD_F32;
+            g.A = opA(fi, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr); g.lda = c.d_ffn;
+            g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
+            g.B = L.w_down; g.ldb = c.d_ffn; g.b_tiled = true; g.b_scale = L.w_down_s;
+            g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
+            return dense_on(s, part, DLM_K_GEMM_DOWN, g, true);
+        };
         if (c.ffn == DLM_FFN_MOE) {
-            // routing reads hA, which the shared expert left untouched
+            // The shared expert goes to the side stream: it reads hA (or its
+            // codes) and writes only fi (codes), its own split-K region and, if
+            // unsplit, x -- which the main stream leaves alone until the join.
+            // The routing chain reads hA too and writes only its own buffers.
+            // (A failing event call leaves its error for hipGetLastError,
+            // which the entry point reads after the forward.)
+            Partials shared;
+            (void)hipEventRecord(m->fork_ev, st);
+            (void)hipStreamWaitEvent(m->side, m->fork_ev, 0);
+            ffn_gate_up(m->side, p.splitk2);
+            shared = ffn_down(m->side, p.splitk2);
+            (void)hipEventRecord(m->join_ev, m->side);
             const int E = c.n_experts, k = c.top_k, De = c.d_expert, A = R * k;
             float* rl = at<float>(ws, p.rl);
             int* tid = at<int>(ws, p.tid);
@@ -447,7 +480,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                 g.dtype = gdt; g.epi = GEMM_SWIGLU; g.out_f32 = f32;
                 g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
                 g.gather = sorted; g.gather_div = k;
-                g.B = L.we_gate; g.B2 = L.we_up; g.ldb = d; g.b_stride = (long)De * d;
+                g.B = L.we_gate; g.B2 = L.we_up; g.ldb = d; g.b_stride = packed_rows(De) * d; g.b_tiled = true;
                 g.b_scale = L.we_gate_s; g.b2_scale = L.we_up_s; g.bs_stride = De;
                 g.offs = offs; g.tile_start = tstart; g.E = E;
                 g.M = A; g.N = De; g.K = d; g.C = ei; g.ldc = De;
@@ -461,35 +494,21 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                 g.dtype = gdt; g.epi = GEMM_STORE_F32;
                 g.A = opA(ei, fp8 ? at<uint8_t>(ws, p.eiq) : nullptr); g.lda = De;
                 g.a_scale = fp8 ? at<float>(ws, p.eis) : nullptr;
-                g.B = L.we_down; g.ldb = De; g.b_stride = (long)d * De;
+                g.B = L.we_down; g.ldb = De; g.b_stride = packed_rows(d) * De; g.b_tiled = true;
                 g.b_scale = L.we_down_s; g.bs_stride = d;
                 g.offs = offs; g.tile_start = tstart; g.E = E;
                 g.M = A; g.N = d; g.K = De; g.C = y; g.ldc = d;
                 Timed t(m, DLM_K_EXPERT_DOWN, st);
                 gemm_grouped(g, st);
             }
-            Partials shared;
-            {
-                GemmDesc g;
-                g.dtype = gdt; g.epi = GEMM_ADD_F32;
-                g.A = opA(fi, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr); g.lda = c.d_ffn;
-                g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
-                g.B = L.w_down; g.ldb = c.d_ffn; g.b_scale = L.w_down_s;
-                g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
-                shared = dense(DLM_K_GEMM_DOWN, g, true);
-            }
+            (void)hipStreamWaitEvent(st, m->join_ev, 0);
             {
                 Timed t(m, DLM_K_COMBINE, st);
                 moe_combine(x, shared, y, inv, tw, R, k, d, st);
             }
         } else {
-            GemmDesc g;
-            g.dtype = gdt; g.epi = GEMM_ADD_F32;
-            g.A = opA(fi, fp8 ? at<uint8_t>(ws, p.fiq) : nullptr); g.lda = c.d_ffn;
-            g.a_scale = fp8 ? at<float>(ws, p.fis) : nullptr;
-            g.B = L.w_down; g.ldb = c.d_ffn; g.b_scale = L.w_down_s;
-            g.M = R; g.N = d; g.K = c.d_ffn; g.C = x; g.ldc = d;
-            pending = dense(DLM_K_GEMM_DOWN, g, true);
+            ffn_gate_up(st, p.splitk);
+            pending = ffn_down(st, p.splitk);
         }
     }
     if (mode != DENOISE) return;
@@ -503,7 +522,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
         GemmDesc g;
         g.dtype = gdt; g.epi = GEMM_LMHEAD;
         g.A = opA(hA, hq); g.lda = d; g.a_scale = hs;
-        g.B = m->w.lm_head; g.ldb = d; g.b_scale = m->w.lm_head_s;
+        g.B = m->w.lm_head; g.ldb = d; g.b_tiled = true; g.b_scale = m->w.lm_head_s;
         g.M = R; g.N = c.vocab; g.K = d;
         g.pmax = pmax; g.psum = psum; g.pidx = pidx; g.mask_col = c.mask_id;
         g.logits = logits; g.ld_logits = c.vocab;
@@ -565,9 +584,17 @@ dlm_status dlm_create(const dlm_config* cfg, const dlm_weights* weights, dlm_mod
     hipError_t e = hipGetDevice(&m->device);
     if (e == hipSuccess) e = hipMalloc((void**)&m->d_err, sizeof(int));
     if (e == hipSuccess) e = hipMemset(m->d_err, 0, sizeof(int));
+    if (e == hipSuccess && cfg->ffn == DLM_FFN_MOE) {
+        e = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->fork_ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->join_ev, hipEventDisableTiming);
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         if (m->d_err) hipFree(m->d_err);
+        if (m->fork_ev) (void)hipEventDestroy(m->fork_ev);
+        if (m->join_ev) (void)hipEventDestroy(m->join_ev);
+        if (m->side) (void)hipStreamDestroy(m->side);
         delete m;
         return fail(DLM_E_HIP, "dlm_create: %s", hipGetErrorString(e));
     }
@@ -583,6 +610,9 @@ void dlm_destroy(dlm_model* m) {
     }
     for (auto e : m->pool) hipEventDestroy(e);
     if (m->d_err) hipFree(m->d_err);
+    if (m->fork_ev) (void)hipEventDestroy(m->fork_ev);
+    if (m->join_ev) (void)hipEventDestroy(m->join_ev);
+    if (m->side) (void)hipStreamDestroy(m->side);
     delete m;
 }
 
@@ -713,7 +743,8 @@ static GemmDesc op_gemm_desc(int32_t dtype, int32_t swiglu, int32_t M, int32_t N
     g.out_f32 = dtype == DLM_F32;
     g.M = M; g.N = N; g.K = K;
     g.lda = K; g.ldb = K; g.ldc = N;
-    g.variant = variant;
+    g.variant = variant & 0xff;
+    g.b_tiled = (variant & DLM_GEMM_B_TILED) != 0;
     g.force_splits = splits;
     return g;
 }
@@ -722,9 +753,35 @@ static dlm_status op_gemm_check(int32_t dtype, int32_t M, int32_t N, int32_t K, 
     if (dtype != DLM_F32 && dtype != DLM_BF16 && dtype != DLM_FP8) return fail(DLM_E_UNSUPPORTED, "dtype %d", dtype);
     if (M < 1 || N < 1 || K < 1) return fail(DLM_E_ARG, "M, N, K must be >= 1");
     if (((long)K * elem_bytes(dtype)) % 128) return fail(DLM_E_SHAPE, "K * element size not a multiple of 128");
-    if (variant < 0 || variant > gemm_variants()) return fail(DLM_E_ARG, "variant %d", variant);
+    if (variant < 0 || (variant & ~(0xff | DLM_GEMM_B_TILED)) || (variant & 0xff) > gemm_variants())
+        return fail(DLM_E_ARG, "variant %d", variant);
     if (splits < 0) return fail(DLM_E_ARG, "splits %d", splits);
     return DLM_OK;
+}
+
+static dlm_status pack_check(int32_t dtype, int32_t batch, int32_t N, int32_t K) {
+    if (dtype != DLM_F32 && dtype != DLM_BF16 && dtype != DLM_FP8) return fail(DLM_E_DTYPE, "dtype %d", dtype);
+    if (batch < 1 || N < 1 || K < 1) return fail(DLM_E_ARG, "batch / N / K < 1");
+    if (((long)K * elem_bytes(dtype)) % 128) return fail(DLM_E_SHAPE, "K * element size not a multiple of 128");
+    return DLM_OK;
+}
+
+size_t dlm_packed_weight_bytes(int32_t dtype, int32_t batch, int32_t N, int32_t K) {
+    if (pack_check(dtype, batch, N, K)) return 0;
+    return (size_t)packed_weight_bytes(elem_bytes(dtype), batch, N, K);
+}
+
+dlm_status dlm_pack_weight(int32_t dtype, int32_t batch, int32_t N, int32_t K, const void* src, void* dst,
+                           void* stream) {
+    g_err.clear();
+    dlm_status s = pack_check(dtype, batch, N, K);
+    if (s) return s;
+    if (!src || !dst) return fail(DLM_E_ARG, "null pointer");
+    const uintptr_t a0 = (uintptr_t)src, a1 = a0 + (size_t)batch * N * K * elem_bytes(dtype);
+    const uintptr_t b0 = (uintptr_t)dst, b1 = b0 + (size_t)packed_weight_bytes(elem_bytes(dtype), batch, N, K);
+    if (a0 < b1 && b0 < a1) return fail(DLM_E_ARG, "src and dst overlap");
+    pack_weight(elem_bytes(dtype), batch, N, K, src, dst, (hipStream_t)stream);
+    return hip_status("dlm_pack_weight");
 }
 
 size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, int32_t variant,

@@ -66,15 +66,18 @@ struct Core {
     static_assert((NS - 2) * LPW < 64, "vmcnt");
 
     const uint8_t* src[LPW];     // this lane's source (row + swizzled chunk) per load
+    int kstep[LPW];              // bytes from one K stage to the next for that load
     f32x4 acc[TM][TN];
     f32x4 acc2[DUAL ? TM : 1][DUAL ? TN : 1];
     int wave;                    // 0 .. NWAVES - 1
     int pos;                     // wave within the k-group: (wm, wn) = (pos / WN, pos % WN)
     int kg;                      // k-group
 
-    // rowptr(R) -> address of stage row R (A rows, then B, then B2), always a
-    // readable row (rows outside the matrix are clamped by the caller: they
-    // only feed outputs that are not stored).
+    // rowptr(R, step) -> address of stage row R's first K stage (A rows, then
+    // B, then B2) and, in step, the bytes to its next stage; always a readable
+    // row (rows outside the matrix are clamped by the caller: they only feed
+    // outputs that are not stored).  A load instruction covers 8 rows, all of A
+    // or all of one B (BM and BN are multiples of 8), so its step is uniform.
     template <class F>
     __device__ __forceinline__ void init(F rowptr) {
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
@@ -85,7 +88,9 @@ struct Core {
         for (int j = 0; j < LPW; ++j) {
             const int R = (wave * LPW + j) * 8 + lane / 8;
             const int chunk = (lane % 8) ^ (R & 7);
-            src[j] = rowptr(R) + chunk * 16;
+            int step = BKB;
+            src[j] = rowptr(R, step) + chunk * 16;
+            kstep[j] = __builtin_amdgcn_readfirstlane(step);
         }
     }
 
@@ -103,7 +108,7 @@ struct Core {
         uint8_t* dst = smem + slot * STAGE + wave * LPW * 1024;
 #pragma unroll
         for (int j = 0; j < LPW; ++j)
-            __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long)kt * BKB), (lds_ptr)(dst + j * 1024), 16,
+            __builtin_amdgcn_global_load_lds((const void*)(src[j] + (long)kt * kstep[j]), (lds_ptr)(dst + j * 1024), 16,
                                              0, 0);
     }
 
@@ -263,6 +268,23 @@ struct Core {
     }
 };
 
+// Weight rows in the tiled layout: blocks of TILE_ROWS rows x BKB bytes, so a
+// K stage of TILE_ROWS consecutive rows is one contiguous 2 KB run (DRAM pages
+// are read whole instead of one 128-byte line per row); block (g, kt) of a
+// matrix with nkt stages per row starts at byte (g * nkt + kt) * TILE_BYTES.
+constexpr int TILE_ROWS = 16;
+constexpr int TILE_BYTES = TILE_ROWS * BKB;
+
+// Address of weight row r's first K stage and the step to its next stage.
+__device__ __forceinline__ const uint8_t* brow(const uint8_t* B, long ldb, bool tiled, int nkt, int r, int& step) {
+    if (!tiled) {
+        step = BKB;
+        return B + (long)r * ldb;
+    }
+    step = TILE_BYTES;
+    return B + ((long)(r / TILE_ROWS) * nkt) * TILE_BYTES + (r % TILE_ROWS) * BKB;
+}
+
 // Remap a linear workgroup id so each XCD (id % 8) gets a contiguous range.
 __device__ __forceinline__ int xcd_remap(int b, int total) {
     if (total % 8 != 0) return b;
@@ -398,6 +420,7 @@ __device__ __forceinline__ void store_partial(C& c, float* part, float* part2, i
 struct DenseArgs {
     const uint8_t* A; long lda;          // bytes
     const uint8_t* B; const uint8_t* B2; long ldb;
+    int b_tiled;                         // B / B2 in the tiled layout (ldb unused)
     int M, N, K;
     int splits;                          // split-K factor (1 = none)
     float* part;                         // [splits][M][N] (+ the same again for the second weight)
@@ -415,8 +438,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dense_kernel(DenseArgs a) {
     const int split = (lin / mt_n) % a.splits;
     const int nt = lin / mt_n / a.splits;
     const int m0 = mt * C::BM, n0 = nt * C::BN;
+    const int nkt = (int)((long)a.K * sizeof(T) / BKB);
     C c;
-    c.init([&](int R) -> const uint8_t* {
+    c.init([&](int R, int& step) -> const uint8_t* {
         if (R < C::BM) {
             const int r = min(m0 + R, a.M - 1);
             return a.A + (long)r * a.lda;
@@ -424,10 +448,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dense_kernel(DenseArgs a) {
         R -= C::BM;
         const uint8_t* B = a.B;
         if (R >= C::BN) { R -= C::BN; B = a.B2; }
-        const int r = min(n0 + R, a.N - 1);
-        return B + (long)r * a.ldb;
+        return brow(B, a.ldb, a.b_tiled, nkt, min(n0 + R, a.N - 1), step);
     });
-    const int nkt = (int)((long)a.K * sizeof(T) / BKB);
     const int per = (nkt + a.splits - 1) / a.splits;
     c.run(smem, split * per, min(nkt, (split + 1) * per));
     if (!c.reduce(smem)) return;
@@ -459,6 +481,7 @@ struct GroupedArgs {
     const uint8_t* A; long lda;          // bytes
     const int* gather; int gather_div;   // A row of permuted row p = gather[p] / gather_div (nullable)
     const uint8_t* B; const uint8_t* B2; long ldb; long b_stride;   // bytes between experts
+    int b_tiled;
     const float* b_scale; const float* b2_scale; long bs_stride;     // elements between experts
     const int* offs;        // [E + 1] permuted row offsets per expert
     const int* tile_start;  // [E + 1] first m-tile of each expert (for this BM)
@@ -495,8 +518,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
     const int n0 = nt * C::BN;
     const uint8_t* Be = a.B + (long)ex * a.b_stride;
     const uint8_t* B2e = C::TWO_B ? a.B2 + (long)ex * a.b_stride : nullptr;
+    const int nkt = (int)((long)a.K * sizeof(T) / BKB);
     C c;
-    c.init([&](int R) -> const uint8_t* {
+    c.init([&](int R, int& step) -> const uint8_t* {
         if (R < C::BM) {
             const int r = min(m0 + R, mlim - 1);
             const int src = a.gather ? a.gather[r] / a.gather_div : r;
@@ -505,10 +529,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
         R -= C::BM;
         const uint8_t* B = Be;
         if (R >= C::BN) { R -= C::BN; B = B2e; }
-        const int r = min(n0 + R, a.N - 1);
-        return B + (long)r * a.ldb;
+        return brow(B, a.ldb, a.b_tiled, nkt, min(n0 + R, a.N - 1), step);
     });
-    c.run(smem, 0, (int)((long)a.K * sizeof(T) / BKB));
+    c.run(smem, 0, nkt);
     if (!c.reduce(smem)) return;
     EpiArgs e = a.e;
     if constexpr (sizeof(T) == 1) {
@@ -596,6 +619,7 @@ static int launch_dense(const GemmDesc& d, hipStream_t st) {
     DenseArgs a;
     a.A = (const uint8_t*)d.A; a.lda = d.lda * (long)sizeof(T);
     a.B = (const uint8_t*)d.B; a.B2 = (const uint8_t*)d.B2; a.ldb = d.ldb * (long)sizeof(T);
+    a.b_tiled = d.b_tiled ? 1 : 0;
     a.M = d.M; a.N = d.N; a.K = d.K;
     a.splits = splits_for<C, T, EPI>(d);
     if (a.splits > 1 && (!d.splitk || part_floats<C, T, DUAL, EPI>(d) > d.splitk_floats))
@@ -623,6 +647,7 @@ static void launch_grouped(const GemmDesc& d, hipStream_t st) {
     a.A = (const uint8_t*)d.A; a.lda = d.lda * (long)sizeof(T);
     a.gather = d.gather; a.gather_div = d.gather_div;
     a.B = (const uint8_t*)d.B; a.B2 = (const uint8_t*)d.B2; a.ldb = d.ldb * (long)sizeof(T);
+    a.b_tiled = d.b_tiled ? 1 : 0;
     a.b_stride = d.b_stride * (long)sizeof(T);
     a.b_scale = d.b_scale; a.b2_scale = d.b2_scale; a.bs_stride = d.bs_stride;
     a.offs = d.offs; a.tile_start = d.tile_start; a.E = d.E; a.N = d.N; a.K = d.K;
@@ -758,6 +783,39 @@ void gemm_grouped(const GemmDesc& d, hipStream_t st) {
 }
 
 int gemm_variants() { return GEMM_VARIANTS; }
+
+// ------------------------------------------------------- weight packing --
+
+long packed_rows(int N) { return (long)(N + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS; }
+
+long packed_weight_bytes(int eb, int batch, int N, int K) { return (long)batch * packed_rows(N) * K * eb; }
+
+// One thread per 16-byte chunk of the packed output: chunk c of matrix b lies
+// in block (g, kt) at row r of the block; rows past N are zero.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint8_t* src, uint8_t* dst, int N, long row_bytes,
+                                                          int nkt, long chunks_per_matrix, long total) {
+    const long c = (long)blockIdx.x * 256 + threadIdx.x;
+    if (c >= total) return;
+    const long b = c / chunks_per_matrix, i = c % chunks_per_matrix;
+    const long blk = i / (TILE_BYTES / 16);
+    const int in = (int)(i % (TILE_BYTES / 16));
+    const int r = in / (BKB / 16), ch = in % (BKB / 16);
+    const long g = blk / nkt, kt = blk % nkt;
+    const long n = g * TILE_ROWS + r;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (n < N) v = *(const uint4*)(src + (b * N + n) * row_bytes + kt * BKB + ch * 16);
+    *(uint4*)(dst + c * 16) = v;
+}
+
+void pack_weight(int eb, int batch, int N, int K, const void* src, void* dst, hipStream_t st) {
+    const long row_bytes = (long)K * eb;
+    const int nkt = (int)(row_bytes / BKB);
+    const long per = packed_rows(N) * row_bytes / 16;
+    const long total = per * batch;
+    if (total == 0) return;
+    launch(pack_weight_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const uint8_t*)src,
+           (uint8_t*)dst, N, row_bytes, nkt, per, total);
+}
 
 int lm_head_tile_n(int M) { return M <= 64 ? CoreHs<bf16_t>::BN : CoreHw<bf16_t>::BN; }
 

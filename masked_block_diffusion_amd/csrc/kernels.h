@@ -46,6 +46,9 @@ struct GemmDesc {
     bool out_f32 = false;       // SwiGLU output in fp32 (f32 models) instead of bf16
     const void* A = nullptr; long lda = 0;
     const void* B = nullptr; const void* B2 = nullptr; long ldb = 0;
+    // B / B2 in the tiled weight layout (blocks of 16 rows x 128 bytes of K,
+    // see dlm_pack_weight); ldb is then unused
+    bool b_tiled = false;
     const float* a_scale = nullptr;   // fp8: per A row
     const float* b_scale = nullptr;   // fp8: per output column (B row)
     const float* b2_scale = nullptr;
@@ -69,6 +72,15 @@ struct GemmDesc {
     int force_splits = 0;
 };
 int gemm_variants();
+
+// Tiled weight layout (what the model's projection GEMMs read): a [N, K]
+// matrix of eb-byte elements as blocks of 16 rows x 128 bytes of K; block
+// (g, kt) at byte (g * nkt + kt) * 2048 with nkt = K * eb / 128, row n % 16
+// of block g = n / 16 at +128 * (n % 16) inside it.  N is padded to a
+// multiple of 16 (zero rows); a batch of matrices (experts) is consecutive.
+long packed_rows(int N);
+long packed_weight_bytes(int eb, int batch, int N, int K);
+void pack_weight(int eb, int batch, int N, int K, const void* src, void* dst, hipStream_t st);
 
 // Dense and grouped GEMMs.  K * element size must be a multiple of 128 bytes.
 // gemm_main launches the GEMM and returns its split-K factor; when that is

@@ -149,16 +149,32 @@ class DLM:
         self._keep.append(t)
         return t
 
+    def _tiled(self, t: torch.Tensor) -> torch.Tensor:
+        """The library's tiled layout of a row-major [..., N, K] projection
+        (dlm_pack_weight, a kernel on the current stream); the row-major
+        copy is not kept."""
+        t = t.to(self.device).contiguous()
+        N, K = t.shape[-2], t.shape[-1]
+        batch = t.numel() // (N * K)
+        dt = _DTYPES[self.dtype]
+        nbytes = self.lib.dlm_packed_weight_bytes(dt, batch, N, K)
+        if nbytes == 0:
+            raise ValueError(f"cannot pack a {tuple(t.shape)} {self.dtype} weight")
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        check(self.lib.dlm_pack_weight(dt, batch, N, K, _ptr(t), _ptr(dst), _stream()), "dlm_pack_weight")
+        self._keep.append(dst)
+        return dst
+
     def _proj(self, weights, name, cat: Sequence[str] = ()):
-        """(codes-or-values pointer, scale pointer) of a projection; `cat`
-        concatenates several along the output dimension."""
+        """(tiled codes-or-values pointer, scale pointer) of a projection;
+        `cat` concatenates several along the output dimension."""
         names = list(cat) or [name]
         if self.dtype == "fp8":
             q = torch.cat([weights[n + ".q"] for n in names], dim=-2) if len(names) > 1 else weights[name + ".q"]
             s = torch.cat([weights[n + ".s"] for n in names], dim=-1) if len(names) > 1 else weights[name + ".s"]
-            return _ptr(self._dev(q)), _ptr(self._dev(s.float()))
+            return _ptr(self._tiled(q)), _ptr(self._dev(s.float()))
         w = torch.cat([weights[n] for n in names], dim=-2) if len(names) > 1 else weights[name]
-        return _ptr(self._dev(w)), None
+        return _ptr(self._tiled(w)), None
 
     def _pack(self, cfg, weights):
         W = {"embed": _ptr(self._dev(weights["embed"])),

@@ -122,3 +122,19 @@ def test_kernel_names():
     assert all(names) and len(set(names)) == abi.DLM_K_COUNT
     assert lib.dlm_kernel_name(abi.DLM_K_COUNT).decode() == ""
     assert names[abi.DLM_K_LM_HEAD] == "lm_head"
+
+
+def test_pack_weight_validates_on_the_host():
+    """dlm_packed_weight_bytes is host arithmetic (16-row padding); bad
+    dtype / shape / pointers are refused before any HIP call."""
+    lib = _lib()
+    assert lib.dlm_packed_weight_bytes(abi.DLM_BF16, 3, 40, 64) == 3 * 48 * 64 * 2
+    assert lib.dlm_packed_weight_bytes(abi.DLM_FP8, 1, 16, 128) == 16 * 128
+    assert lib.dlm_packed_weight_bytes(abi.DLM_F32, 1, 1, 32) == 16 * 32 * 4
+    assert lib.dlm_packed_weight_bytes(abi.DLM_BF16, 1, 16, 100) == 0        # K * 2 not a multiple of 128
+    assert lib.dlm_packed_weight_bytes(7, 1, 16, 64) == 0
+    assert lib.dlm_packed_weight_bytes(abi.DLM_BF16, 0, 16, 64) == 0
+    assert lib.dlm_pack_weight(abi.DLM_BF16, 1, 16, 64, None, None, None) == abi.DLM_E_ARG
+    assert lib.dlm_pack_weight(abi.DLM_BF16, 1, 16, 100, 0x1000, 0x100000, None) == abi.DLM_E_SHAPE
+    assert lib.dlm_pack_weight(9, 1, 16, 64, 0x1000, 0x100000, None) == abi.DLM_E_DTYPE
+    assert lib.dlm_pack_weight(abi.DLM_BF16, 1, 16, 64, 0x1000, 0x1000 + 100, None) == abi.DLM_E_ARG   # overlap

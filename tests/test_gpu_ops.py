@@ -238,3 +238,75 @@ def test_paged_cache_validation():
     torch.cuda.synchronize()
     assert seq.T == len(ids)
     gm.close()
+
+
+def _pack_reference(w_bytes: np.ndarray) -> np.ndarray:
+    """The tiled layout from its definition in include/dlm.h, on the CPU:
+    w_bytes uint8 [batch, N, K*eb] -> blocks of 16 rows x 128 bytes, block
+    (n // 16, kt) at ((n // 16) * nkt + kt) * 2048, rows padded with zeros."""
+    b, N, rb = w_bytes.shape
+    Np = (N + 15) // 16 * 16
+    pad = np.zeros((b, Np, rb), dtype=np.uint8)
+    pad[:, :N] = w_bytes
+    nkt = rb // 128
+    out = np.zeros(b * Np * rb, dtype=np.uint8)
+    for m in range(b):
+        for n in range(Np):
+            for kt in range(nkt):
+                off = m * Np * rb + ((n // 16) * nkt + kt) * 2048 + (n % 16) * 128
+                out[off:off + 128] = pad[m, n, kt * 128:(kt + 1) * 128]
+    return out
+
+
+@pytest.mark.parametrize("dtype,batch,N,K", [("f32", 1, 40, 64), ("bf16", 3, 64, 128), ("bf16", 2, 37, 320),
+                                             ("fp8", 4, 24, 256), ("fp8", 1, 16, 128)])
+def test_pack_weight_matches_layout_definition(dtype, batch, N, K):
+    """dlm_pack_weight writes exactly the documented byte layout (bit-exact),
+    ragged N padded with zero rows, expert batches one after another."""
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    code = {"f32": abi.DLM_F32, "bf16": abi.DLM_BF16, "fp8": abi.DLM_FP8}[dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+    rng = np.random.default_rng(batch * 100 + N)
+    src = rng.integers(0, 256, size=(batch, N, K * eb), dtype=np.uint8)
+    nbytes = lib.dlm_packed_weight_bytes(code, batch, N, K)
+    assert nbytes == batch * ((N + 15) // 16 * 16) * K * eb
+    s = torch.from_numpy(src.copy()).cuda()
+    d = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    abi.check(lib.dlm_pack_weight(code, batch, N, K, s.data_ptr(), d.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream), "pack")
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), _pack_reference(src))
+    # overlapping buffers are refused before anything is enqueued
+    assert lib.dlm_pack_weight(code, batch, N, K, s.data_ptr(), s.data_ptr(), None) == abi.DLM_E_ARG
+
+
+@pytest.mark.parametrize("variant,splits", [(0, 0), (2, 2), (9, 0), (3, 3), (7, 0)])
+@pytest.mark.parametrize("M,N,K", [(37, 200, 1536), (256, 512, 2048), (5, 72, 256)])
+def test_gemm_tiled_weights_bit_identical(variant, splits, M, N, K):
+    """The GEMM reading tiled weights (the layout the model uses) gives the
+    same bits as reading the row-major matrix: only addresses change."""
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    g = torch.Generator().manual_seed(M + N + K)
+    A, B, B2 = _bf16_tensor((M, K), g).cuda(), _bf16_tensor((N, K), g).cuda(), _bf16_tensor((N, K), g).cuda()
+    st = torch.cuda.current_stream().cuda_stream
+
+    def tiled(w):
+        d = torch.empty(lib.dlm_packed_weight_bytes(abi.DLM_BF16, 1, N, K), dtype=torch.uint8, device="cuda")
+        abi.check(lib.dlm_pack_weight(abi.DLM_BF16, 1, N, K, w.data_ptr(), d.data_ptr(), st), "pack")
+        return d
+    Bt, B2t = tiled(B), tiled(B2)
+    for swiglu in (0, 1):
+        outs = []
+        for flag, (b, b2) in ((0, (B, B2)), (abi.DLM_GEMM_B_TILED, (Bt, B2t))):
+            v = variant | flag
+            nws = lib.dlm_op_gemm_workspace(abi.DLM_BF16, swiglu, M, N, K, v, splits)
+            ws = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+            C = torch.empty((M, N), dtype=torch.float32 if not swiglu else torch.bfloat16, device="cuda")
+            abi.check(lib.dlm_op_gemm(abi.DLM_BF16, swiglu, M, N, K, A.data_ptr(), b.data_ptr(), b2.data_ptr(),
+                                      None, None, None, C.data_ptr(), ws.data_ptr(), ws.numel(), v, splits,
+                                      None, st), "gemm")
+            outs.append(C)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
