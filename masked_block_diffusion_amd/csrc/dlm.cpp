@@ -457,16 +457,18 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             int* tstart = at<int>(ws, p.tstart);
             int* sorted = at<int>(ws, p.sorted);
             int* inv = at<int>(ws, p.inv);
+            Partials router_logits;
             {
                 GemmDesc g;   // router logits: bf16 operands (fp32 for f32 models), fp32 out
                 g.dtype = f32 ? DT_F32 : DT_BF16; g.epi = GEMM_STORE_F32;
                 g.A = hA; g.lda = d; g.B = L.w_router; g.ldb = d;
                 g.M = R; g.N = E; g.K = d; g.C = rl; g.ldc = E;
-                dense(DLM_K_ROUTER, g);
+                router_logits = dense(DLM_K_ROUTER, g, true);   // split partials are summed by the top-k
+                if (!router_logits.p) router_logits.p = rl;
             }
             {
                 Timed t(m, DLM_K_TOPK, st);
-                router_topk(rl, R, E, k, tid, tw, m->dbg_router ? m->dbg_router + (long)l * R * k : nullptr,
+                router_topk(router_logits, R, E, k, tid, tw, m->dbg_router ? m->dbg_router + (long)l * R * k : nullptr,
                             m->dbg_router_logits ? m->dbg_router_logits + (long)l * R * E : nullptr, st);
             }
             {

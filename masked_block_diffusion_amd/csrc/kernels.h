@@ -166,9 +166,10 @@ void attention(const void* q, const SeqTab& seqs, int layer, int n_layers, int h
                int dh, bool causal, bool f32, bool p_two_terms, void* out, const AttnWork& w, hipStream_t st);
 long attention_work_floats(int rows, int hq, int dh);
 
-// Router: logits fp32 [rows, E] -> top-k experts (ties -> lower id), weights =
-// softmax probabilities renormalised over the chosen k.
-void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
+// Router: logits fp32 [rows, E] (the router GEMM's output or its split-K
+// partials, no scales) -> top-k experts (ties -> lower id), weights = softmax
+// probabilities renormalised over the chosen k.
+void router_topk(const Partials& logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
                  float* logits_copy, hipStream_t st);
 
 // Stable counting sort of the rows*k assignments by expert: offs [E + 1],

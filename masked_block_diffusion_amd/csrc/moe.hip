@@ -1,11 +1,18 @@
 // Mixture-of-experts routing for gfx950.
 //
-//  router_topk  one wave per token row: softmax over the E router logits, the
-//               top-k experts by logit (ties -> lower expert id; the same order
-//               as by probability), and their probabilities renormalised over
-//               the chosen k (the full softmax denominator cancels).
+//  router_topk  one wave per token row: the router logits (the router GEMM's
+//               split-K partials summed here, in split order), softmax over
+//               the E of them, the top-k experts by logit (ties -> lower
+//               expert id; the same order as by probability), and their
+//               probabilities renormalised over the chosen k (the full softmax
+//               denominator cancels).
 //  moe_route    stable counting sort of the rows * k assignments by expert, so
-//               each expert's rows are contiguous for the grouped GEMM:
+//               each expert's rows are contiguous for the grouped GEMM.  Up to
+//               ROUTE_FUSED_MAX assignments (a canvas step): one workgroup
+//               does it all -- one assignment per lane, its rank among the
+//               lanes of its wave with the same expert from ballots, counts per
+//               (64-assignment chunk, expert), bases by scans.  Beyond
+//               that (prefill, large batches), three kernels:
 //                 hist     per 256-assignment block: per-expert counts and each
 //                          assignment's rank among earlier same-expert ones;
 //                 scan     per-expert totals -> offsets, per-block bases, and the
@@ -21,7 +28,7 @@ namespace dlm {
 
 constexpr int MAX_E = 256;
 
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, int rows, int E, int k, int* ids,
+__global__ __launch_bounds__(256) void router_topk_kernel(Partials logits, int rows, int E, int k, int* ids,
                                                            float* w, int* ids_copy, float* logits_copy) {
     const int lane = threadIdx.x % WAVE;
     const int r = blockIdx.x * 4 + threadIdx.x / WAVE;
@@ -31,8 +38,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, i
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = lane + WAVE * j;
-        v[j] = e < E ? logits[(long)r * E + e] : -INFINITY;
-        if (logits_copy && e < E) logits_copy[(long)r * E + e] = v[j];
+        v[j] = -INFINITY;
+        if (e < E) {
+            float x = 0.f;
+            for (int s = 0; s < logits.splits; ++s) x += logits.p[s * logits.stride + (long)r * E + e];
+            v[j] = x;
+            if (logits_copy) logits_copy[(long)r * E + e] = x;
+        }
     }
     float m = -INFINITY;
 #pragma unroll
@@ -70,7 +82,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* logits, i
         for (int s = 0; s < k; ++s) w[(long)r * k + s] /= sel_sum;
 }
 
-void router_topk(const float* logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
+void router_topk(const Partials& logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,
                  float* logits_copy, hipStream_t st) {
     if (rows <= 0) return;
     launch(router_topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, logits, rows, E, k, ids, w,
@@ -148,10 +160,112 @@ __global__ __launch_bounds__(RB) void route_scatter_kernel(const int* ids, int n
     inv[a] = p;
 }
 
+constexpr int RF_THREADS = 1024;
+constexpr int RF_WAVES = RF_THREADS / WAVE;
+constexpr int ROUTE_FUSED_MAX = 4096;
+constexpr int RF_CHUNKS = ROUTE_FUSED_MAX / WAVE;   // 64-assignment chunks
+constexpr int RF_PER_WAVE = RF_CHUNKS / RF_WAVES;   // chunks per wave
+
+// Chunk c (assignments 64c .. 64c + 63) goes to wave c % RF_WAVES, one
+// assignment per lane.  Lanes holding the same expert are found with one
+// ballot per bit of the expert id; a lane's rank among them is the popcount of
+// the lower ones, and the lowest records the chunk's count in cnt[c][e].
+// Then per expert an exclusive prefix over chunks, an exclusive scan over
+// experts (one wave, shuffles), and position = offs[e] + cnt[c][e] + rank:
+// the (expert, assignment) order.
+__global__ __launch_bounds__(RF_THREADS) void route_fused_kernel(const int* ids, int n_assign, int E, int bm,
+                                                                 int* offs, int* tile_start, int* sorted_assign,
+                                                                 int* inv) {
+    __shared__ int cnt[RF_CHUNKS * MAX_E];           // [chunk][expert]: counts, then bases within the expert
+    __shared__ int tot[MAX_E + 1], tiles[MAX_E + 1];
+    const int t = threadIdx.x, lane = t % WAVE, w = t / WAVE;
+    const int nchunks = (n_assign + WAVE - 1) / WAVE;
+    for (int i = t; i < nchunks * E; i += RF_THREADS) cnt[i] = 0;
+    __syncthreads();
+    int ex[RF_PER_WAVE], rank[RF_PER_WAVE];
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < RF_PER_WAVE; ++j) {
+        const int c = w + j * RF_WAVES;
+        const int a = c * WAVE + lane;
+        const bool valid = c < nchunks && a < n_assign;
+        const int e = valid ? ids[a] : 0;
+        unsigned long long m = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {            // E <= 256
+            const bool bit = (e >> b) & 1;
+            const unsigned long long bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        ex[j] = e;
+        rank[j] = __popcll(m & below);
+        if (valid && rank[j] == 0) cnt[c * E + e] = __popcll(m);
+    }
+    __syncthreads();
+    if (t < E) {
+        int run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int v = cnt[c * E + t];
+            cnt[c * E + t] = run;
+            run += v;
+        }
+        tot[t] = run;
+    }
+    __syncthreads();
+    if (w == 0) {
+        // exclusive scans of the totals and of their m-tile counts; lane l
+        // holds experts 4l .. 4l + 3
+        int n[4], tl[4], sn = 0, st = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            n[i] = e < E ? tot[e] : 0;
+            tl[i] = (n[i] + bm - 1) / bm;
+            sn += n[i];
+            st += tl[i];
+        }
+        int in = sn, it = st;                      // inclusive scan over lanes
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const int pn = __shfl_up(in, o, WAVE), pt = __shfl_up(it, o, WAVE);
+            if (lane >= o) { in += pn; it += pt; }
+        }
+        int on = in - sn, ot = it - st;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (e < E) { tot[e] = on; tiles[e] = ot; }
+            on += n[i];
+            ot += tl[i];
+        }
+        if (lane == WAVE - 1) { tot[E] = in; tiles[E] = it; }   // the grand totals
+    }
+    __syncthreads();
+    if (t <= E) {
+        offs[t] = tot[t];
+        tile_start[t] = tiles[t];
+    }
+#pragma unroll
+    for (int j = 0; j < RF_PER_WAVE; ++j) {
+        const int c = w + j * RF_WAVES;
+        const int a = c * WAVE + lane;
+        if (c < nchunks && a < n_assign) {
+            const int pos = tot[ex[j]] + cnt[c * E + ex[j]] + rank[j];
+            sorted_assign[pos] = a;
+            inv[a] = pos;
+        }
+    }
+}
+
 void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, int* sorted_assign, int* inv,
                const RouteWork& w, hipStream_t st) {
     const int nb = route_blocks(n_assign);
     if (nb == 0) return;
+    if (n_assign <= ROUTE_FUSED_MAX && E <= MAX_E) {
+        launch(route_fused_kernel, dim3(1), dim3(RF_THREADS), 0, st, ids, n_assign, E, GROUPED_BM, offs, tile_start,
+               sorted_assign, inv);
+        return;
+    }
     launch(route_hist_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank);
     launch(route_scan_kernel, dim3(1), dim3(256), 0, st, w.hist, nb, E, GROUPED_BM, offs, tile_start);
     launch(route_scatter_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank,
