@@ -35,9 +35,9 @@ enum GemmEpi { GEMM_STORE_F32 = 0, GEMM_STORE_BF16, GEMM_ADD_F32, GEMM_SWIGLU, G
 
 constexpr int MAX_SEQS = 64;
 
-// m-tile rows of the grouped (per-expert) GEMMs; the routing scan computes
-// each expert's first m-tile for this tile height.
-constexpr int GROUPED_BM = 64;
+// m-tile rows of the grouped (per-expert) GEMMs for operand type `dtype`; the
+// routing scan computes each expert's first m-tile for this tile height.
+int grouped_bm(int dtype);
 
 // C[M, N] (op)= A[M, K] * B[N, K]^T.  Leading dimensions in elements.
 struct GemmDesc {
@@ -173,10 +173,10 @@ void router_topk(const Partials& logits, int rows, int E, int k, int* ids, float
                  float* logits_copy, hipStream_t st);
 
 // Stable counting sort of the rows*k assignments by expert: offs [E + 1],
-// tile_start [E + 1] (GROUPED_BM-row tiles), sorted_assign [A] (assignment
+// tile_start [E + 1] (bm-row tiles, bm = grouped_bm), sorted_assign [A] (assignment
 // index a = row * k + slot, ordered by (expert, a)), inv [A] (position of a).
 struct RouteWork { int* hist; int* local_rank; };   // hist [blocks * E], local_rank [A]
-void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, int* sorted_assign,
+void moe_route(const int* ids, int n_assign, int E, int bm, int* offs, int* tile_start, int* sorted_assign,
                int* inv, const RouteWork& w, hipStream_t st);
 int route_blocks(int n_assign);
 

@@ -16,7 +16,7 @@
 //                 hist     per 256-assignment block: per-expert counts and each
 //                          assignment's rank among earlier same-expert ones;
 //                 scan     per-expert totals -> offsets, per-block bases, and the
-//                          first m-tile of every expert (GROUPED_BM-row tiles);
+//                          first m-tile of every expert (bm-row tiles);
 //                 scatter  sorted position of every assignment and its inverse.
 //               Integer-only and deterministic: order is (expert, row, slot).
 //  moe_combine  x[r] += sum over slots s (in selection order) of
@@ -257,17 +257,17 @@ __global__ __launch_bounds__(RF_THREADS) void route_fused_kernel(const int* ids,
     }
 }
 
-void moe_route(const int* ids, int n_assign, int E, int* offs, int* tile_start, int* sorted_assign, int* inv,
+void moe_route(const int* ids, int n_assign, int E, int bm, int* offs, int* tile_start, int* sorted_assign, int* inv,
                const RouteWork& w, hipStream_t st) {
     const int nb = route_blocks(n_assign);
     if (nb == 0) return;
     if (n_assign <= ROUTE_FUSED_MAX && E <= MAX_E) {
-        launch(route_fused_kernel, dim3(1), dim3(RF_THREADS), 0, st, ids, n_assign, E, GROUPED_BM, offs, tile_start,
+        launch(route_fused_kernel, dim3(1), dim3(RF_THREADS), 0, st, ids, n_assign, E, bm, offs, tile_start,
                sorted_assign, inv);
         return;
     }
     launch(route_hist_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank);
-    launch(route_scan_kernel, dim3(1), dim3(256), 0, st, w.hist, nb, E, GROUPED_BM, offs, tile_start);
+    launch(route_scan_kernel, dim3(1), dim3(256), 0, st, w.hist, nb, E, bm, offs, tile_start);
     launch(route_scatter_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank,
                        sorted_assign, inv);
 }
