@@ -1,11 +1,11 @@
 // Mixture-of-experts routing for gfx950.
 //
 //  router_topk  one wave per token row: the router logits (the router GEMM's
-//               split-K partials summed here, in split order), softmax over
-//               the E of them, the top-k experts by logit (ties -> lower
-//               expert id; the same order as by probability), and their
-//               probabilities renormalised over the chosen k (the full softmax
-//               denominator cancels).
+//               split-K partials summed here, in split order), the top-k
+//               experts by logit (ties -> lower expert id; the same order as
+//               by probability) found by ranking every logit against the row,
+//               and their softmax probabilities renormalised over the chosen k
+//               (the full softmax denominator cancels).
 //  moe_route    stable counting sort of the rows * k assignments by expert, so
 //               each expert's rows are contiguous for the grouped GEMM.  Up to
 //               ROUTE_FUSED_MAX assignments (a canvas step): one workgroup
@@ -28,58 +28,65 @@ namespace dlm {
 
 constexpr int MAX_E = 256;
 
+// One wave per row, four rows per workgroup.  The row's logits are staged in
+// LDS; logit e's rank is the number of logits that beat it (larger, or equal
+// with a lower expert id), so the experts of rank < k in rank order are the
+// top-k in selection order.  Their probabilities exp(l - max) go to slot
+// `rank` and are summed in slot order for the renormalisation.
 __global__ __launch_bounds__(256) void router_topk_kernel(Partials logits, int rows, int E, int k, int* ids,
                                                            float* w, int* ids_copy, float* logits_copy) {
-    const int lane = threadIdx.x % WAVE;
-    const int r = blockIdx.x * 4 + threadIdx.x / WAVE;
-    if (r >= rows) return;
+    __shared__ __attribute__((aligned(16))) float sv[4][MAX_E];
+    __shared__ float sp[4][16];
+    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+    const int r = blockIdx.x * 4 + wv;
+    const bool live = r < rows;                      // every wave reaches both barriers
     constexpr int PER = MAX_E / WAVE;
     float v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = lane + WAVE * j;
         v[j] = -INFINITY;
-        if (e < E) {
+        if (live && e < E) {
             float x = 0.f;
             for (int s = 0; s < logits.splits; ++s) x += logits.p[s * logits.stride + (long)r * E + e];
             v[j] = x;
             if (logits_copy) logits_copy[(long)r * E + e] = x;
         }
+        sv[wv][e] = v[j];
     }
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < PER; ++j) m = fmaxf(m, v[j]);
     m = wave_max(m);
-    float sel_sum = 0.f;
-    for (int s = 0; s < k; ++s) {
-        // best remaining (value, lowest id) in this lane, then across the wave
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
+    __syncthreads();
+    const int E4 = (E + 3) / 4;
+    const f32x4* k4 = (const f32x4*)sv[wv];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int e = lane + WAVE * j;
-            if (e < E && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
+    for (int j = 0; j < PER; ++j) {
+        const int e = lane + WAVE * j;
+        if (!live || e >= E) continue;
+        const float c = v[j];
+        int rank = 0;
+        for (int q = 0; q < E4; ++q) {
+            const f32x4 x = k4[q];
+            const int i = 4 * q;
+            rank += (i + 0 < e) ? (x[0] >= c) : (x[0] > c);
+            rank += (i + 1 < e) ? (x[1] >= c) : (x[1] > c);
+            rank += (i + 2 < e) ? (x[2] >= c) : (x[2] > c);
+            rank += (i + 3 < e) ? (x[3] >= c) : (x[3] > c);
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, WAVE);
-            const int oe = __shfl_xor(be, o, WAVE);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        if (rank < k) {
+            sp[wv][rank] = expf(c - m);
+            ids[(long)r * k + rank] = e;
+            if (ids_copy) ids_copy[(long)r * k + rank] = e;
         }
-        const float p = expf(bv - m);
-        sel_sum += p;
-        if (lane == 0) {
-            ids[(long)r * k + s] = be;
-            if (ids_copy) ids_copy[(long)r * k + s] = be;
-            w[(long)r * k + s] = p;
-        }
-        // retire the chosen expert (k <= E, so a remaining one always exists)
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (lane + WAVE * j == be) v[j] = -INFINITY;
     }
-    if (lane == 0)
-        for (int s = 0; s < k; ++s) w[(long)r * k + s] /= sel_sum;
+    __syncthreads();
+    if (live && lane < k) {
+        float sel_sum = 0.f;
+        for (int s = 0; s < k; ++s) sel_sum += sp[wv][s];
+        w[(long)r * k + lane] = sp[wv][lane] / sel_sum;
+    }
 }
 
 void router_topk(const Partials& logits, int rows, int E, int k, int* ids, float* w, int* ids_copy,

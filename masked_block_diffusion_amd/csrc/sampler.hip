@@ -64,36 +64,47 @@ struct CanvasTab {
 
 constexpr int CMAX = 1024;
 
+// Ranking keys: a masked position's confidence, -inf for the others.  A
+// confidence is 1 / (sum of exp terms, the largest being 1), in (0, 1], so a
+// -inf key never beats or ties a masked one: counting the keys that beat a
+// masked position over all positions counts exactly the masked ones.  The
+// keys are read four at a time (independent loads, not one dependent chain).
 __global__ __launch_bounds__(256) void commit_kernel(CanvasTab tab, int C, const float* conf, const int* pred,
                                                       int mask_id, int kind, int k, float thr, int force_all,
                                                       float edit_thr, int* n_committed, int* n_masked) {
-    __shared__ float sc[CMAX];
-    __shared__ int sm[CMAX];
+    __shared__ __attribute__((aligned(16))) float key[CMAX];
     __shared__ int cnt[2];
     const int s = blockIdx.x;
     int32_t* canvas = tab.c[s];
     const float* cf = conf + (long)s * C;
     const int* pr = pred + (long)s * C;
+    const int C4 = (C + 3) / 4;
     if (threadIdx.x < 2) cnt[threadIdx.x] = 0;
-    for (int j = threadIdx.x; j < C; j += 256) {
-        sm[j] = canvas[j] == mask_id;
-        sc[j] = cf[j];
-    }
+    for (int j = threadIdx.x; j < 4 * C4; j += 256) key[j] = (j < C && canvas[j] == mask_id) ? cf[j] : -INFINITY;
     __syncthreads();
     int my_commit = 0, my_left = 0;
     for (int j = threadIdx.x; j < C; j += 256) {
-        if (!sm[j]) {
+        const float cj = key[j];
+        if (cj == -INFINITY) {
             // token editing: an earlier token whose prediction moved with enough confidence
-            if (edit_thr > 0.f && pr[j] != canvas[j] && sc[j] >= edit_thr) {
+            if (edit_thr > 0.f && pr[j] != canvas[j] && cf[j] >= edit_thr) {
                 canvas[j] = pr[j];
                 ++my_commit;
             }
             continue;
         }
-        const float cj = sc[j];
+        // rank = #{i < j: key_i >= cj} + #{i > j: key_i > cj}
         int rank = 0;
-        for (int i = 0; i < C; ++i)
-            rank += sm[i] && (sc[i] > cj || (sc[i] == cj && i < j));
+        const f32x4* k4 = (const f32x4*)key;
+#pragma unroll 8
+        for (int q = 0; q < C4; ++q) {
+            const f32x4 v = k4[q];
+            const int i = 4 * q;
+            rank += (i + 0 < j) ? (v[0] >= cj) : (v[0] > cj);
+            rank += (i + 1 < j) ? (v[1] >= cj) : (v[1] > cj);
+            rank += (i + 2 < j) ? (v[2] >= cj) : (v[2] > cj);
+            rank += (i + 3 < j) ? (v[3] >= cj) : (v[3] > cj);
+        }
         bool take;
         if (force_all) take = true;
         else if (kind == 0) take = rank < k;
