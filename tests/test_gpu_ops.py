@@ -92,7 +92,7 @@ def _bf16_tensor(shape, g):
     return (torch.randn(*shape, generator=g) * 0.5).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("variant,splits", [(v, 0) for v in range(13)] + [(3, 2), (2, 4), (1, 3), (0, 5), (9, 2), (10, 3)])
+@pytest.mark.parametrize("variant,splits", [(v, 0) for v in range(13)] + [(3, 2), (2, 4), (1, 3), (0, 5), (9, 2), (9, 4), (10, 3)])
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (37, 200, 1536), (256, 512, 2048), (300, 136, 256)])
 def test_gemm_variants_match_fp64(variant, splits, M, N, K):
     """Every tile variant and split factor of the dense GEMM, ragged M / N,
