@@ -547,7 +547,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   small M (<= 64; the tiny model, short canvases)     32 x 64,  waves 1x4, 4 stages
 //   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2 x 2 k-groups, 6 stages
 //     (SwiGLU pair: 128 x 64 x 2 weights, 2 k-groups, if N >= 4096, else 64 x 32 x 2)
-//   prefill M                                           128 x 128, waves 2x2, 4 stages
+//   prefill M                                           128 x 128, waves 2x2 x 2 k-groups, 4 stages (3 SwiGLU);
+//                                                       128 x 64 for a short-K residual add that 128 x 128 leaves the chip idle
 //   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128 (two k-groups), waves 4x1
 //   grouped (experts)                                   SwiGLU pair BM x 64 x 2, else BM x 128 (BM = grouped_bm);
 //                                                       waves 2x2, 3 stages
@@ -560,7 +561,7 @@ template <typename T, bool DUAL> using CoreS = Core<T, 32, 64, 1, 4, DUAL, 4>;
 template <typename T, bool DUAL> using CoreM = Core<T, 64, 64, 2, 2, DUAL, 4>;
 template <typename T, bool DUAL>
 using CoreW = std::conditional_t<DUAL, Core<T, 128, 64, 2, 2, true, 4>, Core<T, 256, 64, 4, 1, false, 3>>;
-template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4>;
+template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>;
 template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
 template <typename T> using CoreHw = Core<T, 256, 128, 4, 1, false, 3, 2>;
 // Expert tiles: 64 rows (about what one expert gets from a 256-row canvas at
@@ -603,8 +604,16 @@ static int splits_for(const GemmDesc& d) {
     // store measured slower from 160 tiles up; a residual add still gains
     // (split partials are plain stores summed by the next kernel, where the
     // unsplit epilogue reads and rewrites the fp32 stream)
+    if (d.M > 256) {
+        // prefill-sized: only a residual add with a long K and too few tiles
+        // for the chip splits, in two (the dense FFN's down projection at a
+        // 1024-token prompt: 42 us against 80 unsplit on 128 x 128 tiles)
+        if (C::TWO_B || EPI != EPI_ADD_F32 || tiles >= SPLIT_TARGET_WG || d.K < 4L * d.N || nkt < 8) return 1;
+        const int per = (nkt + 1) / 2;
+        return (nkt + per - 1) / per;
+    }
     const long no_split = (C::KW > 1 && EPI != EPI_ADD_F32) ? 160 : SPLIT_TARGET_WG * 3 / 4;
-    if (C::TWO_B || tiles >= no_split || d.M > 256) return 1;
+    if (C::TWO_B || tiles >= no_split) return 1;
     int s = (int)((SPLIT_TARGET_WG + tiles - 1) / tiles);
     s = std::min(s, std::max(1, nkt / 4));
     s = std::min(s, 2);
@@ -716,7 +725,20 @@ static void with_core(const GemmDesc& d, F f) {
             } else {
                 f(Core<T, 64, 64, 2, 2, false, 6, 2>{});
             }
-        } else f(CoreL<T, DUAL>{});
+        } else {
+            // prefill-sized M: 128 x 128 tiles with two k-groups; a residual
+            // add whose 128 x 128 tiles would leave CUs idle and whose K is
+            // short (the O projection at a 1024-token prompt: 16.4 us against
+            // 24.5) takes 128 x 64 tiles instead
+            const long t128 = (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+            if constexpr (!DUAL && EPI == EPI_ADD_F32) {
+                if (t128 < SPLIT_TARGET_WG && d.K < 4L * d.N) {
+                    f(Core<T, 128, 64, 2, 2, false, 4, 2>{});
+                    return;
+                }
+            }
+            f(CoreL<T, DUAL>{});
+        }
     }
 }
 
