@@ -30,8 +30,10 @@
 //     for fp8 models it is fed as two bf16 terms (hi + lo), fp32-level P V,
 //     since the per-token E4M3 quantisation of the attention output turns
 //     small differences into flipped codes.
-//   * Long key ranges are split across workgroups (split-KV); partial (max,
-//     sum, unnormalised O) are merged by a second kernel in fixed split order.
+//   * Long key ranges are split across workgroups (split-KV) when the
+//     (request, KV head, query block) workgroups alone are too few for the
+//     chip, in denoising and in prefill; partial (max, sum, unnormalised O)
+//     are merged by a second kernel in fixed split order.
 //   * Keys past the end of the range are never read from memory the caller
 //     has not written: their K rows are fetched from the tile's first key (and
 //     masked), and
@@ -481,7 +483,10 @@ static void launch_attn_bf16(AttnArgs& a, int n_seqs, int max_keys, bool causal,
     a.n_qblocks = (a.seqs.per_seq * a.group + S::QB - 1) / S::QB;
     const int ntiles = (max_keys + KT - 1) / KT;
     const int base = n_seqs * a.hkv * a.n_qblocks;
-    a.n_splits = causal ? 1 : choose_splits(256 * per_cu, base, ntiles, rows);
+    // causal (prefill) ranges split too: a query block's keys end at its last
+    // position, so later splits of early blocks are empty (written as max
+    // -inf, skipped by the merge), and the longest block's work is divided
+    a.n_splits = choose_splits(256 * per_cu, base, ntiles, rows);
     a.tiles_per_split = (ntiles + a.n_splits - 1) / a.n_splits;
     a.n_splits = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
     if (a.n_splits < 1) a.n_splits = 1;
