@@ -474,7 +474,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             {
                 Timed t(m, DLM_K_PERMUTE, st);
                 RouteWork rw{at<int>(ws, p.hist), at<int>(ws, p.lrank)};
-                moe_route(tid, A, E, grouped_bm(gdt), offs, tstart, sorted, inv, rw, st);
+                moe_route(tid, A, E, grouped_bm(gdt, A, E), offs, tstart, sorted, inv, rw, st);
             }
             void* ei = at<void>(ws, p.ei);
             {

@@ -550,8 +550,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   prefill M                                           128 x 128, waves 2x2 x 2 k-groups, 4 stages (3 SwiGLU);
 //                                                       128 x 64 for a short-K residual add that 128 x 128 leaves the chip idle
 //   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128 (two k-groups), waves 4x1
-//   grouped (experts)                                   SwiGLU pair BM x 64 x 2, else BM x 128 (BM = grouped_bm);
-//                                                       waves 2x2, 3 stages
+//   grouped (experts)                                   SwiGLU pair 64 x 64 x 2, else 64 x 128; waves 2x2, 3 stages
+//                                                       (fp8: 2 k-groups); >= 256 rows per expert on average:
+//                                                       128 x 128, 2 k-groups (BM = grouped_bm)
 // The canvas choices come from a sweep of every variant and split factor on
 // the workloads' projection shapes: small tiles give enough workgroups to keep
 // weight bytes in flight on every CU; the m-tiles sharing a weight tile are
@@ -573,10 +574,17 @@ template <typename T, bool DUAL>
 using CoreG = std::conditional_t<sizeof(T) == 1,
                                  std::conditional_t<DUAL, Core<T, 64, 64, 2, 2, true, 3, 2>, Core<T, 64, 128, 2, 2, false, 3, 2>>,
                                  std::conditional_t<DUAL, Core<T, 64, 64, 2, 2, true, 3>, Core<T, 64, 128, 2, 2, false, 3>>>;
+// Experts that average 256 rows or more (many requests' canvases, prompts)
+// are compute-bound: 128 x 128 tiles with two k-groups, as for prefill GEMMs.
+template <typename T, bool DUAL> using CoreGL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>;
 static_assert(CoreG<float, true>::BM == CoreG<float, false>::BM && CoreG<bf16_t, true>::BM == CoreG<bf16_t, false>::BM &&
-              CoreG<fp8_t, true>::BM == CoreG<fp8_t, false>::BM, "one expert m-tile height per operand type");
+              CoreG<fp8_t, true>::BM == CoreG<fp8_t, false>::BM && CoreGL<bf16_t, true>::BM == CoreGL<bf16_t, false>::BM,
+              "one expert m-tile height per operand type and tile family");
 
-int grouped_bm(int dtype) {
+static bool grouped_large(int n_assign, int E) { return (long)n_assign >= 256L * E; }
+
+int grouped_bm(int dtype, int n_assign, int E) {
+    if (grouped_large(n_assign, E)) return CoreGL<bf16_t, true>::BM;
     switch (dtype) {
         case DT_F32: return CoreG<float, true>::BM;
         case DT_FP8: return CoreG<fp8_t, true>::BM;
@@ -781,16 +789,24 @@ static void gemm_op(const GemmDesc& d, hipStream_t st, DenseOp op, long* io) {
     }
 }
 
-template <typename T>
-static void grouped_t(const GemmDesc& d, hipStream_t st) {
+template <typename T, template <typename, bool> class G>
+static void grouped_with(const GemmDesc& d, hipStream_t st) {
     switch (d.epi) {
         case GEMM_SWIGLU:
-            if (d.out_f32) launch_grouped<CoreG<T, true>, T, EPI_SWIGLU_F32>(d, st);
-            else launch_grouped<CoreG<T, true>, T, EPI_SWIGLU_BF16>(d, st);
+            if (d.out_f32) launch_grouped<G<T, true>, T, EPI_SWIGLU_F32>(d, st);
+            else launch_grouped<G<T, true>, T, EPI_SWIGLU_BF16>(d, st);
             break;
-        case GEMM_STORE_F32: launch_grouped<CoreG<T, false>, T, EPI_F32>(d, st); break;
+        case GEMM_STORE_F32: launch_grouped<G<T, false>, T, EPI_F32>(d, st); break;
         default: break;
     }
+}
+
+// The tile family must match the m-tile height the routing used
+// (grouped_bm with the same assignment count).
+template <typename T>
+static void grouped_t(const GemmDesc& d, hipStream_t st) {
+    if (grouped_large(d.M, d.E)) grouped_with<T, CoreGL>(d, st);
+    else grouped_with<T, CoreG>(d, st);
 }
 
 int gemm_main(const GemmDesc& d, hipStream_t st) {

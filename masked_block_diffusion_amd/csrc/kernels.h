@@ -35,9 +35,10 @@ enum GemmEpi { GEMM_STORE_F32 = 0, GEMM_STORE_BF16, GEMM_ADD_F32, GEMM_SWIGLU, G
 
 constexpr int MAX_SEQS = 64;
 
-// m-tile rows of the grouped (per-expert) GEMMs for operand type `dtype`; the
+// m-tile rows of the grouped (per-expert) GEMMs for operand type `dtype` and
+// n_assign (row, expert) assignments over E experts (the GEMM's M and E); the
 // routing scan computes each expert's first m-tile for this tile height.
-int grouped_bm(int dtype);
+int grouped_bm(int dtype, int n_assign, int E);
 
 // C[M, N] (op)= A[M, K] * B[N, K]^T.  Leading dimensions in elements.
 struct GemmDesc {
