@@ -329,7 +329,9 @@ size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N
  * every launch of a timed kernel is bracketed by HIP events on its stream.
  * dlm_timing_read synchronises, sums the elapsed times per kernel id since the
  * last read, and resets.
- *   ms[DLM_K_COUNT], launches[DLM_K_COUNT] (host, out; nullable). */
+ *   ms[DLM_K_COUNT], launches[DLM_K_COUNT] (host, out; nullable).
+ * DLM_K_COMBINE is kept for numbering only: the MoE layer's combine is part of
+ * the RMSNorm that reads its result (DLM_K_NORM). */
 typedef enum {
     DLM_K_EMBED = 0, DLM_K_NORM, DLM_K_GEMM_QKV, DLM_K_ROPE_KV, DLM_K_ATTN,
     DLM_K_ATTN_MERGE, DLM_K_GEMM_O, DLM_K_GEMM_GATE_UP, DLM_K_GEMM_DOWN,

@@ -343,6 +343,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
     void* ao = at<void>(ws, p.ao);
     void* fi = at<void>(ws, p.fi);
     Partials pending;                              // split residual update not yet added to x
+    MoeGather pending_moe;                         // routed experts' output not yet added to x
 
     {
         Timed t(m, DLM_K_EMBED, st);
@@ -352,9 +353,10 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
     // x += pending; RMSNorm into the GEMM operand: fp32 / bf16 in hA, fp8 also codes + scales
     auto norm = [&](const float* g) {
         Timed t(m, DLM_K_NORM, st);
-        rmsnorm(x, pending, g, R, d, c.rms_eps, f32 ? (float*)hA : nullptr, f32 ? nullptr : (uint16_t*)hA, hq, hs,
-                st);
+        rmsnorm(x, pending, pending_moe, g, R, d, c.rms_eps, f32 ? (float*)hA : nullptr,
+                f32 ? nullptr : (uint16_t*)hA, hq, hs, st);
         pending = Partials();
+        pending_moe = MoeGather();
     };
     auto opA = [&](const void* bf, const void* q8) { return fp8 ? q8 : bf; };
     // a GEMM on stream s with split-K partials in region `part`
@@ -504,10 +506,11 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                 gemm_grouped(g, st);
             }
             (void)hipStreamWaitEvent(st, m->join_ev, 0);
-            {
-                Timed t(m, DLM_K_COMBINE, st);
-                moe_combine(x, shared, y, inv, tw, R, k, d, st);
-            }
+            // x += shared + routed experts: added by the RMSNorm that reads x
+            // next (the next layer's, or the final one); nothing touches x,
+            // y, inv or the weights before it
+            pending = shared;
+            pending_moe = MoeGather{y, inv, tw, k};
         } else {
             ffn_gate_up(st, p.splitk);
             pending = ffn_down(st, p.splitk);

@@ -63,15 +63,15 @@ void embed(const IdSource& ids, int rows, const void* table, int dtype, int d, i
 }
 
 // ---------------------------------------------------------------- rmsnorm --
-// One wave per row; lane l holds the float4 chunks l, l + 64, ... of the row
-// (d <= 4 * 64 * MAXC).  x += residual partials (if any), then
-// h = x / sqrt(mean(x^2) + eps) * g.
+// One row per workgroup of four waves; thread t holds the float4 chunks t,
+// t + 256, ... of the row (d <= 4 * 256 * MAXC).  x += residual partials and
+// the MoE layer's routed experts (if any), then h = x / sqrt(mean(x^2) + eps) * g.
 
 constexpr int RN_T = 256;    // threads per row (4 waves)
 constexpr int MAXC = 4;       // float4 per thread: d <= 4 * RN_T * MAXC
 
-__global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, const float* g, int rows, int d,
-                                                        float eps, float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
+__global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, MoeGather moe, const float* g, int rows,
+                                                        int d, float eps, float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
     __shared__ float red[RN_T / WAVE];
     const int lane = threadIdx.x;      // thread of the row (4 waves per row)
     const int r = blockIdx.x;
@@ -90,13 +90,13 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, c
             if (out) gg[k] = *(const f32x4*)(g + 4 * c);
         }
     }
-    if (res.p) {
+    if (res.p || moe.y) {
         // split by split (fixed order); each split's loads of the whole row
         // are issued together, so a row costs one round trip per split
         f32x4 acc[MAXC];
 #pragma unroll
         for (int k = 0; k < MAXC; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < res.splits; ++sp) {
+        for (int sp = 0; res.p && sp < res.splits; ++sp) {
             const float* pr = res.p + sp * res.stride + (long)r * d;
             f32x4 t[MAXC];
 #pragma unroll
@@ -110,12 +110,39 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, c
                 if (c < nc) acc[k] += t[k];
             }
         }
-        if (res.a_scale) {
+        if (res.p && res.a_scale) {
             const float sa = res.a_scale[r];
 #pragma unroll
             for (int k = 0; k < MAXC; ++k) {
                 const int c = lane + RN_T * k;
                 if (c < nc) acc[k] = acc[k] * sa * *(const f32x4*)(res.b_scale + 4 * c);
+            }
+        }
+        // routed experts, slot by slot in selection order; the rows of four
+        // slots are loaded together (one round trip per four slots)
+        for (int s0 = 0; moe.y && s0 < moe.k; s0 += 4) {
+            f32x4 yv[4][MAXC];
+            float ws[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (s0 + j >= moe.k) break;
+                const long a = (long)r * moe.k + s0 + j;
+                ws[j] = moe.w[a];
+                const float* yr = moe.y + (long)moe.inv[a] * d;
+#pragma unroll
+                for (int k = 0; k < MAXC; ++k) {
+                    const int c = lane + RN_T * k;
+                    if (c < nc) yv[j][k] = *(const f32x4*)(yr + 4 * c);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (s0 + j >= moe.k) break;
+#pragma unroll
+                for (int k = 0; k < MAXC; ++k) {
+                    const int c = lane + RN_T * k;
+                    if (c < nc) acc[k] += ws[j] * yv[j][k];
+                }
             }
         }
 #pragma unroll
@@ -183,10 +210,10 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, c
     if (lane == 0) hs[r] = sc;
 }
 
-void rmsnorm(float* x, const Partials& res, const float* g, int rows, int d, float eps, float* hf, uint16_t* hb,
-             uint8_t* hq, float* hs, hipStream_t st) {
+void rmsnorm(float* x, const Partials& res, const MoeGather& moe, const float* g, int rows, int d, float eps,
+             float* hf, uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st) {
     if (rows <= 0) return;
-    launch(rmsnorm_kernel, dim3(rows), dim3(RN_T), 0, st, x, res, g, rows, d, eps, hf, hb, hq, hs);
+    launch(rmsnorm_kernel, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
 }
 
 int rmsnorm_max_dim() { return 4 * RN_T * MAXC; }

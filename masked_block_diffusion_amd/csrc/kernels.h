@@ -134,14 +134,25 @@ struct Partials {
     const float* b_scale = nullptr;
 };
 
-// x += res (when res.p is set; the residual update of a split O / down
-// projection), then h = x / sqrt(mean(x^2) + eps) * g per row, written to every
-// non-null output: hf fp32, hb bf16, and (fp8 models) hq E4M3 codes with
-// per-row scales hs quantised from the bf16 value.  d <= rmsnorm_max_dim(),
-// d % 4 == 0.
+// The routed experts' part of an MoE layer's output, for row r:
+// sum over slots s (in selection order) of w[r * k + s] * y[inv[r * k + s]]
+// (y fp32 [assignments, d] in sorted order).  Unset when y is null.
+struct MoeGather {
+    const float* y = nullptr;
+    const int* inv = nullptr;
+    const float* w = nullptr;
+    int k = 0;
+};
+
+// x += res + moe (the residual update of a split O / down projection when
+// res.p is set, then the MoE layer's routed experts when moe.y is set -- the
+// shared expert arriving as res), then h = x / sqrt(mean(x^2) + eps) * g per
+// row, written to every non-null output: hf fp32, hb bf16, and (fp8 models) hq
+// E4M3 codes with per-row scales hs quantised from the bf16 value.
+// d <= rmsnorm_max_dim(), d % 4 == 0.
 int rmsnorm_max_dim();
-void rmsnorm(float* x, const Partials& res, const float* g, int rows, int d, float eps, float* hf,
-             uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st);
+void rmsnorm(float* x, const Partials& res, const MoeGather& moe, const float* g, int rows, int d, float eps,
+             float* hf, uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st);
 
 // Per-row E4M3 quantisation of a bf16 matrix [rows, d]: s = amax / 448 (1 for a
 // zero row), q = e4m3(x / s).
@@ -181,11 +192,6 @@ void moe_route(const int* ids, int n_assign, int E, int bm, int* offs, int* tile
                int* inv, const RouteWork& w, hipStream_t st);
 int route_blocks(int n_assign);
 
-// x[r] += shared[r] + sum_s w[r, s] * y[inv[r * k + s]]   (y fp32 [A, d] in
-// sorted order; shared: the shared expert's down projection as Partials, or
-// nothing when shared.p is null)
-void moe_combine(float* x, const Partials& shared, const float* y, const int* inv, const float* w, int rows, int k,
-                 int d, hipStream_t st);
 
 // LM-head partials (max, sum exp, argmax) per (row, vocab tile) -> conf = 1/Z,
 // pred = lowest argmax.

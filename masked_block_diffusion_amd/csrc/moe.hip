@@ -19,8 +19,8 @@
 //                          first m-tile of every expert (bm-row tiles);
 //                 scatter  sorted position of every assignment and its inverse.
 //               Integer-only and deterministic: order is (expert, row, slot).
-//  moe_combine  x[r] += sum over slots s (in selection order) of
-//               w[r, s] * y[inv[r * k + s]].
+// The weighted un-permute of the experts' outputs (x += sum over slots of
+// w * y) is done by the RMSNorm that reads x next (MoeGather).
 #include "common.h"
 #include "kernels.h"
 
@@ -277,46 +277,6 @@ void moe_route(const int* ids, int n_assign, int E, int bm, int* offs, int* tile
     launch(route_scan_kernel, dim3(1), dim3(256), 0, st, w.hist, nb, E, bm, offs, tile_start);
     launch(route_scatter_kernel, dim3(nb), dim3(RB), 0, st, ids, n_assign, E, w.hist, w.local_rank,
                        sorted_assign, inv);
-}
-
-// ---------------------------------------------------------------- combine --
-
-// One workgroup per (token row, 1024-column chunk); each thread owns 4
-// consecutive columns (d is a multiple of 4) and issues all of its loads
-// before the arithmetic: x += shared-expert output (split partials summed in
-// order, fp8 scales applied) + sum over the row's k slots of w * y[slot's
-// sorted row].
-constexpr int COMBINE_COLS = 1024;
-__global__ __launch_bounds__(256) void moe_combine_kernel(float* x, Partials shared, const float* y,
-                                                           const int* inv, const float* w, int k, int d) {
-    const long r = blockIdx.x;
-    const int c = blockIdx.y * COMBINE_COLS + 4 * threadIdx.x;
-    if (c >= d) return;
-    const float* wr = w + r * k;
-    const int* ir = inv + r * k;
-    f32x4 yv[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-        if (s < k) yv[s] = *(const f32x4*)(y + (long)ir[s] * d + c);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (shared.p) {
-        const long off = r * d + c;
-        for (int s = 0; s < shared.splits; ++s) acc += *(const f32x4*)(shared.p + s * shared.stride + off);
-        if (shared.a_scale) acc = acc * shared.a_scale[r] * *(const f32x4*)(shared.b_scale + c);
-    }
-    f32x4* xp = (f32x4*)(x + r * d + c);
-    const f32x4 x0 = *xp;
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-        if (s < k) acc += wr[s] * yv[s];
-    *xp = x0 + acc;
-}
-
-void moe_combine(float* x, const Partials& shared, const float* y, const int* inv, const float* w, int rows, int k,
-                 int d, hipStream_t st) {
-    if (rows <= 0) return;
-    launch(moe_combine_kernel, dim3(rows, (d + COMBINE_COLS - 1) / COMBINE_COLS), dim3(256), 0, st, x, shared, y, inv, w, k,
-           d);
 }
 
 }  // namespace dlm
