@@ -325,6 +325,23 @@ dlm_status dlm_op_gemm(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int3
 size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, int32_t variant,
                              int32_t splits);
 
+/* Test hook: the MoE layer's sort of (row, slot) assignments by expert.
+ * ids: HOST int32 [n_assign], expert of each assignment (validated: each in
+ * [0, E), else E_ARG; copied into ws on `stream`).  Outputs (device):
+ * offs int32 [E + 1] (first sorted position of each expert, offs[E] =
+ * n_assign), tile_start int32 [E + 1] (first bm-row tile of each expert, last
+ * = total tiles), sorted_assign int32 [n_assign] (assignment indices ordered
+ * by (expert, index)), inv int32 [n_assign] (sorted position of each
+ * assignment).  Up to 4096 assignments one workgroup sorts them, beyond that
+ * three kernels -- the two paths the model takes.  ws / ws_bytes: device
+ * workspace of dlm_op_route_workspace(n_assign, E) bytes (E_WORKSPACE if
+ * smaller).  E_ARG for null pointers, n_assign < 1, E outside [1, 256] or
+ * bm < 1. */
+dlm_status dlm_op_route(const int32_t* ids, int32_t n_assign, int32_t E, int32_t bm, int32_t* offs,
+                        int32_t* tile_start, int32_t* sorted_assign, int32_t* inv, void* ws, size_t ws_bytes,
+                        void* stream);
+size_t dlm_op_route_workspace(int32_t n_assign, int32_t E);
+
 /* Kernel timing.  `kernel_mask` bit i enables timing of kernel id i (0 = off):
  * every launch of a timed kernel is bracketed by HIP events on its stream.
  * dlm_timing_read synchronises, sums the elapsed times per kernel id since the

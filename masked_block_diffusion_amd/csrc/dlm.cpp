@@ -844,6 +844,42 @@ dlm_status dlm_op_quant_rows(const void* x, int32_t rows, int32_t d, void* q, fl
     return hip_status("dlm_op_quant_rows");
 }
 
+// Workspace of dlm_op_route: the ids, then the multi-kernel path's block
+// histograms and local ranks, each 256-byte aligned.
+static size_t route_ws_layout(int32_t n_assign, int32_t E, size_t* hist_off, size_t* rank_off) {
+    const size_t ids = align_up((size_t)n_assign * 4);
+    const size_t hist = align_up((size_t)route_blocks(n_assign) * E * 4);
+    if (hist_off) *hist_off = ids;
+    if (rank_off) *rank_off = ids + hist;
+    return ids + hist + align_up((size_t)n_assign * 4);
+}
+
+size_t dlm_op_route_workspace(int32_t n_assign, int32_t E) {
+    if (n_assign < 1 || E < 1 || E > 256) return 0;
+    return route_ws_layout(n_assign, E, nullptr, nullptr);
+}
+
+dlm_status dlm_op_route(const int32_t* ids, int32_t n_assign, int32_t E, int32_t bm, int32_t* offs, int32_t* tile_start,
+                        int32_t* sorted_assign, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (!ids || !offs || !tile_start || !sorted_assign || !inv || !ws) return fail(DLM_E_ARG, "null pointer");
+    if (n_assign < 1) return fail(DLM_E_ARG, "n_assign %d < 1", n_assign);
+    if (E < 1 || E > 256) return fail(DLM_E_ARG, "E %d not in [1, 256]", E);
+    if (bm < 1) return fail(DLM_E_ARG, "bm %d < 1", bm);
+    for (int32_t a = 0; a < n_assign; ++a)
+        if (ids[a] < 0 || ids[a] >= E) return fail(DLM_E_ARG, "ids[%d] = %d outside [0, %d)", a, ids[a], E);
+    size_t hist_off, rank_off;
+    const size_t need = route_ws_layout(n_assign, E, &hist_off, &rank_off);
+    if (ws_bytes < need) return fail(DLM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    hipStream_t st = (hipStream_t)stream;
+    int* d_ids = at<int>(ws, 0);
+    hipError_t e = hipMemcpyAsync(d_ids, ids, (size_t)n_assign * 4, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "dlm_op_route: %s", hipGetErrorString(e));
+    RouteWork rw{at<int>(ws, hist_off), at<int>(ws, rank_off)};
+    moe_route(d_ids, n_assign, E, bm, offs, tile_start, sorted_assign, inv, rw, st);
+    return hip_status("dlm_op_route");
+}
+
 dlm_status dlm_debug_router(dlm_model* m, int32_t* router_ids, float* router_logits, int64_t capacity_rows) {
     g_err.clear();
     if (!m) return fail(DLM_E_ARG, "model is NULL");

@@ -138,3 +138,26 @@ def test_pack_weight_validates_on_the_host():
     assert lib.dlm_pack_weight(abi.DLM_BF16, 1, 16, 100, 0x1000, 0x100000, None) == abi.DLM_E_SHAPE
     assert lib.dlm_pack_weight(9, 1, 16, 64, 0x1000, 0x100000, None) == abi.DLM_E_DTYPE
     assert lib.dlm_pack_weight(abi.DLM_BF16, 1, 16, 64, 0x1000, 0x1000 + 100, None) == abi.DLM_E_ARG   # overlap
+
+
+def test_op_route_validates_on_the_host():
+    """The routing test hook checks every expert id (a host array) and its
+    workspace before any HIP call; ids outside [0, E) never reach a kernel."""
+    import numpy as np
+    lib = _lib()
+    assert lib.dlm_op_route_workspace(0, 8) == 0 and lib.dlm_op_route_workspace(10, 257) == 0
+    need = lib.dlm_op_route_workspace(100, 16)
+    assert need > 0
+    ids = np.zeros(100, dtype=np.int32)
+    p = ids.ctypes.data
+    fake = 0x1000
+    assert lib.dlm_op_route(None, 100, 16, 64, fake, fake, fake, fake, fake, need, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_route(p, 100, 0, 64, fake, fake, fake, fake, fake, need, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_route(p, 100, 16, 0, fake, fake, fake, fake, fake, need, None) == abi.DLM_E_ARG
+    ids[57] = 16
+    assert lib.dlm_op_route(p, 100, 16, 64, fake, fake, fake, fake, fake, need, None) == abi.DLM_E_ARG
+    assert b"ids[57]" in lib.dlm_last_error()
+    ids[57] = -1
+    assert lib.dlm_op_route(p, 100, 16, 64, fake, fake, fake, fake, fake, need, None) == abi.DLM_E_ARG
+    ids[57] = 3
+    assert lib.dlm_op_route(p, 100, 16, 64, fake, fake, fake, fake, fake, need - 1, None) == abi.DLM_E_WORKSPACE

@@ -310,3 +310,45 @@ def test_gemm_tiled_weights_bit_identical(variant, splits, M, N, K):
             outs.append(C)
         torch.cuda.synchronize()
         assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("n,E,bm,dist", [(1, 1, 64, "uniform"), (64, 256, 64, "uniform"), (2048, 128, 64, "uniform"),
+                                         (2048, 128, 64, "one"), (4096, 256, 32, "skewed"), (4096, 128, 128, "uniform"),
+                                         (4097, 128, 64, "uniform"), (4097, 256, 64, "skewed"), (1000, 7, 32, "uniform"),
+                                         (65536, 128, 128, "uniform"), (32768, 128, 64, "one")])
+def test_route_sort_bit_exact(n, E, bm, dist):
+    """The expert sort of the MoE layer (one-workgroup path up to 4096
+    assignments, three kernels beyond) against a stable sort on the CPU:
+    offsets, m-tile starts, order by (expert, assignment) and its inverse, bit
+    for bit, including 256 experts, a single expert and the path boundary."""
+    import numpy as np
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    rng = np.random.default_rng(n * 7 + E)
+    if dist == "uniform":
+        ids = rng.integers(0, E, n)
+    elif dist == "one":
+        ids = np.full(n, E - 1)
+    else:                                             # a few hot experts
+        ids = np.minimum(rng.geometric(0.05, n) - 1, E - 1)
+    ids = ids.astype(np.int32)
+    counts = np.bincount(ids, minlength=E)
+    offs_ref = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    tiles_ref = np.concatenate([[0], np.cumsum((counts + bm - 1) // bm)]).astype(np.int32)
+    sorted_ref = np.argsort(ids, kind="stable").astype(np.int32)
+    inv_ref = np.empty(n, dtype=np.int32)
+    inv_ref[sorted_ref] = np.arange(n, dtype=np.int32)
+    dev = "cuda"
+    offs = torch.full((E + 1,), -7, dtype=torch.int32, device=dev)
+    tiles = torch.full((E + 1,), -7, dtype=torch.int32, device=dev)
+    srt = torch.full((n,), -7, dtype=torch.int32, device=dev)
+    inv = torch.full((n,), -7, dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.dlm_op_route_workspace(n, E), dtype=torch.uint8, device=dev)
+    abi.check(lib.dlm_op_route(ids.ctypes.data, n, E, bm, offs.data_ptr(), tiles.data_ptr(), srt.data_ptr(),
+                               inv.data_ptr(), ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream),
+              "route")
+    torch.cuda.synchronize()
+    assert np.array_equal(offs.cpu().numpy(), offs_ref)
+    assert np.array_equal(tiles.cpu().numpy(), tiles_ref)
+    assert np.array_equal(srt.cpu().numpy(), sorted_ref)
+    assert np.array_equal(inv.cpu().numpy(), inv_ref)
