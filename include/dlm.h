@@ -342,6 +342,14 @@ dlm_status dlm_op_route(const int32_t* ids, int32_t n_assign, int32_t E, int32_t
                         void* stream);
 size_t dlm_op_route_workspace(int32_t n_assign, int32_t E);
 
+/* Test hook: the MoE router's selection.  logits: device fp32 [rows, E];
+ * ids: device int32 [rows, k] (out), the k experts with the largest logits in
+ * decreasing order, ties to the lower expert id; w: device fp32 [rows, k]
+ * (out), their softmax probabilities renormalised over the k.  E_ARG for null
+ * pointers, rows < 1, E outside [1, 256] or k outside [1, min(16, E)]. */
+dlm_status dlm_op_router_topk(const float* logits, int32_t rows, int32_t E, int32_t k, int32_t* ids, float* w,
+                              void* stream);
+
 /* Kernel timing.  `kernel_mask` bit i enables timing of kernel id i (0 = off):
  * every launch of a timed kernel is bracketed by HIP events on its stream.
  * dlm_timing_read synchronises, sums the elapsed times per kernel id since the

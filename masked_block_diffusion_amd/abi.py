@@ -53,7 +53,7 @@ EXPORTS = [
     "dlm_commit", "dlm_append_canvas", "dlm_check_device_status", "dlm_last_error",
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
     "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace", "dlm_packed_weight_bytes", "dlm_pack_weight",
-    "dlm_op_route", "dlm_op_route_workspace",
+    "dlm_op_route", "dlm_op_route_workspace", "dlm_op_router_topk",
 ]
 DLM_GEMM_B_TILED = 0x100
 
@@ -139,6 +139,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_pack_weight": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P]),
         "dlm_op_route": (c_int32, [P, c_int32, c_int32, c_int32, P, P, P, P, P, c_size_t, P]),
         "dlm_op_route_workspace": (c_size_t, [c_int32, c_int32]),
+        "dlm_op_router_topk": (c_int32, [P, c_int32, c_int32, c_int32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

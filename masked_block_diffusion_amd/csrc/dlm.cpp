@@ -880,6 +880,19 @@ dlm_status dlm_op_route(const int32_t* ids, int32_t n_assign, int32_t E, int32_t
     return hip_status("dlm_op_route");
 }
 
+dlm_status dlm_op_router_topk(const float* logits, int32_t rows, int32_t E, int32_t k, int32_t* ids, float* w,
+                              void* stream) {
+    g_err.clear();
+    if (!logits || !ids || !w) return fail(DLM_E_ARG, "null pointer");
+    if (rows < 1) return fail(DLM_E_ARG, "rows %d < 1", rows);
+    if (E < 1 || E > 256) return fail(DLM_E_ARG, "E %d not in [1, 256]", E);
+    if (k < 1 || k > 16 || k > E) return fail(DLM_E_ARG, "k %d not in [1, min(16, E)]", k);
+    Partials p;
+    p.p = logits;
+    router_topk(p, rows, E, k, ids, w, nullptr, nullptr, (hipStream_t)stream);
+    return hip_status("dlm_op_router_topk");
+}
+
 dlm_status dlm_debug_router(dlm_model* m, int32_t* router_ids, float* router_logits, int64_t capacity_rows) {
     g_err.clear();
     if (!m) return fail(DLM_E_ARG, "model is NULL");

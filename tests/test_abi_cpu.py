@@ -161,3 +161,13 @@ def test_op_route_validates_on_the_host():
     assert lib.dlm_op_route(p, 100, 16, 64, fake, fake, fake, fake, fake, need, None) == abi.DLM_E_ARG
     ids[57] = 3
     assert lib.dlm_op_route(p, 100, 16, 64, fake, fake, fake, fake, fake, need - 1, None) == abi.DLM_E_WORKSPACE
+
+
+def test_op_router_topk_validates_on_the_host():
+    lib = _lib()
+    f = 0x1000
+    assert lib.dlm_op_router_topk(None, 4, 8, 2, f, f, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_router_topk(f, 0, 8, 2, f, f, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_router_topk(f, 4, 257, 2, f, f, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_router_topk(f, 4, 8, 9, f, f, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_router_topk(f, 4, 32, 17, f, f, None) == abi.DLM_E_ARG

@@ -352,3 +352,28 @@ def test_route_sort_bit_exact(n, E, bm, dist):
     assert np.array_equal(tiles.cpu().numpy(), tiles_ref)
     assert np.array_equal(srt.cpu().numpy(), sorted_ref)
     assert np.array_equal(inv.cpu().numpy(), inv_ref)
+
+
+@pytest.mark.parametrize("rows,E,k", [(1, 1, 1), (257, 128, 8), (64, 256, 16), (33, 16, 4), (5, 7, 7)])
+def test_router_topk_ties_and_weights(rows, E, k):
+    """The router's top-k on logits with many exact ties (small integers):
+    experts in decreasing logit order with ties to the lower id, exactly as a
+    stable sort on the CPU; weights = softmax renormalised over the chosen k
+    (fp32 against float64, relative 1e-6)."""
+    import numpy as np
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    rng = np.random.default_rng(rows * 3 + E)
+    logits = rng.integers(-3, 4, size=(rows, E)).astype(np.float32) * 0.5
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    sel = np.take_along_axis(logits.astype(np.float64), order, axis=1)
+    p = np.exp(sel - logits.max(axis=1, keepdims=True))
+    w_ref = p / p.sum(axis=1, keepdims=True)
+    d = torch.from_numpy(logits).cuda()
+    ids = torch.full((rows, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((rows, k), dtype=torch.float32, device="cuda")
+    abi.check(lib.dlm_op_router_topk(d.data_ptr(), rows, E, k, ids.data_ptr(), w.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream), "router_topk")
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), order.astype(np.int32))
+    assert np.allclose(w.cpu().numpy(), w_ref, rtol=1e-6, atol=0)
