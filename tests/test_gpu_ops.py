@@ -377,3 +377,58 @@ def test_router_topk_ties_and_weights(rows, E, k):
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), order.astype(np.int32))
     assert np.allclose(w.cpu().numpy(), w_ref, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("C", [32, 1000])
+def test_commit_ties_bit_exact(C):
+    """dlm_commit on hand-built confidences drawn from three values (ties
+    everywhere), some positions already committed, three requests: the
+    top-k rule (ties -> lower position) and the threshold rule (inclusive at
+    the threshold, the single most confident when none reaches it, every
+    masked position at the last step) against the oracle's commit functions,
+    canvases and counts bit for bit."""
+    import numpy as np
+    import synth
+    from masked_block_diffusion_amd import DLM, Rule
+    from oracle import sampler as osampler
+    run = synth.get_run("tiny")
+    cfg = run.model
+    w = synth.make_weights(cfg, seed=run.seed)
+    gm = DLM(cfg, {k: v.to("cuda:0") for k, v in w.items()}, canvas=C, device="cuda:0")
+    R, mask = 3, cfg.mask_id
+    rng = np.random.default_rng(C)
+    seqs = [gm.new_seq(C + 64) for _ in range(R)]
+    # (rule, steps, step): top-k of C // steps (+1) per step, all of C at one
+    # step; threshold 0.5 at a first step, a middle step and the last (forced)
+    cases = [("topk", 1, 0), ("topk", 3, 2), ("topk", 7, 0), ("threshold", 3, 0), ("threshold", 3, 1),
+             ("threshold", 3, 2)]
+    for rule_kind, n_steps, step in cases:
+        canv = np.where(rng.random((R, C)) < 0.7, mask, rng.integers(0, mask, (R, C))).astype(np.int32)
+        canv[1, :] = mask                                       # request 1 fully masked
+        conf = rng.choice(np.float32([0.25, 0.5, 0.75]), size=(R, C)).astype(np.float32)
+        if rule_kind == "threshold":
+            conf[2] = np.float32(0.25)                          # request 2: nothing reaches 0.5
+        pred = rng.integers(0, mask, (R, C)).astype(np.int32)
+        if rule_kind == "topk":
+            k = osampler.topk_schedule(C, n_steps)[step]
+            rule = Rule.topk(C, n_steps)
+        else:
+            rule = Rule.threshold(n_steps, 0.5)
+        for i, s in enumerate(seqs):
+            s.canvas.copy_(torch.from_numpy(canv[i]))
+        conf_d = torch.from_numpy(conf.reshape(-1)).cuda()
+        pred_d = torch.from_numpy(pred.reshape(-1)).cuda()
+        ncom = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+        nmask = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+        gm.dlm_commit(seqs, conf_d, pred_d, rule, step, ncom, nmask)
+        torch.cuda.synchronize()
+        for i, s in enumerate(seqs):
+            if rule_kind == "topk":
+                want, chosen = osampler.commit_topk(canv[i], conf[i], pred[i], mask, k)
+            else:
+                want, chosen = osampler.commit_threshold(canv[i], conf[i], pred[i], mask, 0.5, step, n_steps)
+            got = s.canvas.cpu().numpy()
+            assert np.array_equal(got, want), (rule_kind, step, i)
+            assert int(ncom[i]) == len(chosen)
+            assert int(nmask[i]) == int((want == mask).sum())
+    gm.close()
