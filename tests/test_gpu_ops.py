@@ -432,3 +432,55 @@ def test_commit_ties_bit_exact(C):
             assert int(ncom[i]) == len(chosen)
             assert int(nmask[i]) == int((want == mask).sum())
     gm.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "dense-mini"])
+def test_lm_head_argmax_ties(name):
+    """The LM head's fused reduction on exact ties: the head is zero except
+    three identical rows (two ids in one vocabulary tile, one in another) and
+    the [MASK] row at ten times that vector.  Every canvas row then ties --
+    among the three (where h.v > 0) or among all the zero rows -- and the
+    prediction must be the lowest tied id, never [MASK], with confidence
+    1 / sum exp(l - max) over the non-[MASK] logits the kernel exposes."""
+    import numpy as np
+    import synth
+    from masked_block_diffusion_amd import DLM
+    run = synth.get_run(name)
+    cfg, C = run.model, run.canvas
+    w = synth.make_weights(cfg, seed=run.seed)
+    lm = w["lm_head"]
+    g = torch.Generator().manual_seed(5)
+    v = (torch.randn(cfg.d_model, generator=g) * 0.05).to(lm.dtype)
+    lm.zero_()
+    tied = [70, 71, 300]
+    for t in tied:
+        lm[t] = v
+    lm[cfg.mask_id] = (v.float() * 10).to(lm.dtype)
+    if cfg.dtype == "fp8":
+        pytest.skip("fp8 heads are quantised codes")
+    gm = DLM(cfg, {k: x.to("cuda:0") for k, x in w.items()}, canvas=C, device="cuda:0")
+    ids = synth.make_inputs(run)[0].to("cuda:0")
+    seq = gm.new_seq(run.capacity())
+    ws = gm.workspace(max(C, len(ids)), run.capacity())
+    gm.dlm_prefill(seq, ids, ws)
+    conf = torch.empty(C, dtype=torch.float32, device="cuda:0")
+    pred = torch.empty(C, dtype=torch.int32, device="cuda:0")
+    logits = torch.empty(C * cfg.vocab, dtype=torch.float32, device="cuda:0")
+    gm.dlm_denoise_step([seq], conf, pred, ws, logits)
+    torch.cuda.synchronize()
+    L = logits.view(C, cfg.vocab).double().cpu().numpy()
+    keep = np.arange(cfg.vocab) != cfg.mask_id
+    got_pred, got_conf = pred.cpu().numpy(), conf.cpu().numpy()
+    kinds = set()
+    for r in range(C):
+        lr = np.where(keep, L[r], -np.inf)
+        mx = lr.max()
+        assert L[r, tied[0]] == L[r, tied[1]] == L[r, tied[2]]          # the ties are exact in the kernel
+        want = int(np.nonzero(lr == mx)[0][0])
+        kinds.add(want)
+        assert got_pred[r] == want, (r, got_pred[r], want)
+        assert got_pred[r] != cfg.mask_id
+        z = np.exp(lr[keep] - mx).sum()
+        assert abs(got_conf[r] - 1.0 / z) <= 1e-5 / z
+    assert kinds <= {0, tied[0]}
+    gm.close()
