@@ -340,7 +340,7 @@ def main():
         ap.error("--profile-steps needs --profile")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+        print("bench.py measures one GPU: the library runs the hot path on a single MI355X "
               "(no multi-GPU path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -81,7 +81,7 @@ typedef int32_t dlm_status;
 #define DLM_E_WORKSPACE  -6   /* workspace null or smaller than dlm_workspace_bytes */
 #define DLM_E_HIP        -7   /* a HIP runtime call failed */
 #define DLM_E_DEVICE     -8   /* the device error word is set */
-#define DLM_E_UNSUPPORTED -9  /* valid request this build does not implement */
+#define DLM_E_UNSUPPORTED -9  /* valid request the library does not implement */
 
 /* Bits of the device error word. */
 #define DLM_DEVERR_TOKEN_RANGE   1   /* an input id was < 0 or >= vocab */
