@@ -3,16 +3,20 @@
 One bench step is one whole request through the library: causal prefill of
 the prompt, then per canvas the denoising steps (each a bidirectional forward
 + LM head + fused vocab reduction, then the confidence-ranked commit) and the
-append of the finished canvas to the KV cache.  `value` is committed tokens per
-second over the K timed steps, inputs already resident in HBM.
+append of the finished canvas to the KV cache.  `value` is decode-only
+committed tokens per second: the tokens of the K timed requests over their
+wall time minus their prefills (timed with HIP events on the library's
+stream); `end_to_end_tokens_per_s` counts the prefills too.  Inputs are
+resident in HBM before the timed region.
 
-Default workload: the dense 16-layer d=2048 bf16 model (16 Q / 4 KV heads x
-128, SwiGLU 8192, vocab 32768) with a 1024-token prefix and one 256-token
-canvas, 16 steps x 16 commits, then the append.  `--workload moe` runs the
-32-layer 26B-class MoE (128 experts top-8 x 768 + shared 2048, vocab 262144)
-with a 4096-token prefix and 4 canvases of 12 steps; `moe-fp8` the same model
-with E4M3 GEMMs and the confidence-threshold rule; `moe-batch32` 32 requests
-with prefixes of 512..4096 tokens denoised together.  Weights and prompts are
+Default workload: the 32-layer 26B-class MoE (d=2560, 20 Q / 4 KV heads x 128,
+128 experts top-8 x 768 + shared SwiGLU 2048, vocab 262144) in bf16 at batch
+1, with a 4096-token prefix and 4 canvases of 12 steps (21-22 commits each),
+each appended to the KV cache -- the shape of the pages' single-GPU
+measurement (4096 tokens in, 1024 out).  `--workload dense` runs the dense
+16-layer d=2048 bf16 model (1024-token prefix, one canvas of 16 x 16);
+`moe-fp8` the MoE with E4M3 GEMMs and the confidence-threshold rule;
+`moe-batch32` 32 requests with prefixes of 512..4096 tokens denoised together.  Weights and prompts are
 seeded synthetic draws (random init).  Models up to a few billion parameters
 are drawn on the host and copied, so the CPU baseline reads the same bytes;
 the 26B-class ones are drawn on the GPU, and the CPU baseline reads a copy of
@@ -201,7 +205,18 @@ def cpu_baseline(run, weights, prefix_cpu, steps_per_canvas: float, sample_layer
     append_s = (t3 - t2) * scale
     per_req = prefill_s + run.n_canvases * (steps_per_canvas * step_s + append_s)
     R = run.n_requests
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in info] or [1])
+    blas = sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in info
+                   if p.get("user_api") == "blas"})
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     what = (f"the whole {L}-layer model" if Ls == L else
             f"{Ls} of {L} layers at full width (embedding, {'layers 0..' + str(Ls - 1) if Ls > 1 else 'layer 0'}, LM head "
             f"{lm:.2f} s timed alone), layer time scaled x{scale:g}")
@@ -209,6 +224,9 @@ def cpu_baseline(run, weights, prefix_cpu, steps_per_canvas: float, sample_layer
         "value": R * C * run.n_canvases / (R * per_req),
         "unit": "tokens/s",
         "cores": threads,
+        "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model,
+        "blas": ", ".join(blas),
         "kind": "oracle",
         "sample": (f"float64 numpy oracle on the host ({threads} BLAS threads), {what}: prefill of the "
                    f"{len(prefix_cpu)}-token prompt of request 0 ({t1 - t0:.2f} s), one denoising step + commit "
@@ -303,8 +321,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="dense",
-                    help="dense (default), moe, moe-fp8, moe-batch32, tiny, or a reduced run name")
+    ap.add_argument("--workload", default="moe",
+                    help="moe (default: the 26B-class MoE, bf16, batch 1), dense, moe-fp8, moe-batch32, tiny, "
+                         "or a reduced run name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="for runs under a profiler: no per-kernel event timing (no roofline), "
@@ -378,6 +397,8 @@ def main():
     pred = torch.empty(R * C, dtype=torch.int32, device="cuda")
     n_masked = torch.empty(R, dtype=torch.int32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * run.n_canvases)]
+    pf_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    prefill_ms = []       # per timed request
     all_ids = list(range(abi.DLM_K_COUNT))
 
     moe = cfg.ffn == "moe"
@@ -387,10 +408,14 @@ def main():
 
     graph_cache = {}
 
-    def one_request(timed_ids, count_experts=False, graphs=False):
+    def one_request(timed_ids, count_experts=False, graphs=False, time_prefill=False):
+        if time_prefill:
+            pf_ev[0].record()
         for s, ids in zip(seqs, prefixes):
             s.raw.T = 0
             model.dlm_prefill(s, ids, ws)
+        if time_prefill:
+            pf_ev[1].record()
         steps_run = 0
         for ci in range(run.n_canvases):
             for s in seqs:
@@ -398,7 +423,7 @@ def main():
             cg = None
             if graphs:
                 cg = graph_cache.get(ci)
-                if cg is None or not cg.valid_for(seqs):
+                if cg is None or not cg.valid_for(seqs, conf, pred, rule, ws, None, n_masked):
                     cg = graph_cache[ci] = CanvasSteps(model, seqs, conf, pred, rule, ws, None, n_masked)
             model.timing_enable(timed_ids)
             ev[4 * ci].record()
@@ -427,6 +452,8 @@ def main():
             ev[4 * ci + 2].record()
             model.dlm_append_canvas(seqs, ws)
             ev[4 * ci + 3].record()
+        if time_prefill:
+            prefill_ms.append(pf_ev[0].elapsed_time(pf_ev[1]))     # synchronises on the prefill's end only
         return steps_run
 
     log(f"warmup {args.warmup} (+1 with every kernel timed)")
@@ -453,7 +480,7 @@ def main():
     t0 = time.perf_counter()
     n_denoise = 0
     for _ in range(args.steps):
-        n_denoise += one_request(dom_ids)
+        n_denoise += one_request(dom_ids, time_prefill=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kt = model.timing_read()
@@ -470,9 +497,10 @@ def main():
     rows = R * C
     keys = [len(p) + C * (run.n_canvases + 1) / 2 for p in prefixes_cpu]   # mean over the canvases
     step_ms = denoise_ms / max(1, steps_last)
+    decode_s = elapsed - 1e-3 * sum(prefill_ms)
     out = {
         "metric": METRIC,
-        "value": tokens / elapsed,
+        "value": tokens / decode_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -493,9 +521,13 @@ def main():
             "parallelism": "single GPU",
             "kv_cache": "paged, 64-token pages of one pool" if R > 1 else "contiguous per request",
         },
+        "value_note": ("decode only: committed tokens of the timed requests over their wall time minus their "
+                       "prefills (HIP events); ms_per_step is the whole request, prefill included"),
+        "end_to_end_tokens_per_s": tokens / elapsed,
+        "prefill_ms": sum(prefill_ms) / max(1, len(prefill_ms)),
         "ms_per_denoise_step": step_ms,
-        "decode_tokens_per_s": (R * C * run.n_canvases / ((denoise_ms + append_ms) * 1e-3)
-                                if denoise_ms else None),
+        "last_request_denoise_append_tokens_per_s": (R * C * run.n_canvases / ((denoise_ms + append_ms) * 1e-3)
+                                                     if denoise_ms else None),
         "roofline": roofline(dominant, cfg, rows, keys, ms_k / max(1, n_k), experts_used) if dominant else None,
         "denoise_step_kernels_ms": {k: round(v[0] / max(1, steps_full), 4) for k, v in
                                     sorted(per_kernel.items(), key=lambda kv: -kv[1][0])},

@@ -252,7 +252,12 @@ dlm_status dlm_prefill(dlm_model* model, dlm_seq* seq, const int32_t* ids, int32
 /* One denoising pass over the canvases of n_seqs requests.  Request r's canvas
  * sits at positions [T_r, T_r + C); its queries attend to cache slots [0, T_r)
  * and to all C canvas keys (no mask inside the canvas).  The canvas K/V are
- * written to slots [T_r, T_r + C) as scratch; T does not change.
+ * written to slots [T_r, T_r + C) as scratch; T does not change.  Those K/V
+ * are bit-identical to what dlm_append_canvas writes for the same canvas (the
+ * same forward under the same block mask), so a caller whose canvas already
+ * holds final tokens may advance seq->T by C instead of appending -- what
+ * autoregressive decoding with C = 1 does (the canvas holds the newest token;
+ * the pass's prediction is the next one).
  *   conf [n_seqs, C] fp32 (device, out): max softmax probability over the
  *        vocabulary without [MASK];
  *   pred [n_seqs, C] int32 (device, out): lowest-id argmax over the same set;

@@ -26,10 +26,10 @@
 //     The rows of a 16-key score block are taken in a permuted key order
 //     (key_of), chosen so the 8 probabilities a lane feeds to one P V MFMA are
 //     8 consecutive keys: its V^T operand is then one 16-byte LDS read.
-//   * P is rounded to bf16 for the P V MFMAs (the output is stored in bf16);
-//     for fp8 models it is fed as two bf16 terms (hi + lo), fp32-level P V,
-//     since the per-token E4M3 quantisation of the attention output turns
-//     small differences into flipped codes.
+//   * P enters the P V MFMAs as two bf16 terms (hi = bf16(p), lo = bf16(p -
+//     hi)), so P V is taken at fp32 level (relative error ~2^-16 per
+//     probability) like the softmax itself; a single bf16 term would add a
+//     2^-9 rounding of every probability that the model does not have.
 //   * Long key ranges are split across workgroups (split-KV) when the
 //     (request, KV head, query block) workgroups alone are too few for the
 //     chip, in denoising and in prefill; partial (max, sum, unnormalised O)
@@ -117,7 +117,7 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DH, bool PLO>
+template <int DH>
 __global__ __launch_bounds__(AttnShape<DH>::NW * WAVE) void attn_bf16_kernel(AttnArgs a) {
     using S = AttnShape<DH>;
     constexpr int QB = S::QB, QW = S::QW, QBN = S::QBN;
@@ -289,10 +289,8 @@ __global__ __launch_bounds__(AttnShape<DH>::NW * WAVE) void attn_bf16_kernel(Att
                     q1[v] = exp2_raw(fmaf(x[qb][2 * h2 + 1][v], a.scale_log2, -m_use));
                     ph[qb][h2][v] = (__bf16)q0[v];
                     ph[qb][h2][4 + v] = (__bf16)q1[v];
-                    if constexpr (PLO) {
-                        pl[qb][h2][v] = (__bf16)(q0[v] - (float)ph[qb][h2][v]);
-                        pl[qb][h2][4 + v] = (__bf16)(q1[v] - (float)ph[qb][h2][4 + v]);
-                    }
+                    pl[qb][h2][v] = (__bf16)(q0[v] - (float)ph[qb][h2][v]);
+                    pl[qb][h2][4 + v] = (__bf16)(q1[v] - (float)ph[qb][h2][4 + v]);
                 }
                 ps += ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q1[0] + q1[1]) + (q1[2] + q1[3]));
             }
@@ -316,7 +314,7 @@ __global__ __launch_bounds__(AttnShape<DH>::NW * WAVE) void attn_bf16_kernel(Att
 #pragma unroll
                 for (int qb = 0; qb < QBN; ++qb) {
                     o[qb][d] = mfma_bf16(vf, ph[qb][h2], o[qb][d]);
-                    if constexpr (PLO) o[qb][d] = mfma_bf16(vf, pl[qb][h2], o[qb][d]);
+                    o[qb][d] = mfma_bf16(vf, pl[qb][h2], o[qb][d]);
                 }
             }
         }
@@ -476,7 +474,7 @@ static int choose_splits(int target, int base_blocks, int ntiles, int rows) {
 }
 
 template <int DH>
-static void launch_attn_bf16(AttnArgs& a, int n_seqs, int max_keys, bool causal, bool p_two_terms, int rows,
+static void launch_attn_bf16(AttnArgs& a, int n_seqs, int max_keys, bool causal, int rows,
                              hipStream_t st) {
     using S = AttnShape<DH>;
     constexpr int per_cu = (160 * 1024) / (S::NSTAGE * S::STAGE) >= 2 ? 2 : 1;
@@ -490,8 +488,7 @@ static void launch_attn_bf16(AttnArgs& a, int n_seqs, int max_keys, bool causal,
     a.tiles_per_split = (ntiles + a.n_splits - 1) / a.n_splits;
     a.n_splits = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
     if (a.n_splits < 1) a.n_splits = 1;
-    if (p_two_terms) launch(attn_bf16_kernel<DH, true>, dim3(base * a.n_splits), dim3(S::NW * WAVE), 0, st, a);
-    else launch(attn_bf16_kernel<DH, false>, dim3(base * a.n_splits), dim3(S::NW * WAVE), 0, st, a);
+    launch(attn_bf16_kernel<DH>, dim3(base * a.n_splits), dim3(S::NW * WAVE), 0, st, a);
 }
 
 long attention_work_floats(int rows, int hq, int dh) {
@@ -500,7 +497,7 @@ long attention_work_floats(int rows, int hq, int dh) {
 }
 
 void attention(const void* q, const SeqTab& seqs, int layer, int n_layers, int hq, int hkv, int dh, bool causal,
-               bool f32, bool p_two_terms, void* out, const AttnWork& w, hipStream_t st) {
+               bool f32, void* out, const AttnWork& w, hipStream_t st) {
     (void)n_layers;
     const int rows = seqs.n * seqs.per_seq;
     if (rows <= 0) return;
@@ -525,9 +522,9 @@ void attention(const void* q, const SeqTab& seqs, int layer, int n_layers, int h
     a.o_part = w.o_part;
     a.ml_part = w.ml_part;
     a.rows = rows;
-    if (dh == 128) launch_attn_bf16<128>(a, seqs.n, max_keys, causal, p_two_terms, rows, st);
-    else if (dh == 64) launch_attn_bf16<64>(a, seqs.n, max_keys, causal, p_two_terms, rows, st);
-    else launch_attn_bf16<32>(a, seqs.n, max_keys, causal, p_two_terms, rows, st);
+    if (dh == 128) launch_attn_bf16<128>(a, seqs.n, max_keys, causal, rows, st);
+    else if (dh == 64) launch_attn_bf16<64>(a, seqs.n, max_keys, causal, rows, st);
+    else launch_attn_bf16<32>(a, seqs.n, max_keys, causal, rows, st);
     if (a.n_splits > 1) {
         // the merge is a kernel of its own for timing purposes
         LaunchTimer* t = launch_timer();

@@ -400,9 +400,7 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             Timed tm(m, DLM_K_ATTN_MERGE, st, false);   // handed to the split-KV merge launch
             Timed t(m, DLM_K_ATTN, st);
             AttnWork w{at<float>(ws, p.opart), at<float>(ws, p.mlpart), 0, tm.timer()};
-            // fp8 models take P V at fp32 level: their per-token quantisation of
-            // the attention output turns bf16-level differences into flipped codes
-            attention(q, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, mode == PREFILL, f32, fp8, ao, w,
+            attention(q, seqs, l, c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim, mode == PREFILL, f32, ao, w,
                       st);
         }
         quant(ao, R, qd, fp8 ? at<uint8_t>(ws, p.aoq) : nullptr, fp8 ? at<float>(ws, p.aos) : nullptr);

@@ -167,7 +167,6 @@ void rope_kv(const Partials& qkv, int rows, const SeqTab& seqs, int layer, int n
 // Attention of rows' queries (q [rows, Hq * dh]) over request r's cache slots
 // [0, T_r + per_seq): causal (prefill: key t visible to the query at position
 // p iff t <= p) or block (every key visible).  out [rows, Hq * dh].
-// p_two_terms: P enters P V as two bf16 terms (fp32-level) instead of one.
 struct AttnWork {
     float* o_part;      // split-KV partial outputs
     float* ml_part;     // split-KV partial (max, sum)
@@ -175,7 +174,7 @@ struct AttnWork {
     LaunchTimer* merge_timer;   // timer for the split-KV merge kernel (nullable)
 };
 void attention(const void* q, const SeqTab& seqs, int layer, int n_layers, int hq, int hkv,
-               int dh, bool causal, bool f32, bool p_two_terms, void* out, const AttnWork& w, hipStream_t st);
+               int dh, bool causal, bool f32, void* out, const AttnWork& w, hipStream_t st);
 long attention_work_floats(int rows, int hq, int dh);
 
 // Router: logits fp32 [rows, E] (the router GEMM's output or its split-K

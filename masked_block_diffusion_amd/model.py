@@ -138,10 +138,39 @@ class DLM:
         w = abi.dlm_weights(embed=W["embed"], final_norm=W["final_norm"], lm_head=W["lm_head"],
                             lm_head_s=W["lm_head_s"],
                             layers=ctypes.cast(self._layers, ctypes.POINTER(abi.dlm_layer_weights)))
+        self._weights = w
         h = ctypes.c_void_p()
         check(self.lib.dlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)), "dlm_create")
         self.handle = h
         self.kv_dtype = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+    def truncated(self, n_layers: int) -> "DLM":
+        """A second handle over the first `n_layers` layers of this model,
+        reading the same packed device weights (nothing is copied; this model
+        must outlive it).  Its final norm and LM head are this model's, so its
+        logits are those of the depth-`n_layers` prefix of the network.  A
+        contiguous KV cache of this model serves it unchanged (layer l sits at
+        the same offset); paged caches do not (their pages are sized for
+        every layer)."""
+        if not 1 <= n_layers <= self.cfg.n_layers:
+            raise ValueError(f"n_layers {n_layers} not in [1, {self.cfg.n_layers}]")
+        sub = DLM.__new__(DLM)
+        sub.lib, sub.C, sub.device, sub.dtype, sub.kv_dtype = self.lib, self.C, self.device, self.dtype, self.kv_dtype
+        from dataclasses import replace
+        sub.cfg = replace(self.cfg, n_layers=n_layers)
+        sub._keep = [self]
+        c = abi.dlm_config.from_buffer_copy(self.raw_cfg)
+        c.n_layers = n_layers
+        sub.raw_cfg = c
+        sub._layers = (abi.dlm_layer_weights * n_layers)(*self._layers[:n_layers])
+        w = abi.dlm_weights(embed=self._weights.embed, final_norm=self._weights.final_norm,
+                            lm_head=self._weights.lm_head, lm_head_s=self._weights.lm_head_s,
+                            layers=ctypes.cast(sub._layers, ctypes.POINTER(abi.dlm_layer_weights)))
+        sub._weights = w
+        h = ctypes.c_void_p()
+        check(self.lib.dlm_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)), "dlm_create")
+        sub.handle = h
+        return sub
 
     # ------------------------------------------------------------ weights --
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
@@ -307,26 +336,36 @@ class CanvasSteps:
     dlm_denoise_step then dlm_commit(step=s) over `seqs` with the given
     outputs, rule and workspace, captured on torch's capture stream and
     replayed with `replay(s)`.  A graph repeats its launches exactly: the
-    requests' T, cache and canvas pointers, the workspace and the outputs are
-    fixed at capture, so the graphs serve every canvas that starts with the
-    same T in the same buffers (the canvas contents and the cache values may
-    differ).  Capturing runs nothing."""
+    requests' T, cache, canvas and page-table pointers, the workspace, the
+    outputs and the rule's counts are fixed at capture, so the graphs serve
+    every canvas that starts with the same T in the same buffers (the canvas
+    contents and the cache values may differ); `valid_for` checks all of
+    them.  Capturing runs nothing."""
 
     def __init__(self, model: "DLM", seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor, rule: "Rule",
                  ws: torch.Tensor, n_committed: Optional[torch.Tensor] = None,
-                 n_masked: Optional[torch.Tensor] = None):
-        self.T = [s.T for s in seqs]
+                 n_masked: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None):
+        self.key = self._key(seqs, conf, pred, rule, ws, n_committed, n_masked, logits)
         self.graphs = []
-        self._keep = (seqs, conf, pred, rule, ws, n_committed, n_masked)
+        self._keep = (seqs, conf, pred, rule, ws, n_committed, n_masked, logits)
         for step in range(rule.n_steps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                model.dlm_denoise_step(seqs, conf, pred, ws)
+                model.dlm_denoise_step(seqs, conf, pred, ws, logits)
                 model.dlm_commit(seqs, conf, pred, rule, step, n_committed, n_masked)
             self.graphs.append(g)
 
-    def valid_for(self, seqs: Sequence[Seq]) -> bool:
-        return [s.T for s in seqs] == self.T
+    @staticmethod
+    def _key(seqs, conf, pred, rule, ws, n_committed, n_masked, logits):
+        per_seq = tuple((s.T, s.capacity, s.kv.data_ptr(), s.canvas.data_ptr(),
+                         None if s.pages is None else s.pages.data_ptr()) for s in seqs)
+        return (per_seq, conf.data_ptr(), pred.data_ptr(), ws.data_ptr(), ws.numel(), _ptr(n_committed),
+                _ptr(n_masked), _ptr(logits), rule.signature())
+
+    def valid_for(self, seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor, rule: "Rule",
+                  ws: torch.Tensor, n_committed: Optional[torch.Tensor] = None,
+                  n_masked: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None) -> bool:
+        return self.key == self._key(seqs, conf, pred, rule, ws, n_committed, n_masked, logits)
 
     def replay(self, step: int) -> None:
         self.graphs[step].replay()
@@ -346,6 +385,10 @@ class Rule:
             kind=abi.DLM_COMMIT_TOPK if kind == "topk" else abi.DLM_COMMIT_THRESHOLD,
             n_steps=n_steps, k_per_step=ctypes.cast(self._k, ctypes.POINTER(ctypes.c_int32)),
             threshold=threshold, edit_threshold=edit_threshold)
+
+    def signature(self) -> tuple:
+        """Everything a captured commit depends on."""
+        return (self.kind, self.n_steps, tuple(self._k), float(self.raw.threshold), float(self.edit_threshold))
 
     @staticmethod
     def topk(canvas: int, n_steps: int, edit_threshold: float = 0.0) -> "Rule":
@@ -367,25 +410,36 @@ class Rule:
 
 
 def generate(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], rule: Rule,
-             n_canvases: int, ws: torch.Tensor, on_step=None, graphs: Optional[dict] = None):
+             n_canvases: int, ws: torch.Tensor, on_step=None, graphs: Optional[dict] = None,
+             logits: Optional[torch.Tensor] = None):
     """Prefill each request, then for each canvas: reset to [MASK], denoise and
     commit until the schedule ends (for the threshold rule, until nothing is
     masked in any request), append.  Returns the finished canvases
     [n_canvases][n_seqs, C] (device int32) and the steps run per canvas.
 
+    `on_step(canvas_index, step, conf, pred)` sees every step after its commit
+    (the canvases then hold the step's result).  `logits` (fp32, n_seqs * C *
+    vocab): every step also writes its raw logits there, for inspection.
     `graphs`: a dict (kept by the caller across calls) turns the step loop into
     replays of per-step HIP graphs, captured on first use for each canvas
-    index (see CanvasSteps); None runs every step as direct calls."""
+    index and captured again when the requests, buffers or rule differ from
+    the ones they were captured with (see CanvasSteps); None runs every step
+    as direct calls."""
     n = len(seqs)
     C = model.C
     for s, ids in zip(seqs, prefixes):
         model.dlm_prefill(s, ids, ws)
-    conf = graphs.setdefault("conf", torch.empty(n * C, dtype=torch.float32, device=model.device)) \
-        if graphs is not None else torch.empty(n * C, dtype=torch.float32, device=model.device)
-    pred = graphs.setdefault("pred", torch.empty(n * C, dtype=torch.int32, device=model.device)) \
-        if graphs is not None else torch.empty(n * C, dtype=torch.int32, device=model.device)
-    n_masked = graphs.setdefault("n_masked", torch.empty(n, dtype=torch.int32, device=model.device)) \
-        if graphs is not None else torch.empty(n, dtype=torch.int32, device=model.device)
+
+    def buf(name, numel, dtype):
+        if graphs is None:
+            return torch.empty(numel, dtype=dtype, device=model.device)
+        t = graphs.get(name)
+        if t is None or t.numel() != numel:
+            t = graphs[name] = torch.empty(numel, dtype=dtype, device=model.device)
+        return t
+    conf = buf("conf", n * C, torch.float32)
+    pred = buf("pred", n * C, torch.int32)
+    n_masked = buf("n_masked", n, torch.int32)
     outs, steps = [], []
     for ci in range(n_canvases):
         for s in seqs:
@@ -393,14 +447,14 @@ def generate(model: DLM, seqs: Sequence[Seq], prefixes: Sequence[torch.Tensor], 
         cg = None
         if graphs is not None:
             cg = graphs.get(ci)
-            if cg is None or not cg.valid_for(seqs):
-                cg = graphs[ci] = CanvasSteps(model, seqs, conf, pred, rule, ws, None, n_masked)
+            if cg is None or not cg.valid_for(seqs, conf, pred, rule, ws, None, n_masked, logits):
+                cg = graphs[ci] = CanvasSteps(model, seqs, conf, pred, rule, ws, None, n_masked, logits)
         st = 0
         for st in range(rule.n_steps):
             if cg is not None:
                 cg.replay(st)
             else:
-                model.dlm_denoise_step(seqs, conf, pred, ws)
+                model.dlm_denoise_step(seqs, conf, pred, ws, logits)
                 model.dlm_commit(seqs, conf, pred, rule, st, None, n_masked)
             if on_step is not None:
                 on_step(ci, st, conf, pred)

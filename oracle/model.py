@@ -165,10 +165,20 @@ class StepDebug:
 
 
 class OracleModel:
+    """`perturb`: None for the model itself.  The parity tests set it to a
+    function y -> y' to measure how far the model's own outputs move when every
+    contraction result (GEMM outputs, router logits, attention outputs) carries
+    a relative error of fp32 accumulation size; it is applied before the result
+    is stored or rounded, and changes nothing else."""
+
     def __init__(self, cfg, weights: OracleWeights):
         self.cfg = cfg
         self.W = weights
         self.p = Precision(cfg.dtype)
+        self.perturb = None
+
+    def _contract(self, y: np.ndarray) -> np.ndarray:
+        return y if self.perturb is None else self.perturb(y)
 
     # -- state
     def new_seq(self, capacity: int) -> SeqState:
@@ -185,13 +195,13 @@ class OracleModel:
         y = (sum q*w_q) * s_token * s_channel (fp8)."""
         w = self.W[name] if w is None else w
         if self.cfg.dtype == "f32":
-            return x @ w.T
+            return self._contract(x @ w.T)
         a = round_bf16(x)
         if self.cfg.dtype == "bf16":
-            return a @ w.T
+            return self._contract(a @ w.T)
         s_o = self.W.scale(name) if s_out is None else s_out
         q, s_t = quant_per_token_e4m3(a)
-        return (q @ w.T) * s_t[:, None] * s_o[None, :]
+        return self._contract((q @ w.T) * s_t[:, None] * s_o[None, :])
 
     def swiglu(self, h: np.ndarray, gate: str, up: str, down: str,
                e: Optional[int] = None) -> np.ndarray:
@@ -209,7 +219,7 @@ class OracleModel:
         then the top_k experts (ties to the lower expert id), their
         probabilities renormalised to sum to 1."""
         c = self.cfg
-        r = self.p.store(h) @ self.W[f"{l}.w_router"].T            # [n, E]
+        r = self._contract(self.p.store(h) @ self.W[f"{l}.w_router"].T)   # [n, E]
         p = softmax(r)
         order = np.argsort(-p, axis=-1, kind="stable")              # ties -> lower id first
         sel = order[:, : c.top_k]
@@ -256,7 +266,7 @@ class OracleModel:
         n_keys = st.T + n
         allowed = causal_mask(pos, n_keys) if causal else block_mask(n, n_keys)
         o = attention(q.transpose(1, 0, 2), st.k[l][:, :n_keys], st.v[l][:, :n_keys], allowed)
-        o = self.p.store(o.transpose(1, 0, 2).reshape(n, c.q_dim))
+        o = self.p.store(self._contract(o.transpose(1, 0, 2).reshape(n, c.q_dim)))
         x = x + self.linear(o, p + "wo")
         h2 = rms_norm(x, self.W[p + "ffn_norm"], c.rms_eps)
         if c.ffn == "dense":

@@ -107,14 +107,16 @@ def commit(canvas, conf, pred, mask_id, run, step):
     return out, chosen
 
 
-def generate(model, run, prefix_ids, capacity=None, on_step=None):
+def generate(model, run, prefix_ids, capacity=None, on_step=None, with_state=False):
     """Prefill the prefix, then for each canvas: start all-[MASK], denoise and
     commit until the schedule ends (or, for the threshold rule, until nothing is
     masked), then append the canvas to the KV cache.
 
     Returns (list of finished canvases, list of per-canvas step counts, state).
     `on_step(canvas_index, step, canvas_before, conf, pred, canvas_after)` sees
-    every step.
+    every step; with `with_state` it also receives the request's state (its
+    cache holds the prefix and the appended canvases up to T) and the step's
+    debug record (logits, routing): on_step(..., canvas_after, state, dbg).
     """
     mask_id = model.cfg.mask_id
     st = model.new_seq(capacity or (len(prefix_ids) + run.n_canvases * run.canvas))
@@ -124,10 +126,13 @@ def generate(model, run, prefix_ids, capacity=None, on_step=None):
         canvas = np.full(run.canvas, mask_id, dtype=np.int32)
         s = 0
         for s in range(run.n_steps):
-            conf, pred, _ = model.denoise(st, canvas)
+            conf, pred, dbg = model.denoise(st, canvas, debug=with_state)
             new, _ = commit(canvas, conf, pred, mask_id, run, s)
             if on_step is not None:
-                on_step(ci, s, canvas, conf, pred, new)
+                if with_state:
+                    on_step(ci, s, canvas, conf, pred, new, st, dbg)
+                else:
+                    on_step(ci, s, canvas, conf, pred, new)
             canvas = new
             if not np.any(canvas == mask_id):
                 break

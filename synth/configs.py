@@ -39,6 +39,7 @@ class ModelConfig:
     rope_base: float = 10000.0
     init_std: float = 0.02
     router_std: Optional[float] = None   # None -> d_model ** -0.5
+    lm_head_std: Optional[float] = None  # None -> init_std; larger values give peaked confidences
 
     @property
     def q_dim(self) -> int:

@@ -1,7 +1,8 @@
 """Seeded synthetic weights and inputs.
 
 Random-init weights stand in for trained ones (the pages ship none): every matrix
-and embedding is drawn N(0, init_std); RMSNorm gains are 1; the router matrix is
+and embedding is drawn N(0, init_std) (the LM head N(0, lm_head_std) when a
+workload sets it, for confidences far from uniform); RMSNorm gains are 1; the router matrix is
 drawn N(0, d_model^-1/2) so that router logits have unit variance.  Each tensor
 has its own generator, seeded from (run seed, tensor name), so any tensor can be
 regenerated alone.  Values are drawn in fp32 and stored in the model's precision:
@@ -89,7 +90,8 @@ def make_weights(cfg: ModelConfig, seed: int = 0, device="cpu",
     out["embed"] = emb.contiguous() if cfg.dtype == "f32" else emb.to(torch.bfloat16).contiguous()
     del emb
     out["final_norm"] = torch.ones(d, dtype=torch.float32, device=device)
-    _store(out, "lm_head", normal(seed, "lm_head", (cfg.vocab, d), std, device),
+    lm_std = std if cfg.lm_head_std is None else cfg.lm_head_std
+    _store(out, "lm_head", normal(seed, "lm_head", (cfg.vocab, d), lm_std, device),
            cfg.dtype, projection=True)
     for l in (range(cfg.n_layers) if layers is None else layers):
         p = f"{l}."

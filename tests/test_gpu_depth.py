@@ -1,0 +1,211 @@
+"""Parity at depth: the 26B-class MoE at full width (d = 2560, 128 experts
+top-8 x 768 + shared 2048, vocab 262144) through all 32 of its layers
+("DiffusionGemma: 4x Faster Text Generation via Parallel Diffusion",
+"Parallel Generation and Hardware Efficiency": the 26B MoE), free running:
+the GPU's own prefill, its own first denoising step, its own append and the
+first step of the next canvas.
+
+The oracle cannot hold 26B weights in float64, so it streams them: layer by
+layer, the tensors the GPU drew are copied to the host in float64 and dropped
+after use (the embedding stays float32, exact for its bf16 values; rows are
+gathered and widened).  Both passes over the stack run layer
+by layer -- pass 1: the prompt's causal prefill, then the first step of canvas
+0 on it; pass 2: the append of canvas 0, then the first step of canvas 1 --
+each exactly and perturbed at fp32 level (tests/parity.py), so the decision
+and logit bands cover the whole free run.  The prompt is 256 tokens, which
+keeps the float64 prefill to seconds per layer; the 4096-token prompt runs at
+full width in tests/test_gpu_fullsize.py.  Canvas 0 is finished with the
+oracle's depth-32 predictions before the append (on both sides).
+
+Reported and checked per depth (2, 8, 16, 32; the GPU's shallower logits come
+from handles over the model's first layers, DLM.truncated): the largest
+logit difference relative to max|logit| against the bar of tests/parity.py
+(LOGIT_TOL, or the conditioning bar where the oracle itself moves further),
+router flips only at near-ties, and every layer's new KV slots (prefill and
+append) within LOGIT_TOL of the largest oracle value of that layer and kind."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.model import NEG_INF, OracleModel, SeqState, StepDebug
+from tests.parity import LOGIT_TOL, StepReport, compare_logits, logit_bar, oracle_bands, perturbed, router_exemptions
+
+pytestmark = pytest.mark.gpu
+
+DEPTHS = (2, 8, 16, 32)
+PROMPT = 256
+
+
+class StreamedWeights:
+    """OracleWeights over GPU tensors, one layer at a time: `load(l)` copies
+    layer l's tensors to the host in float64, `drop(l)` releases them.  The
+    global tensors stay loaded (the embedding as float32, exact for its bf16
+    values)."""
+
+    def __init__(self, cfg, gpu: dict):
+        self.cfg, self.gpu = cfg, gpu
+        self.w = {k: (v.float().cpu().numpy() if k == "embed" else self._host(v))
+                  for k, v in gpu.items() if not k.split(".", 1)[0].isdigit()}
+
+    @staticmethod
+    def _host(t):
+        return t.to(torch.float64).cpu().numpy()
+
+    def load(self, l):
+        for k, v in self.gpu.items():
+            if k.startswith(f"{l}."):
+                self.w[k] = self._host(v)
+
+    def drop(self, l):
+        for k in [k for k in self.w if k.startswith(f"{l}.")]:
+            del self.w[k]
+
+    def __getitem__(self, name):
+        return self.w[name]
+
+    def scale(self, name):
+        return None
+
+
+def _logits(om, x, mask_id):
+    lg = om.logits(x)
+    lg[:, mask_id] = NEG_INF
+    return lg
+
+
+def _conf_pred(lg):
+    m = lg.max(axis=-1)
+    return 1.0 / np.exp(lg - m[:, None]).sum(axis=-1), np.argmax(lg, axis=-1).astype(np.int32)
+
+
+def test_moe_full_width_all_layers():
+    from masked_block_diffusion_amd import DLM
+    run = synth.get_run("moe")
+    run = replace(run, prefix_len=(PROMPT, PROMPT), n_canvases=2)
+    cfg, C, L = run.model, run.canvas, run.model.n_layers
+    print(f"[depth] moe full width, {L} layers, prompt {PROMPT}, canvas {C}", flush=True)
+    w = synth.make_weights(cfg, seed=run.seed, device="cuda")
+    gm = DLM(cfg, w, canvas=C)
+    subs = {k: gm.truncated(k) for k in DEPTHS if k < L}
+    subs[L] = gm
+    prompt = synth.make_inputs(run)[0]
+    cap = run.capacity()
+    seq = gm.new_seq(cap)
+    ws = gm.workspace(max(C, PROMPT), cap)
+    conf = torch.empty(C, dtype=torch.float32, device="cuda")
+    pred = torch.empty(C, dtype=torch.int32, device="cuda")
+    logits = torch.empty(C * cfg.vocab, dtype=torch.float32, device="cuda")
+    rdbg = torch.empty(L * max(C, PROMPT) * cfg.top_k, dtype=torch.int32, device="cuda")
+    rlog = torch.empty(L * max(C, PROMPT) * cfg.n_experts, dtype=torch.float32, device="cuda")
+    gm.dlm_debug_router(rdbg, rlog, L * max(C, PROMPT))
+
+    def gpu_step():
+        out = {}
+        for k in sorted(subs):            # the full model last: its routing stays in the debug buffers
+            subs[k].dlm_denoise_step([seq], conf, pred, ws, logits)
+            torch.cuda.synchronize()
+            out[k] = logits.view(C, cfg.vocab).cpu().numpy()
+        out["rsets"] = rdbg[:L * C * cfg.top_k].view(L, C, cfg.top_k).cpu().numpy()
+        out["rlog"] = rlog[:L * C * cfg.n_experts].view(L, C, cfg.n_experts).cpu().numpy().astype(np.float64)
+        return out
+
+    gm.dlm_prefill(seq, prompt.cuda(), ws)
+    seq.canvas.fill_(cfg.mask_id)
+    g0 = gpu_step()
+
+    # the oracle, streamed: exact and perturbed states side by side
+    W = StreamedWeights(cfg, w)
+    om = OracleModel(cfg, W)
+    shape = (cfg.n_kv_heads, cap, cfg.head_dim)
+    st = {s: SeqState([np.zeros(shape) for _ in range(L)], [np.zeros(shape) for _ in range(L)], 0)
+          for s in ("exact", "noisy")}
+
+    def sweep(first_ids, first_causal, canvas, seed):
+        """One pass over the stack: rows `first_ids` (the prompt, causal, or the
+        finished canvas, block mask) written into the cache, then the canvas
+        `canvas` denoised on top; exact and perturbed.  Returns per depth the
+        (conf, pred, StepDebug) of both."""
+        xs = {s: W["embed"][np.asarray(first_ids, dtype=np.int64)].astype(np.float64) for s in st}
+        ys = {s: W["embed"][canvas.astype(np.int64)].astype(np.float64) for s in st}
+        dbg = {s: StepDebug() for s in st}
+        T0 = st["exact"].T
+        out = {}
+        for l in range(L):
+            W.load(l)
+            for s in st:
+                ctx = perturbed(om, seed=seed + l) if s == "noisy" else None
+                if ctx:
+                    ctx.__enter__()
+                try:
+                    st[s].T = T0
+                    xs[s] = om.layer(l, xs[s], st[s], first_causal)
+                    st[s].T = T0 + len(first_ids)
+                    ys[s] = om.layer(l, ys[s], st[s], False, dbg[s])
+                finally:
+                    if ctx:
+                        ctx.__exit__(None, None, None)
+            W.drop(l)
+            if l + 1 in DEPTHS:
+                res = {}
+                for s in st:
+                    with (perturbed(om, seed=seed + 100 + l) if s == "noisy" else _null()):
+                        lg = _logits(om, ys[s], cfg.mask_id)
+                    c, p = _conf_pred(lg)
+                    d = StepDebug(lg, list(dbg[s].router_sets), list(dbg[s].router_gap), list(dbg[s].router_logits))
+                    res[s] = (c, p, d)
+                out[l + 1] = res
+                print(f"[depth] oracle through layer {l + 1}", flush=True)
+        for s in st:
+            st[s].T = T0 + len(first_ids)
+        return out
+
+    def compare(g, o, what):
+        worst = {}
+        for k in DEPTHS:
+            ex_, no_ = o[k]["exact"], o[k]["noisy"]
+            masked = np.ones(C, dtype=bool)
+            bands = oracle_bands(cfg.mask_id, masked, ex_, no_)
+            rep = StepReport()
+            rows = router_exemptions(g["rsets"][:k], g["rlog"][:k], ex_[2], bands, cfg.dtype, rep)
+            compare_logits(g[k], ex_[2].logits, cfg.mask_id, cfg.dtype, rep, rows, bands)
+            print(f"[depth] {what} depth {k}: max rel logit err {rep.logit_err / rep.logit_scale:.4g} "
+                  f"(oracle's own move {bands.delta_logit_rel:.4g}, bar {logit_bar(cfg.dtype, bands):.3g}), "
+                  f"router-exempt rows {len(rows)}/{C}, decisive router flips {rep.router_flips_decisive}",
+                  flush=True)
+            assert not rep.problems, f"{what} depth {k}: {rep.problems}"
+            worst[k] = rep.logit_err / rep.logit_scale
+        return worst
+
+    o0 = sweep(prompt.numpy(), True, np.full(C, cfg.mask_id, dtype=np.int32), seed=1)
+    kv_worst = 0.0
+    from tests.lockstep import kv_check
+    kv_worst = max(kv_worst, kv_check(seq, st["exact"], 0, PROMPT, cfg.dtype, "prefill"))
+    e0 = compare(g0, o0, "canvas 0 step 0 (own prefill)")
+
+    # finish canvas 0 with the oracle's depth-32 predictions; append on both sides
+    finished = o0[L]["exact"][1].astype(np.int32)
+    seq.canvas.copy_(torch.from_numpy(finished))
+    gm.dlm_append_canvas([seq], ws)
+    seq.canvas.fill_(cfg.mask_id)
+    g1 = gpu_step()
+    o1 = sweep(finished, False, np.full(C, cfg.mask_id, dtype=np.int32), seed=1000)
+    kv_worst = max(kv_worst, kv_check(seq, st["exact"], PROMPT, PROMPT + C, cfg.dtype, "append"))
+    e1 = compare(g1, o1, "canvas 1 step 0 (own append)")
+    assert gm.dlm_check_device_status() == 0
+    print(f"[depth] max rel logit err by depth, canvas 0: {e0}; canvas 1: {e1}; KV max|d| / bound {kv_worst:.3g}",
+          flush=True)
+    for s in subs.values():
+        if s is not gm:
+            s.close()
+    gm.close()
+
+
+class _null:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False

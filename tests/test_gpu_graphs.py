@@ -96,3 +96,27 @@ def test_generate_with_graphs_matches_direct():
             assert torch.equal(a, b), f"pass {rep} canvas {ci} differs"
     assert sorted(k for k in cache if isinstance(k, int)) == list(range(run.n_canvases))
     gm.close()
+
+
+def test_graph_cache_recaptures_for_new_requests():
+    """A graph cache kept across calls and handed fresh requests (same T, other
+    canvases and caches) or another rule must not replay the old buffers: the
+    results equal direct calls on the new requests."""
+    from masked_block_diffusion_amd import Rule, generate
+    run, gm, seqs, prefixes, ws, rule = _setup("dense-mini")
+    cache = {}
+    for s in seqs:
+        s.raw.T = 0
+    generate(gm, seqs, prefixes, rule, 1, ws, graphs=cache)
+    fresh = [gm.new_seq(run.capacity()) for _ in seqs]
+    ref, _ = generate(gm, [gm.new_seq(run.capacity()) for _ in seqs], prefixes, rule, 1, ws)
+    out, _ = generate(gm, fresh, prefixes, rule, 1, ws, graphs=cache)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], ref[0])
+    other = Rule.topk(run.canvas, run.n_steps // 2)
+    ref2, _ = generate(gm, [gm.new_seq(run.capacity()) for _ in seqs], prefixes, other, 1, ws)
+    out2, _ = generate(gm, [gm.new_seq(run.capacity()) for _ in seqs], prefixes, other, 1, ws, graphs=cache)
+    torch.cuda.synchronize()
+    assert torch.equal(out2[0], ref2[0])
+    assert gm.dlm_check_device_status() == 0
+    gm.close()

@@ -355,20 +355,26 @@ def test_canvas_is_bidirectional_and_cache_is_untouched():
 
 
 def test_denoise_conf_pred_hand_built():
+    """OracleModel.denoise itself on a hand-built head: the prediction and the
+    confidence exclude [MASK] (whose logit is made the largest), ties go to the
+    lower id, and conf = 1 / sum exp(l - max) over the remaining vocabulary."""
     cfg = _tiny_cfg(vocab=4, mask_id=3)
     m = _model(cfg)
-    # replace the head so logits are a known function of the final hidden state
+    # the transformer is bypassed so the final hidden state is known: row 0 is
+    # e_0, row 1 is e_1; the head makes the logits a known function of it
     x = np.zeros((2, cfg.d_model)); x[0, 0] = 1.0; x[1, 1] = 1.0
     hn = rms_norm(x, m.W["final_norm"], cfg.rms_eps)
     scale = hn[0, 0]
     m.W.w["lm_head"] = np.zeros((4, cfg.d_model))
-    m.W.w["lm_head"][1, 0] = np.log(3.0) / scale    # row 0: logits [0, log3, 0, 0(mask)]
+    m.W.w["lm_head"][1, 0] = np.log(3.0) / scale    # row 0: logits [0, log3, 0, 10 (mask)]
     m.W.w["lm_head"][3, 0] = 10.0 / scale           # mask logit largest: must be ignored
-    m.W.w["lm_head"][0, 1] = 1.0 / scale            # row 1: logits [1, 0, 1, 0] -> tie 0/2
+    m.W.w["lm_head"][0, 1] = 1.0 / scale            # row 1: logits [1, 0, 1, 0 (mask)] -> tie 0/2
     m.W.w["lm_head"][2, 1] = 1.0 / scale
-    lg = m.logits(x)
-    lg[:, 3] = -np.inf
-    pred = np.argmax(lg, axis=-1)
+    m.forward = lambda ids, st, causal, dbg=None: x.copy()
+    st = m.new_seq(8)
+    conf, pred, dbg = m.denoise(st, np.full(2, cfg.mask_id), debug=True)
     assert pred.tolist() == [1, 0]
-    z = np.exp(lg - lg.max(-1, keepdims=True)).sum(-1)
-    np.testing.assert_allclose(1 / z, [3 / 5, np.e / (2 * np.e + 1)], rtol=1e-12)
+    np.testing.assert_allclose(conf, [3 / 5, np.e / (2 * np.e + 1)], rtol=1e-12)
+    assert np.all(np.isneginf(dbg.logits[:, 3]))
+    # a confidence taken over the whole vocabulary (mask included) would differ
+    assert abs(conf[0] - 3 / (5 + np.exp(10.0))) > 0.5
