@@ -39,7 +39,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-from .numerics import e4m3_decode, quant_per_token_e4m3, round_bf16
+from .numerics import e4m3_decode, mxfp4_decode, quant_per_token_e4m3, round_bf16
 
 NEG_INF = -np.inf
 
@@ -123,6 +123,13 @@ class OracleWeights:
                 self.w[base] = e4m3_decode(t.detach().cpu().numpy())
             elif name.endswith(".s"):
                 self.s[name[:-2]] = t.detach().to("cpu", torch.float64).numpy()
+            elif name.endswith(".q4"):
+                # MXFP4: two E2M1 codes per byte (element 2i low nibble), E8M0 block scales
+                packed = t.detach().cpu().numpy()
+                codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(*packed.shape[:-1], -1)
+                self.w[name[:-3]] = mxfp4_decode(codes, tensors[name[:-3] + ".e8"].detach().cpu().numpy())
+            elif name.endswith(".e8"):
+                pass
             else:
                 self.w[name] = t.detach().to("cpu", torch.float64).numpy()
 
@@ -283,10 +290,10 @@ class OracleModel:
         return x
 
     # -- the four operations
-    def prefill(self, st: SeqState, ids: np.ndarray) -> None:
+    def prefill(self, st: SeqState, ids: np.ndarray, dbg: Optional[StepDebug] = None) -> None:
         """Causal forward over ids at positions [T, T+n); K/V cached; T += n.
-        No LM head."""
-        self.forward(ids, st, causal=True)
+        No LM head.  `dbg` (optional) records the routing of every layer."""
+        self.forward(ids, st, causal=True, dbg=dbg)
         st.T += len(ids)
 
     def logits(self, x: np.ndarray) -> np.ndarray:
@@ -314,8 +321,9 @@ class OracleModel:
             dbg.logits = lg
         return conf, pred, dbg
 
-    def append(self, st: SeqState, canvas: np.ndarray) -> None:
+    def append(self, st: SeqState, canvas: np.ndarray, dbg: Optional[StepDebug] = None) -> None:
         """Forward over the finished canvas with the denoising mask, writing its
-        K/V at [T, T+C); then T += C.  No LM head."""
-        self.forward(canvas, st, causal=False)
+        K/V at [T, T+C); then T += C.  No LM head.  `dbg` (optional) records
+        the routing of every layer."""
+        self.forward(canvas, st, causal=False, dbg=dbg)
         st.T += len(canvas)

@@ -25,17 +25,27 @@ E4M3_MAX = 448.0
 def round_bf16(x) -> np.ndarray:
     """Round to the nearest bfloat16 value, ties to even (8 significant bits,
     exponent range of fp32, subnormals kept, overflow to +-inf)."""
-    x = np.asarray(x, dtype=np.float64)
-    finite = np.isfinite(x) & (x != 0)
-    out = x.copy()
-    xf = x[finite]
-    _, e = np.frexp(xf)                 # xf = m * 2**e, 0.5 <= |m| < 1
-    e = np.maximum(e, -125)             # below 2**-126 the spacing stays 2**-133
-    ulp = np.ldexp(1.0, e - 8)
-    r = np.round(xf / ulp) * ulp        # np.round: half to even; xf/ulp is exact
-    r[np.abs(r) > BF16_MAX] = np.inf * np.sign(r[np.abs(r) > BF16_MAX])
-    out[finite] = r
-    return out
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    # bf16's normal range: keep the 8 leading significant bits of the float64
+    # value (1 implicit + 7 of its 52 fraction bits) and round the 45 bits below
+    # them to nearest, ties to the even kept pattern; a carry out of the
+    # fraction moves the exponent up, as rounding does
+    b = x.view(np.uint64)
+    rb = b >> np.uint64(45)
+    rb &= np.uint64(1)
+    rb += np.uint64((1 << 44) - 1)
+    rb += b
+    rb &= ~np.uint64((1 << 45) - 1)
+    r = rb.view(np.float64)
+    ax = np.abs(x)
+    if not (np.isfinite(ax).all() and ax.max(initial=0.0) < BF16_MAX and
+            ax[ax != 0].min(initial=np.inf) >= 2.0 ** -126):
+        r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, x), r)
+        # below 2**-126 bf16 values are multiples of 2**-133 (scaling by 2**133 is exact)
+        tiny = ax < 2.0 ** -126
+        r = np.where(tiny, np.round(x * 2.0 ** 133) * 2.0 ** -133, r)
+        r = np.where(np.isfinite(x), r, x)
+    return r
 
 
 def e4m3_decode_table() -> np.ndarray:
@@ -109,3 +119,79 @@ def quant_per_token_e4m3(x):
     quot = (x32 / s[..., None]).astype(np.float32)
     q = e4m3_round(quot.astype(np.float64))
     return q, s.astype(np.float64)
+
+
+# ----------------------------------------------------------------- MXFP4 --
+# OCP Microscaling Formats (MX) v1.0: an MXFP4 block is 32 consecutive
+# elements in FP4 E2M1 sharing one E8M0 scale.  The pages name a 4-bit weight
+# format for the 26B model's deployment ("DiffusionGemma: 4x Faster Text
+# Generation via Parallel Diffusion", "Deployment and Tooling"); MXFP4 is the
+# 4-bit block format of this hardware's matrix cores.
+
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+E2M1_EMAX = 2          # exponent of the largest normal E2M1 value (6 = 1.5 * 2^2)
+
+
+def e2m1_decode_table() -> np.ndarray:
+    """Value of each of the 16 E2M1 codes: sign bit 3, exponent bits 2..1 with
+    bias 1, mantissa bit 0; exponent field 0 holds the subnormal m * 0.5; no
+    infinity or NaN."""
+    vals = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        s = -1.0 if code & 8 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        vals[code] = s * (0.5 * m if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1))
+    return vals
+
+
+_E2M1_TABLE = e2m1_decode_table()
+
+
+def e8m0_decode(e) -> np.ndarray:
+    """E8M0 scale code: 2^(e - 127); the code 255 is NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+
+
+def e2m1_round(x) -> np.ndarray:
+    """Nearest E2M1 value, ties to the even mantissa, saturating at +-6.  The
+    representable magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6} lie on a grid of
+    spacing 0.5 below 2, 1 in [2, 4) and 2 in [4, 6]; on each grid the even
+    multiples are exactly the codes with an even mantissa."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -E2M1_MAX, E2M1_MAX)
+    a = np.abs(x)
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    return np.copysign(np.round(a / step) * step, x)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Codes of e2m1_round(x) (zero keeps the sign of x)."""
+    v = e2m1_round(x)
+    idx = np.searchsorted(_E2M1_TABLE[:8], np.abs(v))
+    return np.where(np.signbit(v), idx | 8, idx).astype(np.uint8)
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """MXFP4 quantisation of the last axis (a multiple of 32): per block of 32
+    the shared exponent is floor(log2(max |w|)) - 2, clamped to E8M0's
+    [-127, 127] (an all-zero block takes exponent 0), and each element is
+    e2m1_round(w / 2^exponent).  Returns (E2M1 codes uint8 with w's shape,
+    E8M0 scale codes uint8 [..., K / 32])."""
+    w = np.asarray(w, dtype=np.float64)
+    blocks = w.reshape(*w.shape[:-1], w.shape[-1] // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))       # amax = f * 2^e, 0.5 <= f < 1
+    shared = np.where(amax > 0, e - 1 - E2M1_EMAX, 0)     # floor(log2 amax) = e - 1
+    shared = np.clip(shared, -127, 127)
+    codes = e2m1_encode(blocks / np.ldexp(1.0, shared)[..., None])
+    return codes.reshape(w.shape), (shared + 127).astype(np.uint8)
+
+
+def mxfp4_decode(codes, scales) -> np.ndarray:
+    """Values of MXFP4 data: E2M1 codes [..., K] times their blocks' E8M0 scales
+    [..., K / 32]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    v = _E2M1_TABLE[codes]
+    s = e8m0_decode(scales)
+    return (v.reshape(*v.shape[:-1], -1, MX_BLOCK) * s[..., None]).reshape(v.shape)

@@ -40,6 +40,7 @@ class ModelConfig:
     init_std: float = 0.02
     router_std: Optional[float] = None   # None -> d_model ** -0.5
     lm_head_std: Optional[float] = None  # None -> init_std; larger values give peaked confidences
+    expert_dtype: Optional[str] = None   # MoE experts' storage when it differs from dtype: "mxfp4"
 
     @property
     def q_dim(self) -> int:

@@ -56,9 +56,41 @@ def quantize_e4m3_rows(w: torch.Tensor):
     return q.view(torch.uint8), s.contiguous()
 
 
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)    # codes 0..7; bit 3 is the sign
+
+
+def quantize_mxfp4_rows(w: torch.Tensor):
+    """MXFP4 (OCP Microscaling v1.0) quantisation along the last axis, a
+    multiple of 32: each block of 32 shares the E8M0 exponent floor(log2 max|w|)
+    - 2 (clamped to [-127, 127]; 0 for an all-zero block) and each element is
+    w / 2^exponent rounded to the nearest E2M1 value, ties to the even
+    mantissa, saturating at +-6.
+
+    Returns (codes uint8 [..., K / 2], two E2M1 codes per byte, element 2i in
+    the low nibble and 2i + 1 in the high one; scales uint8 [..., K / 32],
+    the E8M0 codes exponent + 127)."""
+    blocks = w.float().reshape(*w.shape[:-1], w.shape[-1] // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, e = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))   # amax = m * 2^e, m in [0.5, 1)
+    shared = torch.where(amax > 0, e - 3, torch.zeros_like(e)).clamp_(-127, 127)
+    x = torch.ldexp(blocks, -shared.unsqueeze(-1).float())
+    a = x.abs().clamp_(max=6.0)
+    step = torch.where(a < 2.0, 0.5, torch.where(a < 4.0, 1.0, 2.0))
+    r = torch.round(a / step) * step                                          # half to even on each grid
+    mags = torch.tensor(E2M1_MAGNITUDES, dtype=r.dtype, device=r.device)
+    codes = torch.bucketize(r, mags).to(torch.uint8) | (torch.signbit(x).to(torch.uint8) << 3)
+    codes = codes.reshape(w.shape)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), (shared + 127).to(torch.uint8).contiguous()
+
+
 def _store(out: Dict[str, torch.Tensor], name: str, w: torch.Tensor, dtype: str,
            projection: bool):
-    if dtype == "f32":
+    if dtype == "mxfp4":
+        q, e = quantize_mxfp4_rows(w)
+        out[name + ".q4"] = q
+        out[name + ".e8"] = e
+    elif dtype == "f32":
         out[name] = w.contiguous()
     elif dtype == "bf16" or not projection:
         out[name] = w.to(torch.bfloat16).contiguous()
@@ -106,8 +138,8 @@ def make_weights(cfg: ModelConfig, seed: int = 0, device="cpu",
             E, de = cfg.n_experts, cfg.d_expert
             shapes.update({"we_gate": (E, de, d), "we_up": (E, de, d), "we_down": (E, d, de)})
         for name, shape in shapes.items():
-            _store(out, p + name, normal(seed, p + name, shape, std, device), cfg.dtype,
-                   projection=True)
+            dt = cfg.expert_dtype if (name.startswith("we_") and cfg.expert_dtype) else cfg.dtype
+            _store(out, p + name, normal(seed, p + name, shape, std, device), dt, projection=True)
         if cfg.ffn == "moe":
             wr = normal(seed, p + "w_router", (cfg.n_experts, d), cfg.router_sigma, device)
             out[p + "w_router"] = wr.contiguous() if cfg.dtype == "f32" else wr.to(torch.bfloat16).contiguous()

@@ -12,7 +12,12 @@ Prefill and append are checked element by element twice: the new KV slots
 oracle value of that layer and kind, and through the logits -- the first step
 of every canvas is also run on the GPU's own cache (its own prefill for the
 first canvas, its own append for the next ones) and its logits compared with
-the oracle's like any step's.
+the oracle's like any step's.  For MoE models the routing of the prefill and
+append forwards is compared too (every token, every layer that feeds the
+cache): a token re-routed at a router near-tie is left out of the KV check
+above the layer of the flip; any other routing difference fails.  Their bands
+are those of the first step of the canvas (prefill) and of its last step
+(append): the same model and layers, measured on the canvas rows.
 
 `max_steps` stops a canvas early: both sides then fill its remaining masked
 positions with the oracle's predictions, so the append is still compared.
@@ -26,31 +31,55 @@ the commit kernel applies the rule exactly to the GPU's own confidences, only
 `caps` bounds the exempt fractions ({"rank", "token", "router_rows"}); the
 fractions are printed either way.
 """
+from dataclasses import replace
+
 import numpy as np
 import torch
 
 import synth
 from oracle import sampler as osampler
-from oracle.model import OracleModel, OracleWeights
-from tests.parity import (LOGIT_TOL, StepReport, compare_commit, compare_logits, oracle_bands, perturbed,
-                          router_exemptions)
+from oracle.model import OracleModel, OracleWeights, StepDebug
+from tests.parity import LOGIT_TOL, StepReport, compare_commit, compare_logits, router_exemptions, step_bands
+from tests.progress import progress
 
 
-def kv_check(gseq, ost, lo, hi, dtype, what):
+def kv_check(gseq, ost, lo, hi, dtype, what, skip=None):
     """GPU cache slots [lo, hi) of every layer against the oracle's: max |d|
     per layer and kind (keys, values) within LOGIT_TOL of the largest oracle
-    value of that layer and kind.  Returns the worst ratio to the bound."""
+    value of that layer and kind.  `skip` maps a slot (relative to lo) to the
+    layer where its token was re-routed at a router near-tie: its K/V are
+    compared up to that layer (they are computed before the layer's experts)
+    and not above.  Returns the worst ratio to the bound."""
     g = [t.float().cpu().numpy() for t in gseq.read_kv()]
     worst = 0.0
+    skip = skip or {}
     for l in range(g[0].shape[0]):
+        keep = np.array([t for t in range(hi - lo) if skip.get(t, l) >= l], dtype=np.int64)
+        if keep.size == 0:
+            continue
         for kind, ref in ((0, ost.k[l]), (1, ost.v[l])):
-            o = ref[:, lo:hi]
-            d = float(np.max(np.abs(g[kind][l, :, lo:hi] - o)))
+            o = ref[:, lo:hi][:, keep]
+            d = float(np.max(np.abs(g[kind][l, :, lo:hi][:, keep] - o)))
             bound = LOGIT_TOL[dtype] * float(np.max(np.abs(o)))
             assert d <= bound, (f"{what}: layer {l} {'KV'[kind]} max|d| {d:.4g} > {LOGIT_TOL[dtype]} * "
                                 f"max|ref| = {bound:.4g}")
             worst = max(worst, d / max(bound, 1e-30))
     return worst
+
+
+def cache_routing_flips(gpu_sets, gpu_logits, odbg, bands, dtype, what):
+    """Routing of a prefill or append forward (GPU [L, rows, k] / [L, rows, E]
+    against the oracle's StepDebug of the same forward) over the layers whose
+    experts feed the cache -- all but the last, which the library skips there.
+    Returns {row: layer of its near-tie flip}; fails on any other difference."""
+    L = len(odbg.router_sets) - 1
+    if L <= 0:
+        return {}
+    sub = StepDebug(None, odbg.router_sets[:L], odbg.router_gap[:L], odbg.router_logits[:L])
+    rep = StepReport()
+    flips = router_exemptions(gpu_sets[:L], gpu_logits[:L], sub, replace(bands, noisy_flips=[]), dtype, rep)
+    assert not rep.problems, f"{what}: {rep.problems[:5]}"
+    return flips
 
 
 def load_cache(gseq, ost):
@@ -66,10 +95,11 @@ def lockstep(run, label, max_steps=None, sample=None, weights=None, paged=False,
     from masked_block_diffusion_amd import DLM, KVPool, Rule
 
     cfg = run.model
+    L = cfg.n_layers
     C, n = run.canvas, run.n_requests
     sample = list(range(n)) if sample is None else list(sample)
     steps = run.n_steps if max_steps is None else min(run.n_steps, max_steps)
-    print(f"[parity] run={label} dtype={cfg.dtype} ffn={cfg.ffn} L={cfg.n_layers} d={cfg.d_model} "
+    print(f"[parity] run={label} dtype={cfg.dtype} ffn={cfg.ffn} L={L} d={cfg.d_model} "
           f"V={cfg.vocab} C={C} requests={n} sampled={sample} steps/canvas={steps} paged={paged}", flush=True)
     w = synth.make_weights(cfg, seed=run.seed) if weights is None else weights
     om = OracleModel(cfg, OracleWeights(cfg, w))
@@ -85,16 +115,31 @@ def lockstep(run, label, max_steps=None, sample=None, weights=None, paged=False,
         gseqs = [gm.new_seq(cap, pool, order=lambda nf: int(rng.integers(nf))) for _ in range(n)]
     else:
         gseqs = [gm.new_seq(cap) for _ in range(n)]
-    ws = gm.workspace(max(n * C, max(len(p) for p in prefixes)), cap)
+    rows_cap = max(n * C, max(len(p) for p in prefixes))
+    ws = gm.workspace(rows_cap, cap)
+    moe = cfg.ffn == "moe"
+    rdbg = torch.empty(L * rows_cap * max(cfg.top_k, 1), dtype=torch.int32, device="cuda") if moe else None
+    rlog = torch.empty(L * rows_cap * max(cfg.n_experts, 1), dtype=torch.float32, device="cuda") if moe else None
+    gm.dlm_debug_router(rdbg, rlog, L * rows_cap)
+
+    def routing(rows):
+        """The last forward's routing: ([L, rows, k], [L, rows, E])."""
+        torch.cuda.synchronize()
+        return (rdbg[:L * rows * cfg.top_k].view(L, rows, cfg.top_k).cpu().numpy(),
+                rlog[:L * rows * cfg.n_experts].view(L, rows, cfg.n_experts).cpu().numpy().astype(np.float64))
+
+    pre_dbg, pre_route = {}, {}
     for r in range(n):
+        progress(f"[parity] {label}: prefill request {r} ({len(prefixes[r])} tokens)")
         if r in ost:
-            om.prefill(ost[r], prefixes[r].numpy())
+            pre_dbg[r] = StepDebug() if moe else None
+            om.prefill(ost[r], prefixes[r].numpy(), pre_dbg[r])
         gm.dlm_prefill(gseqs[r], prefixes[r].cuda(), ws)
+        if moe and r in ost:
+            pre_route[r] = routing(len(prefixes[r]))
     torch.cuda.synchronize()
-    kv_worst = 0.0
     for r in sample:
         assert gseqs[r].T == ost[r].T
-        kv_worst = max(kv_worst, kv_check(gseqs[r], ost[r], 0, ost[r].T, cfg.dtype, f"prefill request {r}"))
 
     rule = Rule.for_run(run)
     sched = osampler.topk_schedule(C, run.n_steps)
@@ -103,34 +148,38 @@ def lockstep(run, label, max_steps=None, sample=None, weights=None, paged=False,
     logits = torch.empty(n * C * cfg.vocab, dtype=torch.float32, device="cuda")
     ncom = torch.empty(n, dtype=torch.int32, device="cuda")
     nmask = torch.empty(n, dtype=torch.int32, device="cuda")
-    moe = cfg.ffn == "moe"
-    rdbg = torch.empty(cfg.n_layers * n * C * max(cfg.top_k, 1), dtype=torch.int32, device="cuda") if moe else None
-    rlog = torch.empty(cfg.n_layers * n * C * max(cfg.n_experts, 1), dtype=torch.float32,
-                       device="cuda") if moe else None
-    gm.dlm_debug_router(rdbg, rlog, cfg.n_layers * n * C)
     totals = StepReport()
     own_err = 0.0
+    kv_worst = 0.0
+    cache_flips = 0
 
     def router_views(r):
         if not moe:
             return None, None
-        return (rdbg.view(cfg.n_layers, n, C, cfg.top_k)[:, r].cpu().numpy(),
-                rlog.view(cfg.n_layers, n, C, cfg.n_experts)[:, r].cpu().numpy().astype(np.float64))
+        sets, lgs = routing(n * C)
+        return sets.reshape(L, n, C, -1)[:, r], lgs.reshape(L, n, C, -1)[:, r]
 
     for ci in range(run.n_canvases):
         canv = {r: np.full(C, cfg.mask_id, dtype=np.int32) for r in sample}
         for s in gseqs:
             s.canvas.fill_(cfg.mask_id)
-        last_pred = {}
+        last_pred, bands = {}, {}
         for step in range(steps):
+            progress(f"[parity] {label}: canvas {ci} step {step}")
             outs = {r: om.denoise(ost[r], canv[r], debug=True) for r in sample}
-            bands = {}
             for r in sample:
-                with perturbed(om, seed=1000 * ci + 10 * step + r):
-                    noisy = om.denoise(ost[r], canv[r], debug=True)
-                bands[r] = oracle_bands(cfg.mask_id, canv[r] == cfg.mask_id, outs[r], noisy)
-                del noisy
+                bands[r] = step_bands(om, ost[r], canv[r], outs[r], seed=100000 * ci + 100 * step + 10 * r)
             new = {r: osampler.commit(canv[r], outs[r][0], outs[r][1], cfg.mask_id, run, step)[0] for r in sample}
+            if ci == 0 and step == 0:
+                # the GPU's own prefill, element by element (now that bands exist)
+                for r in sample:
+                    skip = {}
+                    if moe:
+                        skip = cache_routing_flips(*pre_route[r], pre_dbg[r], bands[r], cfg.dtype,
+                                                   f"prefill routing, request {r}")
+                    cache_flips += len(skip)
+                    kv_worst = max(kv_worst, kv_check(gseqs[r], ost[r], 0, ost[r].T, cfg.dtype,
+                                                      f"prefill request {r}", skip))
             for r in sample:
                 gseqs[r].canvas.copy_(torch.from_numpy(canv[r]))
             if step == 0:
@@ -186,28 +235,37 @@ def lockstep(run, label, max_steps=None, sample=None, weights=None, paged=False,
                 break
         if steps == run.n_steps:
             assert not any(np.any(c == cfg.mask_id) for c in canv.values()), "masked positions left after the schedule"
+        app_dbg = {}
         for r in range(n):
             if r in canv:
                 c = canv[r]
                 c[c == cfg.mask_id] = last_pred[r][c == cfg.mask_id]       # stopped early: fill like the oracle
                 gseqs[r].canvas.copy_(torch.from_numpy(c))
                 load_cache(gseqs[r], ost[r])
-                om.append(ost[r], c)
+                app_dbg[r] = StepDebug() if moe else None
+                om.append(ost[r], c, app_dbg[r])
             else:
                 g = gseqs[r].canvas
                 gp = pred.view(n, C)[r]
                 gseqs[r].canvas.copy_(torch.where(g == cfg.mask_id, gp, g))
         gm.dlm_append_canvas(gseqs, ws)
         torch.cuda.synchronize()
+        app_route = routing(n * C) if moe else None
         for r in sample:
             assert gseqs[r].T == ost[r].T
+            skip = {}
+            if moe:
+                sets, lgs = app_route
+                skip = cache_routing_flips(sets.reshape(L, n, C, -1)[:, r], lgs.reshape(L, n, C, -1)[:, r],
+                                           app_dbg[r], bands[r], cfg.dtype, f"append routing, canvas {ci} request {r}")
+            cache_flips += len(skip)
             kv_worst = max(kv_worst, kv_check(gseqs[r], ost[r], ost[r].T - C, ost[r].T, cfg.dtype,
-                                              f"append canvas {ci} request {r}"))
+                                              f"append canvas {ci} request {r}", skip))
     assert gm.dlm_check_device_status() == 0
-    print(f"[parity] run={label} {totals.summary()}; first step on the GPU's own cache: max rel logit err "
-          f"{own_err:.3g}; KV max|d| / bound {kv_worst:.3g}", flush=True)
+    progress(f"[parity] run={label} {totals.summary()}; first step on the GPU's own cache: max rel logit err "
+          f"{own_err:.3g}; KV max|d| / bound {kv_worst:.3g} ({cache_flips} cached tokens re-routed at near-ties)")
     frac = totals.fractions()
-    for key, cap in (caps or {}).items():
-        assert frac[key] <= cap, f"{label}: exempt {key} fraction {frac[key]:.3f} above the cap {cap}"
+    for key, cap_ in (caps or {}).items():
+        assert frac[key] <= cap_, f"{label}: exempt {key} fraction {frac[key]:.3f} above the cap {cap_}"
     gm.close()
     return totals

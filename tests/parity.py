@@ -15,21 +15,26 @@ Decision bands.  1e-3 is a floor, not the band: a model stored in bf16 or fp8
 cannot decide a 1e-3 margin reproducibly, because an fp32-sized difference
 anywhere flips some storage rounding and the flips propagate.  The band of a
 step is measured on the oracle alone, never on the GPU: the oracle runs the
-step twice from the same state, exactly and with every contraction result
-(GEMM outputs, router logits, attention outputs) multiplied by
-(1 + EPS * N(0, 1)), EPS = 2^-20 -- the relative error an fp32 dot product of
-a few thousand terms carries.  delta_lc is the largest move of a masked
+step exactly and N_PERTURB more times from the same state with every
+contraction result (GEMM outputs, router logits, attention outputs)
+multiplied by (1 + EPS * N(0, 1)), EPS = 2^-20 -- the relative error an fp32
+dot product of a few thousand terms carries -- each with its own noise
+stream.  Over the perturbed runs: delta_lc is the largest move of a masked
 position's log-confidence, delta_gap the largest move of a row's top-1 margin
 (the exact argmax's logit minus the best other one), delta_router[l] the
-largest move of a router logit at layer l.  With SAFETY = 2 (the GPU's own
-fp32 arithmetic is another such perturbation, of similar size):
+largest move of a router logit at layer l over rows routed alike before l.
+The GPU's fp32 arithmetic is another such perturbation; SAFETY (2, and 4 for
+fp8, whose moves come in jumps of a flipped E4M3 code and scatter several-fold
+between noise streams) covers its draw:
   rank band      2 * SAFETY * delta_lc   (both ends of a rank pair move)
   threshold band     SAFETY * delta_lc
   token band         SAFETY * delta_gap
   router band    2 * SAFETY * delta_router[l]
-each at least 1e-3.  A decision inside its band is exempt; only what is unique
-is then compared (the number of commits, the decisive positions on either
-side).  Every run reports its exempt fractions; the callers cap them.
+each at least 1e-3.  A router choice that a perturbed run itself changes is
+undecidable at fp32 precision and exempt whatever its gap.  A decision inside
+its band is exempt; only what is unique is then compared (the number of
+commits, the decisive positions on either side).  Every run reports its
+exempt fractions; the callers cap them.
 
 Router-exempt rows keep a check: their router logits are compared with the
 oracle's at every layer up to and including the layer of the flip (a flip
@@ -49,7 +54,9 @@ import numpy as np
 MARGIN = 1e-3
 LOGIT_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
 EPS = 2.0 ** -20
-SAFETY = 2.0
+N_PERTURB = 3
+SAFETY_OF = {"f32": 2.0, "bf16": 2.0, "fp8": 4.0}
+SAFETY = SAFETY_OF["bf16"]
 
 
 @contextmanager
@@ -86,44 +93,73 @@ class Bands:
     delta_gap: float = 0.0
     delta_router: List[float] = field(default_factory=list)
     delta_logit_rel: float = 0.0
+    safety: float = SAFETY
+    noisy_flips: List[Set[int]] = field(default_factory=list)   # per layer: rows a perturbed run re-routed
 
     @property
     def rank(self) -> float:
-        return max(MARGIN, 2 * SAFETY * self.delta_lc)
+        return max(MARGIN, 2 * self.safety * self.delta_lc)
 
     @property
     def thr(self) -> float:
-        return max(MARGIN, SAFETY * self.delta_lc)
+        return max(MARGIN, self.safety * self.delta_lc)
 
     @property
     def tok(self) -> float:
-        return max(MARGIN, SAFETY * self.delta_gap)
+        return max(MARGIN, self.safety * self.delta_gap)
 
     def router(self, layer: int) -> float:
         d = self.delta_router[layer] if layer < len(self.delta_router) else 0.0
-        return max(MARGIN, 2 * SAFETY * d)
+        return max(MARGIN, 2 * self.safety * d)
+
+    def noisy_flip(self, layer: int, row: int) -> bool:
+        return layer < len(self.noisy_flips) and row in self.noisy_flips[layer]
 
 
-def oracle_bands(mask_id: int, masked: np.ndarray, exact, noisy) -> Bands:
+def oracle_bands(mask_id: int, masked: np.ndarray, exact, noisy, dtype: str = "bf16") -> Bands:
     """Bands from the exact and the perturbed oracle outputs of one step:
-    `exact`, `noisy` = (conf, pred, StepDebug) of OracleModel.denoise(debug=True)."""
-    (c0, p0, d0), (c1, _, d1) = exact, noisy
-    b = Bands()
-    same = np.ones(d0.logits.shape[0], dtype=bool)
-    for s0, s1, r0, r1 in zip(d0.router_sets, d1.router_sets, d0.router_logits, d1.router_logits):
-        same &= np.all(s0 == s1, axis=-1)      # rows routed alike so far
-        b.delta_router.append(float(np.max(np.abs(r1 - r0)[same])) if same.any() else 0.0)
-    # a row the perturbation re-routes at a router near-tie moves by a whole
-    # expert's share: that is the router exemption's case, not fp32 noise
-    lc0, lc1 = np.log(np.maximum(c0, 1e-300)), np.log(np.maximum(c1, 1e-300))
-    if np.any(masked & same):
-        b.delta_lc = float(np.max(np.abs(lc1 - lc0)[masked & same]))
-    if np.any(same):
-        b.delta_gap = float(np.max(np.abs(pred_margin(d1.logits, p0) - pred_margin(d0.logits, p0))[same]))
-        keep = np.arange(d0.logits.shape[1]) != mask_id
-        b.delta_logit_rel = float(np.max(np.abs(d1.logits[same][:, keep] - d0.logits[same][:, keep])) /
-                                  max(np.max(np.abs(d0.logits[:, keep])), 1e-30))
+    `exact` = (conf, pred, StepDebug) of OracleModel.denoise(debug=True),
+    `noisy` = one or a list of the same from perturbed runs."""
+    c0, p0, d0 = exact
+    b = Bands(safety=SAFETY_OF[dtype])
+    L = len(d0.router_sets)
+    b.delta_router = [0.0] * L
+    b.noisy_flips = [set() for _ in range(L)]
+    lc0 = np.log(np.maximum(c0, 1e-300))
+    keep = np.arange(d0.logits.shape[1]) != mask_id
+    scale = max(np.max(np.abs(d0.logits[:, keep])), 1e-30)
+    for c1, _, d1 in (noisy if isinstance(noisy, list) else [noisy]):
+        same = np.ones(d0.logits.shape[0], dtype=bool)      # rows routed alike before the layer
+        for l, (s0, s1, r0, r1) in enumerate(zip(d0.router_sets, d1.router_sets, d0.router_logits,
+                                                  d1.router_logits)):
+            if same.any():
+                b.delta_router[l] = max(b.delta_router[l], float(np.max(np.abs(r1 - r0)[same])))
+            flip = same & np.any(s0 != s1, axis=-1)
+            b.noisy_flips[l].update(int(r) for r in np.nonzero(flip)[0])
+            same &= ~flip
+        # a row the perturbation re-routes at a router near-tie moves by a whole
+        # expert's share: that is the router exemption's case, not fp32 noise
+        lc1 = np.log(np.maximum(c1, 1e-300))
+        if np.any(masked & same):
+            b.delta_lc = max(b.delta_lc, float(np.max(np.abs(lc1 - lc0)[masked & same])))
+        if np.any(same):
+            b.delta_gap = max(b.delta_gap, float(np.max(
+                np.abs(pred_margin(d1.logits, p0) - pred_margin(d0.logits, p0))[same])))
+            b.delta_logit_rel = max(b.delta_logit_rel, float(np.max(
+                np.abs(d1.logits[same][:, keep] - d0.logits[same][:, keep])) / scale))
     return b
+
+
+def step_bands(om, st, canvas: np.ndarray, exact, seed: int, n: int = N_PERTURB) -> Bands:
+    """Bands of the oracle step OracleModel.denoise(st, canvas) whose exact
+    outputs are `exact`, from `n` perturbed runs (noise streams seed ..
+    seed + n - 1).  The perturbed runs write the canvas's scratch K/V slots
+    of `st` like any denoising pass; the cached slots are untouched."""
+    noisy = []
+    for i in range(n):
+        with perturbed(om, seed + i):
+            noisy.append(om.denoise(st, canvas, debug=True))
+    return oracle_bands(om.cfg.mask_id, canvas == om.cfg.mask_id, exact, noisy, om.cfg.dtype)
 
 
 @dataclass
@@ -176,15 +212,17 @@ class StepReport:
 
 
 def router_exemptions(gpu_sets: Optional[np.ndarray], gpu_logits: Optional[np.ndarray], dbg, bands: Bands,
-                      dtype: str, rep: StepReport) -> Set[int]:
-    """Rows exempt because of a router near-tie flip.  gpu_sets: [L, rows, k]
-    (any order), gpu_logits: [L, rows, E]; dbg: the exact oracle's StepDebug
-    (router_sets sorted, router_gap = k-th minus (k+1)-th logit,
-    router_logits).  A flip at layer l is exempt when the oracle's gap is
-    inside the layer's router band; every row's router logits are compared
-    with the oracle's (LOGIT_TOL of the layer's largest) at every layer up to
-    and including its first flip."""
-    rows: Set[int] = set()
+                      dtype: str, rep: StepReport) -> Dict[int, int]:
+    """Rows exempt because of a router near-tie flip, mapped to the layer of
+    their first flip.  gpu_sets: [L, rows, k] (any order), gpu_logits:
+    [L, rows, E]; dbg: the exact oracle's StepDebug (router_sets sorted,
+    router_gap = k-th minus (k+1)-th logit, router_logits) of the same rows.
+    A flip at layer l is exempt when the oracle's gap is inside the layer's
+    router band or a perturbed oracle run changed that row's choice at that
+    layer too; every row's router logits are compared with the oracle's
+    (LOGIT_TOL of the layer's largest) at every layer up to and including its
+    first flip."""
+    rows: Dict[int, int] = {}
     if gpu_sets is None or not dbg.router_sets:
         return rows
     n = len(dbg.router_gap[0])
@@ -204,8 +242,8 @@ def router_exemptions(gpu_sets: Optional[np.ndarray], gpu_logits: Optional[np.nd
         diff = live & np.any(np.sort(gpu_sets[l], axis=-1) != os_, axis=-1)
         for r in np.nonzero(diff)[0]:
             first_flip[r] = l
-            if gap[r] < band:
-                rows.add(int(r))
+            if gap[r] < band or bands.noisy_flip(l, int(r)):
+                rows[int(r)] = l
             else:
                 rep.router_flips_decisive += 1
                 rep.problems.append(f"layer {l} row {r}: router set differs with oracle gap {gap[r]:.3g} "
@@ -222,7 +260,7 @@ def logit_bar(dtype: str, bands: Optional[Bands]) -> float:
     SAFETY times the oracle's own move."""
     tol = LOGIT_TOL[dtype]
     if bands is not None and bands.delta_logit_rel > tol:
-        return SAFETY * bands.delta_logit_rel
+        return bands.safety * bands.delta_logit_rel
     return tol
 
 
@@ -302,9 +340,10 @@ def compare_commit(before: np.ndarray, gpu_after: np.ndarray, oracle_after: np.n
     else:
         ambiguous |= masked & (np.abs(lc - np.log(threshold)) <= thr_m)
         if len(order) > 1 and not np.any(oracle_conf[idx] >= threshold):
-            # the at-least-one rule picks the most confident position
+            # the at-least-one rule picks the most confident position: any
+            # position within the rank band of it could take its place
             if lc[order[0]] - lc[order[1]] <= rank_m:
-                ambiguous |= masked & (lc >= lc[order[0]] - 2 * rank_m)
+                ambiguous |= masked & (lc >= lc[order[0]] - rank_m)
     ambiguous |= ex & masked
     if decided:
         rep.rank_decisions += int(masked.sum())

@@ -25,7 +25,7 @@ import torch
 import synth
 from oracle.model import OracleModel, OracleWeights
 from tests.lockstep import kv_check, load_cache
-from tests.parity import StepReport, compare_logits, oracle_bands, perturbed, router_exemptions, top2_margin
+from tests.parity import StepReport, compare_logits, router_exemptions, step_bands, top2_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -61,13 +61,11 @@ def test_ar_decode_lockstep(name):
     gm.dlm_debug_router(rdbg, rlog, cfg.n_layers * n)
     feed = [int(p[-1]) for p in prefixes]
     fed, gpu_pred = [], []
+    last_ex = [{} for _ in range(n)]
     for t in range(N_TOKENS):
         outs = [om.denoise(ost[r], np.array([feed[r]], dtype=np.int32), debug=True) for r in range(n)]
-        bands = []
-        for r in range(n):
-            with perturbed(om, seed=100 * t + r):
-                noisy = om.denoise(ost[r], np.array([feed[r]], dtype=np.int32), debug=True)
-            bands.append(oracle_bands(cfg.mask_id, np.zeros(1, dtype=bool), outs[r], noisy))
+        bands = [step_bands(om, ost[r], np.array([feed[r]], dtype=np.int32), outs[r], seed=1000 * t + 10 * r)
+                 for r in range(n)]
         for r in range(n):
             load_cache(gseqs[r], ost[r])
             gseqs[r].canvas.fill_(feed[r])
@@ -80,7 +78,7 @@ def test_ar_decode_lockstep(name):
         for r in range(n):
             _, pred_o, dbg = outs[r]
             rep = StepReport()
-            ex = router_exemptions(None if g_router is None else g_router[:, r],
+            ex = last_ex[r] = router_exemptions(None if g_router is None else g_router[:, r],
                                    None if g_rlog is None else g_rlog[:, r], dbg, bands[r], cfg.dtype, rep)
             compare_logits(lg[r:r + 1], dbg.logits, cfg.mask_id, cfg.dtype, rep, ex, bands[r])
             assert not rep.problems, f"step {t} request {r}: {rep.problems}"
@@ -97,7 +95,7 @@ def test_ar_decode_lockstep(name):
     # oracle's appended K/V; earlier slots came from the oracle's cache (lockstep)
     for r in range(n):
         assert gseqs[r].T == ost[r].T == T0[r] + N_TOKENS
-        kv_check(gseqs[r], ost[r], ost[r].T - 1, ost[r].T, cfg.dtype, f"AR cache request {r}")
+        kv_check(gseqs[r], ost[r], ost[r].T - 1, ost[r].T, cfg.dtype, f"AR cache request {r}", last_ex[r])
 
     # ar_decode: the product loop, fed the same tokens from a fresh prefill
     if moe:
@@ -110,7 +108,10 @@ def test_ar_decode_lockstep(name):
     # without the lockstep cache the GPU's own K/V differs from the oracle's by
     # rounding only; the dense runs' argmax tokens must then agree with the
     # lockstep GPU run wherever the oracle's gap is clear of the tolerance
+    # (for MoE models the first layer's: a prompt token re-routed at a router
+    # near-tie changes its K/V in every later layer)
     for r in range(n):
-        kv_check(gseqs2[r], ost[r], 0, ost[r].T, cfg.dtype, f"ar_decode cache request {r}")
+        kv_check(gseqs2[r], ost[r], 0, ost[r].T, cfg.dtype, f"ar_decode cache request {r}",
+                 {t: 0 for t in range(ost[r].T)} if moe else None)
     assert toks.shape == (n, N_TOKENS) and bool((toks != cfg.mask_id).all())
     gm.close()

@@ -24,7 +24,8 @@ import torch
 import synth
 from oracle import sampler as osampler
 from oracle.model import OracleModel, OracleWeights
-from tests.parity import StepReport, compare_commit, compare_logits, oracle_bands, perturbed, router_exemptions
+from tests.parity import StepReport, compare_commit, compare_logits, router_exemptions, step_bands
+from tests.progress import progress
 
 pytestmark = pytest.mark.gpu
 
@@ -59,10 +60,12 @@ def test_free_run_against_oracle_generate(name, graphs):
         steps = []
 
         def on_step(ci, s, before, conf, pred, after, st, dbg):
-            with perturbed(om, seed=1000 * ci + s):
-                noisy = om.denoise(st, before, debug=True)
+            # the full-size dense model's bands from one perturbation (its
+            # bf16 moves scatter little between noise streams), the others' from three
             steps.append((ci, s, before.copy(), conf, pred, after.copy(), dbg,
-                          oracle_bands(cfg.mask_id, before == cfg.mask_id, (conf, pred, dbg), noisy)))
+                          step_bands(om, st, before, (conf, pred, dbg), seed=1000 * ci + 10 * s,
+                                     n=1 if name == "dense-full" else 3)))
+            progress(f"[freerun] {name}: oracle request {r} canvas {ci} step {s}")
         osampler.generate(om, run, prefixes[r].numpy(), capacity=cap, on_step=on_step, with_state=True)
         oracle.append(steps)
 
@@ -124,10 +127,10 @@ def test_free_run_against_oracle_generate(name, graphs):
             before = after
         if diverged is None:
             assert len(o_steps) == len(gpu), "both runs take the same number of steps"
-            print(f"[freerun] run={name} request {r}: identical to the oracle over all {len(gpu)} steps "
-                  f"of {run.n_canvases} canvas(es)", flush=True)
+            progress(f"[freerun] run={name} request {r}: identical to the oracle over all {len(gpu)} steps "
+                  f"of {run.n_canvases} canvas(es)")
         else:
-            print(f"[freerun] run={name} request {r}: diverged legitimately at canvas {diverged[0]} step "
-                  f"{diverged[1]} (a commit inside the oracle's band)", flush=True)
-    print(f"[freerun] run={name} {tot.summary()}", flush=True)
+            progress(f"[freerun] run={name} request {r}: diverged legitimately at canvas {diverged[0]} step "
+                  f"{diverged[1]} (a commit inside the oracle's band)")
+    progress(f"[freerun] run={name} {tot.summary()}")
     gm.close()

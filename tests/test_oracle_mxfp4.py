@@ -1,0 +1,94 @@
+"""Pins of the oracle's MXFP4 functions (oracle/numerics.py) against the OCP
+Microscaling (MX) v1.0 format definition: the E2M1 value table, E8M0 scales,
+round-to-nearest-even with saturation (brute force over the representable
+values), and the block quantiser's shared exponent."""
+import numpy as np
+
+from oracle.numerics import (E2M1_MAX, MX_BLOCK, e2m1_decode_table, e2m1_encode, e2m1_round, e8m0_decode,
+                             mxfp4_decode, mxfp4_quantize)
+
+# the format's value table: codes 0..7 are the non-negative values, 8..15 their negatives
+SPEC_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_table_is_the_spec_table():
+    t = e2m1_decode_table()
+    np.testing.assert_array_equal(t[:8], SPEC_E2M1)
+    np.testing.assert_array_equal(t[8:], [-v for v in SPEC_E2M1])
+    assert np.signbit(t[8]) and t[8] == 0.0
+
+
+def test_e8m0_scales():
+    np.testing.assert_array_equal(e8m0_decode([127, 128, 126, 0, 254]), [1.0, 2.0, 0.5, 2.0 ** -127, 2.0 ** 127])
+    assert np.isnan(e8m0_decode(255))
+
+
+def test_e2m1_round_midpoints_and_saturation():
+    # every midpoint between neighbours goes to the value with the even mantissa (code bit 0 clear)
+    cases = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for x, want in cases.items():
+        assert e2m1_round(x) == want and e2m1_round(-x) == -want
+        assert e2m1_encode(want) & 1 == 0
+    for x in (6.0, 6.5, 7.99, 1e9):
+        assert e2m1_round(x) == 6.0 and e2m1_round(-x) == -6.0
+
+
+def test_e2m1_round_is_the_nearest_value_brute_force():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.uniform(-7, 7, 20000), np.array(SPEC_E2M1) * 1.0])
+    vals = np.array(SPEC_E2M1)
+    got = e2m1_round(x)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    dist = np.abs(a[:, None] - vals[None, :])
+    best = dist.min(axis=1)
+    # the result is one of the nearest values (ties are the midpoint cases above)
+    assert np.all(np.abs(np.abs(got) - a) <= best + 1e-12)
+    assert np.all(np.isin(np.abs(got), vals))
+
+
+def test_encode_decode_roundtrip_of_every_code():
+    t = e2m1_decode_table()
+    codes = np.arange(16, dtype=np.uint8)
+    np.testing.assert_array_equal(e2m1_encode(t), codes)
+
+
+def test_block_quantiser_shared_exponent():
+    # a block whose largest magnitude is 6 keeps scale 1 (code 127) and its values
+    w = np.zeros((1, MX_BLOCK))
+    w[0, :8] = SPEC_E2M1
+    w[0, 8:16] = [-v for v in SPEC_E2M1]
+    codes, scales = mxfp4_quantize(w)
+    assert scales.tolist() == [[127]]
+    np.testing.assert_array_equal(mxfp4_decode(codes, scales), w)
+    # max |w| = 1: exponent floor(log2 1) - 2 = -2, elements divided by 1/4
+    w = np.full((1, MX_BLOCK), 0.375)
+    w[0, 0] = -1.0
+    codes, scales = mxfp4_quantize(w)
+    assert scales.tolist() == [[125]]
+    np.testing.assert_array_equal(mxfp4_decode(codes, scales)[0, :2], [-1.0, 0.375])
+    # max |w| just below 8 * 2^k saturates at 6 * 2^k (the clipping the format defines)
+    w = np.full((1, MX_BLOCK), 0.01)
+    w[0, 5] = 7.9
+    codes, scales = mxfp4_quantize(w)
+    assert scales.tolist() == [[127]] and mxfp4_decode(codes, scales)[0, 5] == 6.0
+    # an all-zero block: exponent 0, zero codes
+    codes, scales = mxfp4_quantize(np.zeros((2, 2 * MX_BLOCK)))
+    assert scales.tolist() == [[127, 127], [127, 127]] and not codes.any()
+
+
+def test_block_quantiser_error_bound_and_roundtrip():
+    rng = np.random.default_rng(1)
+    w = rng.standard_normal((16, 8 * MX_BLOCK)) * 0.02
+    codes, scales = mxfp4_quantize(w)
+    deq = mxfp4_decode(codes, scales)
+    X = e8m0_decode(scales)[..., None]
+    blk = w.reshape(16, 8, MX_BLOCK)
+    err = np.abs(deq.reshape(16, 8, MX_BLOCK) - blk)
+    a = np.abs(blk) / X
+    step = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0))
+    # within half a step of the element's grid, or the clipping of the largest elements above 6
+    assert np.all((err <= step / 2 * X + 1e-15) | (a > E2M1_MAX))
+    # quantising dequantised data gives the same codes and scales back
+    c2, s2 = mxfp4_quantize(deq)
+    np.testing.assert_array_equal(s2, scales)
+    np.testing.assert_array_equal(mxfp4_decode(c2, s2), deq)

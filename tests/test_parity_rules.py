@@ -14,7 +14,7 @@ import pytest
 import synth
 from oracle import sampler as osampler
 from oracle.model import OracleModel, OracleWeights
-from tests.parity import (MARGIN, Bands, StepReport, compare_commit, compare_logits, oracle_bands, perturbed,
+from tests.parity import (MARGIN, Bands, StepReport, compare_commit, compare_logits, oracle_bands, perturbed, step_bands,
                           router_exemptions)
 
 
@@ -80,7 +80,7 @@ def _run_rules(name, steps, **model_changes):
     tot = StepReport()
     for step in range(steps):
         exact = _step(om, st, canvas)
-        bands = oracle_bands(cfg.mask_id, canvas == cfg.mask_id, exact, _step(om, st, canvas, seed=11 + step))
+        bands = step_bands(om, st, canvas, exact, seed=11 + 10 * step)
         impl = _step(om, st, canvas, seed=5000 + step)
         rep = StepReport()
         ex = router_exemptions(None if not exact[2].router_sets else np.stack(impl[2].router_sets),
@@ -103,10 +103,9 @@ def _run_rules(name, steps, **model_changes):
 def test_fp32_accurate_implementation_passes(name, steps):
     tot = _run_rules(name, steps)
     print(f"[rules] {name}: {tot.summary()}")
-    # an independent perturbation moves about as far as the one the bands came
-    # from; an E4M3 code flipped at a near-tie moves its row by a whole
-    # quantisation step, so fp8 step maxima scatter more
-    assert tot.gpu_lc_dev <= (4.0 if "fp8" in name else 2.0)
+    # an independent perturbation moves about as far as the ones the bands came
+    # from (a maximum over the few masked positions of a late step scatters)
+    assert tot.gpu_lc_dev <= 4.0
 
 
 def test_planted_logit_error_is_caught():
@@ -212,15 +211,20 @@ def test_router_flip_rules():
     g = np.array([[[0, 2], [2, 3]]])
     rep = StepReport()
     rows = router_exemptions(g, np.stack(D.router_logits), D, bands, "bf16", rep)
-    assert rows == {0} and not rep.problems
+    assert rows == {0: 0} and not rep.problems
     g = np.array([[[0, 1], [1, 3]]])
     rep = StepReport()
     rows = router_exemptions(g, np.stack(D.router_logits), D, bands, "bf16", rep)
-    assert rows == set() and rep.problems
+    assert rows == {} and rep.problems
     # a router band of 4 * 0.15 = 0.6 (from the oracle's own move, not the GPU's) exempts the 0.5-gap flip
     rep = StepReport()
     rows = router_exemptions(g, np.stack(D.router_logits), D, Bands(delta_router=[0.15]), "bf16", rep)
-    assert rows == {1} and not rep.problems
+    assert rows == {1: 0} and not rep.problems
+    # a choice a perturbed oracle run itself changed is exempt whatever its gap
+    rep = StepReport()
+    rows = router_exemptions(g, np.stack(D.router_logits), D, Bands(delta_router=[0.0], noisy_flips=[{1}]), "bf16",
+                             rep)
+    assert rows == {1: 0} and not rep.problems
     # router logits off by more than the tolerance at the flip layer are caught even when the flip is exempt
     glog = np.stack(D.router_logits).copy()
     glog[0, 1, 0] += 0.5
