@@ -287,6 +287,25 @@ dlm_status dlm_commit(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
 dlm_status dlm_append_canvas(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * denoising pass as dlm_denoise_step (same kernels, same results), with its
+ * workspace taken from a static device array of DLM_STATIC_SCRATCH_BYTES that
+ * the library holds on each device it runs on, from its first use there until
+ * the process ends, instead of a caller-provided one.  The call allocates
+ * nothing.  Every call on a device shares that device's array and leaves its
+ * contents behind (no kernel of the pass reads scratch it has not written in
+ * the same call, so nothing is cleared): calls that overlap on one device --
+ * from two streams or two models -- race, and the caller must serialise them.
+ * E_WORKSPACE (nothing enqueued) if the pass needs more than
+ * DLM_STATIC_SCRATCH_BYTES, i.e. if dlm_workspace_bytes(model, n_seqs * C,
+ * max T_r + C) exceeds it: the batch-1 canvases of the models this library
+ * is built for need 50 to 100 MiB.  Other arguments and errors as
+ * dlm_denoise_step. */
+#define DLM_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+dlm_status dlm_denoise_step_noalloc(dlm_model* model, dlm_seq* const* seqs, int32_t n_seqs,
+                                    float* conf, int32_t* pred, float* logits, void* stream);
+
 /* Synchronises `stream`, reads and clears the device error word.  Returns
  * DLM_OK, or DLM_E_DEVICE with the bits in *bits (nullable). */
 dlm_status dlm_check_device_status(dlm_model* model, void* stream, int32_t* bits);

@@ -31,6 +31,7 @@ DLM_E_UNSUPPORTED = -9
 DLM_DEVERR_TOKEN_RANGE = 1
 DLM_DEVERR_MASK_APPEND = 2
 DLM_MAX_SEQS = 64
+DLM_STATIC_SCRATCH_BYTES = 128 << 20
 
 DLM_F32, DLM_BF16, DLM_FP8 = 0, 1, 2
 DLM_FFN_DENSE, DLM_FFN_MOE = 0, 1
@@ -53,7 +54,7 @@ EXPORTS = [
     "dlm_commit", "dlm_append_canvas", "dlm_check_device_status", "dlm_last_error",
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
     "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace", "dlm_packed_weight_bytes", "dlm_pack_weight",
-    "dlm_op_route", "dlm_op_route_workspace", "dlm_op_router_topk",
+    "dlm_op_route", "dlm_op_route_workspace", "dlm_op_router_topk", "dlm_denoise_step_noalloc",
 ]
 DLM_GEMM_B_TILED = 0x100
 
@@ -122,6 +123,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_workspace_bytes": (c_size_t, [P, c_int32, c_int32]),
         "dlm_prefill": (c_int32, [P, POINTER(dlm_seq), P, c_int32, P, c_size_t, P]),
         "dlm_denoise_step": (c_int32, [P, POINTER(POINTER(dlm_seq)), c_int32, P, P, P, P, c_size_t, P]),
+        "dlm_denoise_step_noalloc": (c_int32, [P, POINTER(POINTER(dlm_seq)), c_int32, P, P, P, P]),
         "dlm_commit": (c_int32, [P, POINTER(POINTER(dlm_seq)), c_int32, P, P, POINTER(dlm_commit_rule),
                                  c_int32, P, P, P]),
         "dlm_append_canvas": (c_int32, [P, POINTER(POINTER(dlm_seq)), c_int32, P, c_size_t, P]),

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -23,9 +24,33 @@ LaunchTimer*& launch_timer() {
 }
 }  // namespace dlm
 
+// Workspace of dlm_denoise_step_noalloc: one copy per device, allocated when
+// the library's code object is loaded there.  Host code never uses this name
+// as an address (on the host it is only a handle): dlm_create looks up the
+// device address once per device with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[DLM_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device `dev` (looked up once).
+hipError_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
 
 dlm_status fail(dlm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 dlm_status fail(dlm_status s, const char* fmt, ...) {
@@ -55,6 +80,7 @@ struct dlm_model {
     std::vector<dlm_layer_weights> layers;
     int* d_err = nullptr;
     int device = 0;
+    void* scratch = nullptr;         // this device's static workspace (dlm_denoise_step_noalloc)
     // MoE models: the shared expert runs on a second stream of the library's
     // own (default priority), forked from and joined back into the caller's
     // stream with these events, so it overlaps the routing chain
@@ -585,6 +611,7 @@ dlm_status dlm_create(const dlm_config* cfg, const dlm_weights* weights, dlm_mod
     m->layers.assign(weights->layers, weights->layers + cfg->n_layers);
     m->w.layers = nullptr;
     hipError_t e = hipGetDevice(&m->device);
+    if (e == hipSuccess) e = scratch_address(m->device, &m->scratch);
     if (e == hipSuccess) e = hipMalloc((void**)&m->d_err, sizeof(int));
     if (e == hipSuccess) e = hipMemset(m->d_err, 0, sizeof(int));
     if (e == hipSuccess && cfg->ffn == DLM_FFN_MOE) {
@@ -663,6 +690,28 @@ dlm_status dlm_denoise_step(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, 
     src.per_seq = m->cfg.canvas;
     forward(m, DENOISE, tab, src, ws, conf, pred, logits, (hipStream_t)stream);
     return hip_status("dlm_denoise_step");
+}
+
+dlm_status dlm_denoise_step_noalloc(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, float* conf, int32_t* pred,
+                                    float* logits, void* stream) {
+    g_err.clear();
+    if (!m) return fail(DLM_E_ARG, "model is NULL");
+    if (!conf || !pred) return fail(DLM_E_ARG, "conf / pred is NULL");
+    SeqTab tab;
+    int max_kv;
+    dlm_status s = build_tab(m, seqs, n_seqs, m->cfg.canvas, true, tab, max_kv);
+    if (s) return s;
+    const size_t need = plan(m->cfg, n_seqs * m->cfg.canvas, max_kv).total;
+    if (need > DLM_STATIC_SCRATCH_BYTES)
+        return fail(DLM_E_WORKSPACE, "the pass needs %zu bytes of workspace, the static scratch holds %zu", need,
+                    (size_t)DLM_STATIC_SCRATCH_BYTES);
+    s = check_ws(m, m->scratch, DLM_STATIC_SCRATCH_BYTES, n_seqs * m->cfg.canvas, max_kv);
+    if (s) return s;
+    IdSource src{};
+    for (int i = 0; i < n_seqs; ++i) src.canvas[i] = seqs[i]->canvas;
+    src.per_seq = m->cfg.canvas;
+    forward(m, DENOISE, tab, src, m->scratch, conf, pred, logits, (hipStream_t)stream);
+    return hip_status("dlm_denoise_step_noalloc");
 }
 
 dlm_status dlm_commit(dlm_model* m, dlm_seq* const* seqs, int32_t n_seqs, const float* conf, const int32_t* pred,

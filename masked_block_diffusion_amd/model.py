@@ -278,6 +278,19 @@ class DLM:
                                         _ptr(logits), ws.data_ptr(), ws.numel(), _stream()),
               "dlm_denoise_step")
 
+    def dlm_denoise_step_noalloc(self, seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor,
+                                 logits: Optional[torch.Tensor] = None) -> None:
+        """dlm_denoise_step with the library's static per-device workspace
+        (no workspace argument, nothing allocated)."""
+        n = len(seqs)
+        assert conf.dtype == torch.float32 and conf.numel() >= n * self.C
+        assert pred.dtype == torch.int32 and pred.numel() >= n * self.C
+        if logits is not None:
+            assert logits.dtype == torch.float32 and logits.numel() >= n * self.C * self.cfg.vocab
+        check(self.lib.dlm_denoise_step_noalloc(self.handle, self._seq_array(seqs), n, conf.data_ptr(),
+                                                pred.data_ptr(), _ptr(logits), _stream()),
+              "dlm_denoise_step_noalloc")
+
     def dlm_commit(self, seqs: Sequence[Seq], conf: torch.Tensor, pred: torch.Tensor, rule: "Rule",
                    step: int, n_committed: Optional[torch.Tensor] = None,
                    n_masked: Optional[torch.Tensor] = None) -> None:
