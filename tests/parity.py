@@ -38,7 +38,11 @@ exempt fractions; the callers cap them.
 
 Router-exempt rows keep a check: their router logits are compared with the
 oracle's at every layer up to and including the layer of the flip (a flip
-changes the row only after it); their final logits are not compared.
+changes the row only after it); their final logits are not compared.  Their
+confidence is unknown, so in a top-k step each of them may take the place of
+one of the last committed rows (the last n_exempt non-exempt ranks above the
+boundary are exempt), and under the threshold rule's at-least-one fallback
+the oracle's top non-exempt row is exempt when any row is.
 
 The commit kernel itself is checked with no tolerance at all, against the
 oracle's rule applied to the GPU's own confidences and predictions.
@@ -335,22 +339,42 @@ def compare_commit(before: np.ndarray, gpu_after: np.ndarray, oracle_after: np.n
             hi, lo = lc[order[k - 1]], lc[order[k]]
             if hi - lo <= rank_m:
                 ambiguous |= (lc >= lo - rank_m) & (lc <= hi + rank_m) & masked
+            # an exempt row (re-routed at a near-tie) has no confidence to
+            # compare, so it may hold any rank on the GPU: each one can push
+            # one of the last committed rows out of the top k
+            n_ex = int((ex & masked).sum())
+            if n_ex:
+                ne = [j for j in order if not ex[j]]
+                ambiguous[ne[max(0, k - n_ex):k]] = True
         if int(g_set.sum()) != min(k, len(order)):
             rep.problems.append(f"top-k committed {int(g_set.sum())}, expected {min(k, len(order))}")
     else:
         ambiguous |= masked & (np.abs(lc - np.log(threshold)) <= thr_m)
         if len(order) > 1 and not np.any(oracle_conf[idx] >= threshold):
             # the at-least-one rule picks the most confident position: any
-            # position within the rank band of it could take its place
+            # position within the rank band of it could take its place, and
+            # so could an exempt row (on the GPU it may even pass the threshold)
             if lc[order[0]] - lc[order[1]] <= rank_m:
                 ambiguous |= masked & (lc >= lc[order[0]] - rank_m)
+            ne = [j for j in order if not ex[j]]
+            if np.any(ex & masked) and ne:
+                ambiguous[ne[0]] = True
     ambiguous |= ex & masked
     if decided:
         rep.rank_decisions += int(masked.sum())
         rep.exempt_ranks += int(ambiguous.sum())
     bad = (g_set != o_set) & ~ambiguous
     if np.any(bad):
-        rep.problems.append(f"commit sets differ at decisive positions {np.nonzero(bad)[0][:10].tolist()}")
+        where = np.nonzero(bad)[0][:10].tolist()
+        detail = ""
+        if gpu_conf is not None:
+            glc = np.log(np.maximum(gpu_conf, 1e-300))
+            detail = (f" (oracle log-conf {[round(float(lc[j]), 5) for j in where]}, GPU's "
+                      f"{[round(float(glc[j]), 5) for j in where]}; the oracle's {k}th / {k + 1}th "
+                      f"{[round(float(lc[order[i]]), 5) for i in (k - 1, k) if 0 <= i < len(order)]}, GPU's there "
+                      f"{[round(float(glc[order[i]]), 5) for i in (k - 1, k) if 0 <= i < len(order)]}; rank band "
+                      f"{rank_m:.3g}; largest GPU log-conf deviation {rep.gpu_lc_dev:.3g})")
+        rep.problems.append(f"commit sets differ at decisive positions {where}{detail}")
     both = g_set & o_set
     rep.token_decisions += int(both.sum())
     decisive_tok = both & (tm > tok_m) & ~ex

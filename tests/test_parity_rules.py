@@ -276,3 +276,32 @@ def test_fp8_noise_flips_codes_in_almost_every_row():
         if q0.shape[0] == run.canvas and q0.shape == q1.shape:
             flipped |= np.any(q0 != q1, axis=1)
     assert flipped.mean() >= 0.9
+
+
+def test_exempt_rows_may_displace_the_last_committed_ranks():
+    """Top-k: a row whose routing flipped at a near-tie is exempt, and its GPU
+    confidence may land anywhere, so it can push the oracle's last committed
+    non-exempt row out of the GPU's top k: that row is inside the band (the
+    rest of the ranking is still checked).  Without the exemption the same
+    commit is a mistake."""
+    C, mask = 6, 99
+    before = np.full(C, mask, dtype=np.int32)
+    conf = np.array([0.9, 0.8, 0.7, 0.6, 0.2, 0.1])
+    logits = np.zeros((C, 100))
+    logits[np.arange(C), np.arange(C)] = 5.0
+    o_after = before.copy()
+    o_after[:3] = [0, 1, 2]                      # the oracle commits its top 3
+    g_after = before.copy()
+    g_after[[0, 1, 5]] = [0, 1, 5]              # the GPU: row 5's confidence rose above row 2's
+    for exempt, ok in (({5}, True), (set(), False)):
+        rep = StepReport()
+        compare_commit(before, g_after, o_after, conf, logits, mask, "topk", 3, 0.5, False, rep, Bands(),
+                       exempt_rows=exempt)
+        assert (not rep.problems) == ok, rep.problems
+    # a second displaced row is still a mistake with one exempt row
+    g_after = before.copy()
+    g_after[[0, 4, 5]] = [0, 4, 5]
+    rep = StepReport()
+    compare_commit(before, g_after, o_after, conf, logits, mask, "topk", 3, 0.5, False, rep, Bands(),
+                   exempt_rows={5})
+    assert rep.problems
