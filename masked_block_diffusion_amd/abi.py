@@ -33,7 +33,7 @@ DLM_DEVERR_MASK_APPEND = 2
 DLM_MAX_SEQS = 64
 DLM_STATIC_SCRATCH_BYTES = 128 << 20
 
-DLM_F32, DLM_BF16, DLM_FP8 = 0, 1, 2
+DLM_F32, DLM_BF16, DLM_FP8, DLM_MXFP4 = 0, 1, 2, 3
 DLM_FFN_DENSE, DLM_FFN_MOE = 0, 1
 DLM_COMMIT_TOPK, DLM_COMMIT_THRESHOLD = 0, 1
 
@@ -55,6 +55,7 @@ EXPORTS = [
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
     "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace", "dlm_packed_weight_bytes", "dlm_pack_weight",
     "dlm_op_route", "dlm_op_route_workspace", "dlm_op_router_topk", "dlm_denoise_step_noalloc",
+    "dlm_packed_mxfp4_bytes", "dlm_pack_mxfp4", "dlm_op_mx_gemm", "dlm_op_mx_gemm_workspace",
 ]
 DLM_GEMM_B_TILED = 0x100
 
@@ -65,7 +66,7 @@ class dlm_config(ctypes.Structure):
         ("n_kv_heads", c_int32), ("head_dim", c_int32), ("vocab", c_int32),
         ("mask_id", c_int32), ("ffn", c_int32), ("d_ffn", c_int32), ("n_experts", c_int32),
         ("top_k", c_int32), ("d_expert", c_int32), ("dtype", c_int32), ("canvas", c_int32),
-        ("rms_eps", c_float), ("rope_base", c_float),
+        ("rms_eps", c_float), ("rope_base", c_float), ("expert_dtype", c_int32),
     ]
 
 
@@ -81,6 +82,7 @@ class dlm_layer_weights(ctypes.Structure):
         ("we_gate", c_void_p), ("we_gate_s", c_void_p),
         ("we_up", c_void_p), ("we_up_s", c_void_p),
         ("we_down", c_void_p), ("we_down_s", c_void_p),
+        ("we_gate_e8", c_void_p), ("we_up_e8", c_void_p), ("we_down_e8", c_void_p),
     ]
 
 
@@ -142,6 +144,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_op_route": (c_int32, [P, c_int32, c_int32, c_int32, P, P, P, P, P, c_size_t, P]),
         "dlm_op_route_workspace": (c_size_t, [c_int32, c_int32]),
         "dlm_op_router_topk": (c_int32, [P, c_int32, c_int32, c_int32, P, P, P]),
+        "dlm_packed_mxfp4_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+        "dlm_pack_mxfp4": (c_int32, [c_int32, c_int32, c_int32, P, P, P, P, P]),
+        "dlm_op_mx_gemm": (c_int32, [c_int32, c_int32, POINTER(c_int32), c_int32, c_int32, P, P, P, P, P, P, P,
+                                     c_size_t, c_int32, POINTER(c_float), P]),
+        "dlm_op_mx_gemm_workspace": (c_size_t, [c_int32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -96,6 +96,37 @@ long gemm_splitk_floats(const GemmDesc& d);
 // the narrowest tile is used for M <= 64
 int lm_head_tile_n(int M);
 
+// MXFP4 expert weights (mxfp4.hip).  Packed layout of a [N, K] matrix (K a
+// multiple of 128, N padded to a multiple of 16): codes in blocks of 16 rows x
+// 64 bytes (128 E2M1 codes per row, the even element in the low nibble), block
+// (g, t) at byte (g * K / 128 + t) * 1024; E8M0 scales in blocks of 64 bytes,
+// block (g, t) at byte (g * K / 128 + t) * 64, byte r + 16 j = row 16 g + r,
+// elements 128 t + 32 j .. + 32.  Matrices of a batch follow one another.
+long mx_code_bytes(int N, int K);
+long mx_scale_bytes(int N, int K);
+// codes [batch, N, K / 2] and scales [batch, N, K / 32] row-major -> packed
+void mx_pack(int batch, int N, int K, const void* codes, const void* scales, void* dst_codes, void* dst_scales,
+             hipStream_t st);
+// m-tile rows of the MXFP4 grouped GEMM (the routing's tile height for it)
+int mx_grouped_bm();
+// Grouped expert GEMM with bf16 A [M, K] (rows in expert order, or gathered as
+// in GemmDesc) and MXFP4 B: swiglu -> C bf16 = silu(A B^T) * (A B2^T), else
+// C fp32 = A B^T.  offs / tile_start as for gemm_grouped with mx_grouped_bm().
+struct MxDesc {
+    bool swiglu = false;
+    const void* A = nullptr; long lda = 0;        // elements
+    const int* gather = nullptr; int gather_div = 1;
+    const void* B = nullptr; const void* B2 = nullptr;
+    const void* S = nullptr; const void* S2 = nullptr;
+    long b_stride = 0, s_stride = 0;              // bytes between experts
+    const int* offs = nullptr; const int* tile_start = nullptr;
+    int E = 0, M = 0, N = 0, K = 0;
+    void* C = nullptr; long ldc = 0;              // elements
+    int variant = 0;                              // 0 = default tile shape, 1..mx_variants() forced
+};
+void mx_grouped(const MxDesc& d, hipStream_t st);
+int mx_variants();
+
 // Token ids of one forward: one flat array, or per-request canvases.
 struct IdSource {
     const int32_t* flat;               // nullable

@@ -24,7 +24,7 @@ import torch
 from . import abi
 from .abi import check
 
-_DTYPES = {"f32": abi.DLM_F32, "bf16": abi.DLM_BF16, "fp8": abi.DLM_FP8}
+_DTYPES = {"f32": abi.DLM_F32, "bf16": abi.DLM_BF16, "fp8": abi.DLM_FP8, "mxfp4": abi.DLM_MXFP4}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -131,7 +131,7 @@ class DLM:
             mask_id=cfg.mask_id, ffn=abi.DLM_FFN_MOE if cfg.ffn == "moe" else abi.DLM_FFN_DENSE,
             d_ffn=cfg.d_ffn, n_experts=cfg.n_experts, top_k=cfg.top_k, d_expert=cfg.d_expert,
             dtype=_DTYPES[cfg.dtype], canvas=canvas, rms_eps=cfg.rms_eps,
-            rope_base=cfg.rope_base)
+            rope_base=cfg.rope_base, expert_dtype=_DTYPES[getattr(cfg, "expert_dtype", None) or cfg.dtype])
         self.raw_cfg = c
         W = self._pack(cfg, weights)
         self._layers = (abi.dlm_layer_weights * cfg.n_layers)(*W["layers"])
@@ -194,6 +194,24 @@ class DLM:
         self._keep.append(dst)
         return dst
 
+    def _mx(self, weights, name):
+        """(packed codes pointer, packed scales pointer) of an MXFP4 expert
+        tensor: codes `name.q4` uint8 [E, N, K / 2] and E8M0 scales `name.e8`
+        uint8 [E, N, K / 32], rearranged by dlm_pack_mxfp4 (a kernel on the
+        current stream)."""
+        q = weights[name + ".q4"].to(self.device).contiguous()
+        e = weights[name + ".e8"].to(self.device).contiguous()
+        E, N, K = q.shape[0], q.shape[1], q.shape[2] * 2
+        nc = self.lib.dlm_packed_mxfp4_bytes(E, N, K, 0)
+        ns = self.lib.dlm_packed_mxfp4_bytes(E, N, K, 1)
+        if nc == 0 or ns == 0 or tuple(e.shape) != (E, N, K // 32):
+            raise ValueError(f"cannot pack MXFP4 {name}: codes {tuple(q.shape)}, scales {tuple(e.shape)}")
+        dc = torch.empty(nc, dtype=torch.uint8, device=self.device)
+        ds = torch.empty(ns, dtype=torch.uint8, device=self.device)
+        check(self.lib.dlm_pack_mxfp4(E, N, K, _ptr(q), _ptr(e), _ptr(dc), _ptr(ds), _stream()), "dlm_pack_mxfp4")
+        self._keep += [dc, ds]
+        return _ptr(dc), _ptr(ds)
+
     def _proj(self, weights, name, cat: Sequence[str] = ()):
         """(tiled codes-or-values pointer, scale pointer) of a projection;
         `cat` concatenates several along the output dimension."""
@@ -222,9 +240,14 @@ class DLM:
             L.w_down, L.w_down_s = self._proj(weights, p + "w_down")
             if cfg.ffn == "moe":
                 L.w_router = _ptr(self._dev(weights[p + "w_router"]))
-                L.we_gate, L.we_gate_s = self._proj(weights, p + "we_gate")
-                L.we_up, L.we_up_s = self._proj(weights, p + "we_up")
-                L.we_down, L.we_down_s = self._proj(weights, p + "we_down")
+                if getattr(cfg, "expert_dtype", None) == "mxfp4":
+                    L.we_gate, L.we_gate_e8 = self._mx(weights, p + "we_gate")
+                    L.we_up, L.we_up_e8 = self._mx(weights, p + "we_up")
+                    L.we_down, L.we_down_e8 = self._mx(weights, p + "we_down")
+                else:
+                    L.we_gate, L.we_gate_s = self._proj(weights, p + "we_gate")
+                    L.we_up, L.we_up_s = self._proj(weights, p + "we_up")
+                    L.we_down, L.we_down_s = self._proj(weights, p + "we_down")
             layers.append(L)
         W["layers"] = layers
         return W

@@ -115,6 +115,9 @@ MOE_BF16 = ModelConfig(
 
 MOE_FP8 = replace(MOE_BF16, name="moe-26b-a3b-fp8", dtype="fp8")
 
+# the same model with its routed experts' weights in MXFP4 (4.25 bits per weight)
+MOE_MXFP4 = replace(MOE_BF16, name="moe-26b-a3b-mxfp4", expert_dtype="mxfp4")
+
 # Reduced models for oracle-speed parity: same structure, small dims, ragged
 # vocab (not a multiple of any tile) so tails are exercised.
 DENSE_BF16_MINI = ModelConfig(
@@ -127,6 +130,8 @@ MOE_BF16_MINI = ModelConfig(
     n_experts=16, top_k=4, d_expert=128, dtype="bf16")
 
 MOE_FP8_MINI = replace(MOE_BF16_MINI, name="moe-mini-fp8", dtype="fp8")
+
+MOE_MXFP4_MINI = replace(MOE_BF16_MINI, name="moe-mini-mxfp4", expert_dtype="mxfp4")
 
 DENSE_FP8_MINI = replace(DENSE_BF16_MINI, name="dense-mini-fp8", dtype="fp8")
 
@@ -147,6 +152,9 @@ RUNS = {
     "moe-fp8": RunConfig("moe-fp8", MOE_FP8, canvas=256, n_requests=1,
                          prefix_len=(4096, 4096), n_canvases=1, rule="threshold",
                          n_steps=48, threshold=0.5),
+    # 3 with MXFP4 routed experts
+    "moe-mxfp4": RunConfig("moe-mxfp4", MOE_MXFP4, canvas=256, n_requests=1,
+                           prefix_len=(4096, 4096), n_canvases=4, rule="topk", n_steps=12),
     # 5: 32 independent requests, prefixes U[512, 4096], paged KV
     "moe-batch32": RunConfig("moe-batch32", MOE_BF16, canvas=256, n_requests=32,
                              prefix_len=(512, 4096), n_canvases=1, rule="topk",
@@ -165,6 +173,10 @@ RUNS = {
     "dense-mini-fp8": RunConfig("dense-mini-fp8", DENSE_FP8_MINI, canvas=64, n_requests=1,
                                 prefix_len=(70, 70), n_canvases=1, rule="threshold",
                                 n_steps=48, threshold=0.5),
+    "moe-mini-mxfp4": RunConfig("moe-mini-mxfp4", MOE_MXFP4_MINI, canvas=64, n_requests=1,
+                                prefix_len=(100, 100), n_canvases=2, rule="topk", n_steps=12),
+    "moe-mini-mxfp4-batch": RunConfig("moe-mini-mxfp4-batch", MOE_MXFP4_MINI, canvas=64, n_requests=4,
+                                      prefix_len=(20, 150), n_canvases=1, rule="topk", n_steps=12),
     "moe-mini-batch": RunConfig("moe-mini-batch", MOE_BF16_MINI, canvas=64, n_requests=4,
                                 prefix_len=(20, 150), n_canvases=1, rule="topk",
                                 n_steps=12),

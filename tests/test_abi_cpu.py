@@ -22,7 +22,7 @@ def _lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dlm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dlm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -39,9 +39,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_the_c_layout():
-    # 16 int/float fields; 19 pointers; 4 pointers + a pointer; seq: p, i, i, p, p, i (+pad)
-    assert ctypes.sizeof(abi.dlm_config) == 16 * 4
-    assert ctypes.sizeof(abi.dlm_layer_weights) == 19 * 8
+    # 17 int/float fields; 22 pointers; 4 pointers + a pointer; seq: p, i, i, p, p, i (+pad)
+    assert ctypes.sizeof(abi.dlm_config) == 17 * 4
+    assert ctypes.sizeof(abi.dlm_layer_weights) == 22 * 8
     assert ctypes.sizeof(abi.dlm_weights) == 5 * 8
     assert ctypes.sizeof(abi.dlm_seq) == 8 + 4 + 4 + 8 + 8 + 8
     assert ctypes.sizeof(abi.dlm_commit_rule) == 4 + 4 + 8 + 8
@@ -69,6 +69,14 @@ def _cfg(**kw):
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=9, d_expert=64), abi.DLM_E_SHAPE),
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=64, top_k=17, d_expert=64), abi.DLM_E_SHAPE),
     (dict(n_layers=0), abi.DLM_E_SHAPE),
+    # MXFP4 experts: only for bf16 MoE models, d_model and d_expert multiples of 128
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=128, expert_dtype=abi.DLM_MXFP4), abi.DLM_E_DTYPE),
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=64, dtype=abi.DLM_BF16,
+          expert_dtype=abi.DLM_MXFP4), abi.DLM_E_SHAPE),
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=128, dtype=abi.DLM_BF16, expert_dtype=7),
+     abi.DLM_E_DTYPE),
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=128, dtype=abi.DLM_FP8,
+          expert_dtype=abi.DLM_MXFP4), abi.DLM_E_DTYPE),
 ])
 def test_create_rejects_bad_config(kw, status):
     lib = _lib()
@@ -171,3 +179,26 @@ def test_op_router_topk_validates_on_the_host():
     assert lib.dlm_op_router_topk(f, 4, 257, 2, f, f, None) == abi.DLM_E_ARG
     assert lib.dlm_op_router_topk(f, 4, 8, 9, f, f, None) == abi.DLM_E_ARG
     assert lib.dlm_op_router_topk(f, 4, 32, 17, f, f, None) == abi.DLM_E_ARG
+
+
+def test_mxfp4_pack_and_gemm_validate_on_the_host():
+    """Packed MXFP4 sizes are host arithmetic (16-row padding; codes K / 2 and
+    scales K / 32 bytes per row); bad shapes and pointers are refused before
+    any HIP call."""
+    lib = _lib()
+    assert lib.dlm_packed_mxfp4_bytes(3, 40, 256, 0) == 3 * 48 * 128
+    assert lib.dlm_packed_mxfp4_bytes(3, 40, 256, 1) == 3 * 48 * 8
+    assert lib.dlm_packed_mxfp4_bytes(1, 16, 192, 0) == 0                   # K not a multiple of 128
+    assert lib.dlm_packed_mxfp4_bytes(0, 16, 128, 0) == 0
+    assert lib.dlm_pack_mxfp4(1, 16, 128, None, None, None, None, None) == abi.DLM_E_ARG
+    assert lib.dlm_pack_mxfp4(1, 16, 192, 0x1000, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_SHAPE
+    assert lib.dlm_pack_mxfp4(1, 16, 128, 0x1008, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_ARG   # misaligned
+    assert lib.dlm_pack_mxfp4(1, 16, 128, 0x1000, 0x2000, 0x1000, 0x20000, None) == abi.DLM_E_ARG   # overlap
+    cnt = (ctypes.c_int32 * 2)(3, 4)
+    assert lib.dlm_op_mx_gemm_workspace(0) == 0
+    assert lib.dlm_op_mx_gemm(0, 2, cnt, 16, 128, None, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
+                              None, None) == abi.DLM_E_ARG
+    assert lib.dlm_op_mx_gemm(0, 2, cnt, 16, 96, 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
+                              None, None) == abi.DLM_E_SHAPE
+    assert lib.dlm_op_mx_gemm(1, 2, cnt, 16, 128, 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
+                              None, None) == abi.DLM_E_ARG                   # SwiGLU without B2 / S2

@@ -8,7 +8,7 @@ canvas lengths, so every kernel runs its real grid and tile choice):
     262144) at full width but two of its 32 layers (all 32 run in
     tests/test_gpu_depth.py with a shorter prompt): prefill of the 4096-token
     prompt, the first denoising steps, the append -- in bf16, and in fp8 with
-    the threshold rule (one and two layers);
+    the threshold rule (one and two layers), and with MXFP4 routed experts;
   * the 32-request batch (prefixes of 512..4096 tokens, 8192 canvas rows per
     step, every request's cache in 64-token pages of one pool) at full width,
     two layers: the GPU runs the whole batch, the oracle follows two of the
@@ -51,6 +51,14 @@ def test_fullsize_dense():
 
 def test_fullsize_moe_two_layers():
     lockstep(_layers(synth.get_run("moe"), 2), "moe (full width, 2 layers)", max_steps=2, caps=BF16_CAPS)
+
+
+def test_fullsize_moe_mxfp4_two_layers():
+    """The same two layers with the routed experts' weights in MXFP4: the
+    prefill's 32768 assignments (several 64-row m-tiles per expert) and the
+    canvas's 2048 through the MXFP4 grouped GEMM."""
+    lockstep(_layers(synth.get_run("moe-mxfp4"), 2), "moe-mxfp4 (full width, 2 layers)", max_steps=2,
+             caps=BF16_CAPS)
 
 
 def test_fullsize_moe_fp8_one_layer():

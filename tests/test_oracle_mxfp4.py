@@ -92,3 +92,29 @@ def test_block_quantiser_error_bound_and_roundtrip():
     c2, s2 = mxfp4_quantize(deq)
     np.testing.assert_array_equal(s2, scales)
     np.testing.assert_array_equal(mxfp4_decode(c2, s2), deq)
+
+
+def test_synth_quantiser_agrees_with_the_oracle():
+    """The weight generator's MXFP4 quantiser (synth, torch) writes the codes
+    and scales both the GPU and the oracle read; it must be the quantiser
+    pinned above: identical codes and scales on normal weights, an all-zero
+    block, blocks whose maximum is a power of two or just below one, and
+    values at E2M1 midpoints."""
+    import torch
+    from synth.weights import quantize_mxfp4_rows
+    rng = np.random.default_rng(7)
+    w = rng.standard_normal((6, 256)) * 0.02
+    w[0, :32] = 0.0                                       # all-zero block
+    w[1, :32] = rng.choice([-1, 1], 32) * 2.0 ** -5       # max a power of two
+    w[1, 32:64] = np.linspace(-0.0624, 0.0624, 32)        # max just below 2^-4
+    w[2, :32] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0] * 4) * 2.0 ** -3   # midpoints
+    w[2, 31] = 6.0 * 2.0 ** -3
+    w = w.astype(np.float32).astype(np.float64)          # the generator quantises fp32 values
+    q, e = quantize_mxfp4_rows(torch.from_numpy(w).float())
+    q = q.numpy()
+    codes = np.empty((w.shape[0], w.shape[1]), dtype=np.uint8)
+    codes[:, 0::2] = q & 15
+    codes[:, 1::2] = q >> 4
+    want_codes, want_scales = mxfp4_quantize(w)
+    np.testing.assert_array_equal(codes, want_codes)
+    np.testing.assert_array_equal(e.numpy(), want_scales)
