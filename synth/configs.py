@@ -135,6 +135,10 @@ MOE_MXFP4_MINI = replace(MOE_BF16_MINI, name="moe-mini-mxfp4", expert_dtype="mxf
 
 DENSE_FP8_MINI = replace(DENSE_BF16_MINI, name="dense-mini-fp8", dtype="fp8")
 
+# the bf16 attention kernel's smaller head sizes (4 waves per workgroup)
+DENSE_BF16_MINI_DH64 = replace(DENSE_BF16_MINI, name="dense-mini-dh64-bf16", n_q_heads=8, n_kv_heads=2, head_dim=64)
+DENSE_BF16_MINI_DH32 = replace(DENSE_BF16_MINI, name="dense-mini-dh32-bf16", n_q_heads=16, n_kv_heads=4, head_dim=32)
+
 
 # ---- runs -------------------------------------------------------------------
 
@@ -173,6 +177,10 @@ RUNS = {
     "dense-mini-fp8": RunConfig("dense-mini-fp8", DENSE_FP8_MINI, canvas=64, n_requests=1,
                                 prefix_len=(70, 70), n_canvases=1, rule="threshold",
                                 n_steps=48, threshold=0.5),
+    "dense-mini-dh64": RunConfig("dense-mini-dh64", DENSE_BF16_MINI_DH64, canvas=48, n_requests=1,
+                                 prefix_len=(77, 77), n_canvases=2, rule="topk", n_steps=6),
+    "dense-mini-dh32": RunConfig("dense-mini-dh32", DENSE_BF16_MINI_DH32, canvas=48, n_requests=2,
+                                 prefix_len=(30, 140), n_canvases=1, rule="topk", n_steps=6),
     "moe-mini-mxfp4": RunConfig("moe-mini-mxfp4", MOE_MXFP4_MINI, canvas=64, n_requests=1,
                                 prefix_len=(100, 100), n_canvases=2, rule="topk", n_steps=12),
     "moe-mini-mxfp4-batch": RunConfig("moe-mini-mxfp4-batch", MOE_MXFP4_MINI, canvas=64, n_requests=4,

@@ -1,5 +1,6 @@
 """Parity at depth: the 26B-class MoE at full width (d = 2560, 128 experts
-top-8 x 768 + shared 2048, vocab 262144) through all 32 of its layers
+top-8 x 768 + shared 2048, vocab 262144) through all 32 of its layers, with
+bf16 and with MXFP4 routed experts
 ("DiffusionGemma: 4x Faster Text Generation via Parallel Diffusion",
 "Parallel Generation and Hardware Efficiency": the 26B MoE), free running:
 the GPU's own prefill, its own first denoising step, its own append and the
@@ -32,7 +33,7 @@ import pytest
 import torch
 
 import synth
-from oracle.model import NEG_INF, OracleModel, SeqState, StepDebug
+from oracle.model import NEG_INF, OracleModel, OracleWeights, SeqState, StepDebug
 from tests.lockstep import cache_routing_flips, kv_check
 from tests.progress import progress
 from tests.parity import StepReport, compare_logits, logit_bar, oracle_bands, perturbed, router_exemptions
@@ -43,11 +44,26 @@ DEPTHS = (2, 8, 16, 32)
 PROMPT = 256
 
 
+class _MxExperts:
+    """The experts of one MXFP4 tensor (codes and E8M0 scales on the GPU),
+    each decoded by the oracle (OracleWeights) when first used."""
+
+    def __init__(self, cfg, name, q, e8):
+        self.cfg, self.name, self.q, self.e8, self.cache = cfg, name, q, e8, {}
+
+    def __getitem__(self, e):
+        if e not in self.cache:
+            one = {self.name + ".q4": self.q[e:e + 1].cpu(), self.name + ".e8": self.e8[e:e + 1].cpu()}
+            self.cache[e] = OracleWeights(self.cfg, one)[self.name][0]
+        return self.cache[e]
+
+
 class StreamedWeights:
     """OracleWeights over GPU tensors, one layer at a time: `load(l)` copies
-    layer l's tensors to the host in float64, `drop(l)` releases them.  The
-    global tensors stay loaded (the embedding as float32, exact for its bf16
-    values)."""
+    layer l's tensors to the host in float64 (MXFP4 experts: decoded one
+    expert at a time, when the oracle first uses it), `drop(l)` releases
+    them.  The global tensors stay loaded (the embedding as float32, exact for
+    its bf16 values)."""
 
     def __init__(self, cfg, gpu: dict):
         self.cfg, self.gpu = cfg, gpu
@@ -60,7 +76,11 @@ class StreamedWeights:
 
     def load(self, l):
         for k, v in self.gpu.items():
-            if k.startswith(f"{l}."):
+            if not k.startswith(f"{l}.") or k.endswith(".e8"):
+                continue
+            if k.endswith(".q4"):
+                self.w[k[:-3]] = _MxExperts(self.cfg, k[:-3], v, self.gpu[k[:-3] + ".e8"])
+            else:
                 self.w[k] = self._host(v)
 
     def drop(self, l):
@@ -85,12 +105,13 @@ def _conf_pred(lg):
     return 1.0 / np.exp(lg - m[:, None]).sum(axis=-1), np.argmax(lg, axis=-1).astype(np.int32)
 
 
-def test_moe_full_width_all_layers():
+@pytest.mark.parametrize("name", ["moe", "moe-mxfp4"])
+def test_moe_full_width_all_layers(name):
     from masked_block_diffusion_amd import DLM
-    run = synth.get_run("moe")
+    run = synth.get_run(name)
     run = replace(run, prefix_len=(PROMPT, PROMPT), n_canvases=2)
     cfg, C, L = run.model, run.canvas, run.model.n_layers
-    print(f"[depth] moe full width, {L} layers, prompt {PROMPT}, canvas {C}", flush=True)
+    print(f"[depth] {name} full width, {L} layers, prompt {PROMPT}, canvas {C}", flush=True)
     w = synth.make_weights(cfg, seed=run.seed, device="cuda")
     gm = DLM(cfg, w, canvas=C)
     subs = {k: gm.truncated(k) for k in DEPTHS if k < L}
@@ -214,7 +235,7 @@ def test_moe_full_width_all_layers():
     flips += len(skip)
     e1 = compare(g1, o1, "canvas 1 step 0 (own append)", bands_of)
     assert gm.dlm_check_device_status() == 0
-    progress(f"[depth] max rel logit err by depth, canvas 0: {e0}; canvas 1: {e1}; KV max|d| / bound {kv_worst:.3g} "
+    progress(f"[depth] {name}: max rel logit err by depth, canvas 0: {e0}; canvas 1: {e1}; KV max|d| / bound {kv_worst:.3g} "
           f"({flips} cached tokens re-routed at near-ties)")
     for s in subs.values():
         if s is not gm:

@@ -2,7 +2,7 @@
 tests/lockstep.py for what is compared at every step).
 
 Runs: the tiny fp32 model at its full size, and reduced bf16/fp8, dense/MoE
-(MoE also with MXFP4 routed experts),
+(MoE also with MXFP4 routed experts; dense also at head sizes 64 and 32),
 single- and multi-request variants whose vocabulary, canvas and prefix sizes
 are not multiples of any kernel tile; three of them again with paged caches.  The full-size workloads are in
 tests/test_gpu_fullsize.py.
@@ -15,7 +15,7 @@ from tests.lockstep import lockstep
 pytestmark = pytest.mark.gpu
 
 RUNS = ["tiny", "dense-mini", "dense-mini-ragged", "moe-mini", "dense-mini-fp8", "moe-mini-fp8",
-        "moe-mini-batch", "tiny-t2t", "moe-mini-mxfp4", "moe-mini-mxfp4-batch"]
+        "moe-mini-batch", "tiny-t2t", "moe-mini-mxfp4", "moe-mini-mxfp4-batch", "dense-mini-dh64", "dense-mini-dh32"]
 
 
 @pytest.mark.parametrize("name", RUNS)
