@@ -95,8 +95,10 @@ def kernel_model(name: str, cfg, rows: int, keys_per_req, experts_used=None):
     if name in ("expert_gate_up", "expert_down") and cfg.ffn == "moe":
         De, A = cfg.d_expert, M * cfg.top_k
         used = experts_used if experts_used is not None else experts_touched(cfg.n_experts, cfg.top_k, M)
-        # MXFP4 experts: 4-bit codes plus one E8M0 byte per 32 weights; bf16 activations
-        web, aeb = (0.5 + 1.0 / 32, 2) if getattr(cfg, "expert_dtype", None) == "mxfp4" else (eb, eb)
+        # MX experts: 4-bit (MXFP4) or 6-bit (MXFP6) codes plus one E8M0 byte per
+        # 32 weights; bf16 activations
+        mx_bits = {"mxfp4": 4, "mxfp6": 6}.get(getattr(cfg, "expert_dtype", None))
+        web, aeb = (mx_bits / 8 + 1.0 / 32, 2) if mx_bits else (eb, eb)
         if name == "expert_gate_up":
             return used * 2 * De * d * web + A * d * aeb + A * De * ab, 2.0 * A * 2 * De * d
         return used * d * De * web + A * De * aeb + A * d * 4, 2.0 * A * d * De

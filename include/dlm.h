@@ -89,8 +89,9 @@ typedef int32_t dlm_status;
 
 #define DLM_MAX_SEQS 64              /* requests per denoise/commit/append call */
 
-/* DLM_MXFP4: storage of the routed experts' weights only (dlm_config.expert_dtype). */
-typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_FP8 = 2, DLM_MXFP4 = 3 } dlm_dtype;
+/* DLM_MXFP4, DLM_MXFP6: storage of the routed experts' weights only
+ * (dlm_config.expert_dtype). */
+typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_FP8 = 2, DLM_MXFP4 = 3, DLM_MXFP6 = 4 } dlm_dtype;
 typedef enum { DLM_FFN_DENSE = 0, DLM_FFN_MOE = 1 } dlm_ffn_kind;
 
 /* Model shape.  Constraints checked by dlm_create: head_dim in {32, 64, 128};
@@ -116,14 +117,15 @@ typedef struct {
     float   rms_eps;
     float   rope_base;
     /* Storage of the routed experts' weights (MoE only; ignored for dense
-     * models): equal to dtype, or DLM_MXFP4 with a DLM_BF16 model -- OCP
-     * Microscaling (MX) v1.0 MXFP4, E2M1 codes in blocks of 32 along K sharing an
-     * E8M0 scale, 4.25 bits per weight (the 4-bit expert weights of
-     * DiffusionGemma 4x, "Deployment and Tooling", in the chip's own 4-bit
-     * format).  The experts then compute with the decoded weights (code value
-     * times block scale, exact in bf16) on the bf16 activations, fp32 sums; the
-     * rest of the model is bf16.  MXFP4 needs d_model and d_expert multiples of
-     * 128.  E_DTYPE for any other value. */
+     * models): equal to dtype, or with a DLM_BF16 model one of the OCP
+     * Microscaling (MX) v1.0 formats, elements in blocks of 32 along K sharing
+     * an E8M0 scale: DLM_MXFP4 (E2M1 elements, 4.25 bits per weight -- the
+     * 4-bit expert weights of DiffusionGemma 4x, "Deployment and Tooling", in
+     * the chip's own 4-bit format) or DLM_MXFP6 (E2M3 elements, 6.25 bits per
+     * weight).  The experts then compute with the decoded weights (element
+     * value times block scale, exact in bf16) on the bf16 activations, fp32
+     * sums; the rest of the model is bf16.  MX experts need d_model and
+     * d_expert multiples of 128.  E_DTYPE for any other value. */
     int32_t expert_dtype;
 } dlm_config;
 
@@ -152,9 +154,9 @@ typedef struct {
     const void*  we_gate; const float* we_gate_s;
     const void*  we_up;   const float* we_up_s;
     const void*  we_down; const float* we_down_s;
-    /* MXFP4 experts (expert_dtype DLM_MXFP4): we_gate / we_up / we_down hold
-     * the packed E2M1 codes and these the packed E8M0 scales, both in the
-     * layout dlm_pack_mxfp4 writes; NULL otherwise. */
+    /* MX experts (expert_dtype DLM_MXFP4 / DLM_MXFP6): we_gate / we_up /
+     * we_down hold the packed element codes and these the packed E8M0 scales,
+     * both in the layout dlm_pack_mx writes; NULL otherwise. */
     const uint8_t* we_gate_e8;
     const uint8_t* we_up_e8;
     const uint8_t* we_down_e8;
@@ -188,28 +190,32 @@ size_t dlm_packed_weight_bytes(int32_t dtype, int32_t batch, int32_t N, int32_t 
 dlm_status dlm_pack_weight(int32_t dtype, int32_t batch, int32_t N, int32_t K, const void* src, void* dst,
                            void* stream);
 
-/* MXFP4 weight layout.  Layout only: the codes and scales of OCP MX v1.0
- * MXFP4 matrices, rearranged so that one wave's 16-byte-per-lane load fetches
- * 128 consecutive K elements of 16 rows (1 KB) and one byte per lane their 64
- * scales.  For a [N, K] matrix (K a multiple of 128, nT = K / 128; N padded to
- * a multiple of 16 with zero codes and scale code 127):
- *   codes:  the 64 bytes of row n holding elements [128 t, 128 t + 128) sit at
- *           byte ((n / 16) * nT + t) * 1024 + (n % 16) * 64, unchanged (two
- *           codes per byte, the even element in the low nibble);
+/* MX weight layout (DLM_MXFP4: 4-bit E2M1 codes, DLM_MXFP6: 6-bit E2M3
+ * codes).  Layout only: the codes and scales of OCP MX v1.0 matrices,
+ * rearranged so that one wave's loads fetch 128 consecutive K elements of 16
+ * rows (16 x RB bytes, RB = 128 * bits / 8 = 64 or 96) and one byte per lane
+ * their 64 scales.  For a [N, K] matrix (K a multiple of 128, nT = K / 128; N
+ * padded to a multiple of 16 with zero codes and scale code 127):
+ *   codes:  the RB bytes of row n holding elements [128 t, 128 t + 128) sit at
+ *           byte ((n / 16) * nT + t) * 16 RB + (n % 16) * RB, unchanged from
+ *           the row-major codes (MXFP4: two per byte, the even element in the
+ *           low nibble; MXFP6: four per 3 bytes, element 4i + j at bits 6j ..
+ *           6j + 5 of the little-endian 24-bit group i);
  *   scales: the scale of row n, elements [128 t + 32 j, 128 t + 32 j + 32) sits
  *           at byte ((n / 16) * nT + t) * 64 + (n % 16) + 16 j.
  * `batch` matrices follow one another in each.
- * dlm_packed_mxfp4_bytes: bytes of the packed codes (scales = 0) or scales
+ * dlm_packed_mx_bytes: bytes of the packed codes (scales = 0) or scales
  * (scales = 1); 0 on invalid arguments.
- * dlm_pack_mxfp4: codes device uint8 [batch, N, K / 2] (element 2i in the low
- * nibble of byte i of its row), scales device uint8 [batch, N, K / 32] (E8M0
- * codes, one per 32 elements of a row), both row-major, 16-byte aligned ->
- * dst_codes, dst_scales (device, caller-allocated, dlm_packed_mxfp4_bytes long,
- * overlapping no input); enqueued on `stream`.  E_ARG for null, misaligned or
- * overlapping pointers or batch / N / K < 1; E_SHAPE unless K % 128 == 0. */
-size_t dlm_packed_mxfp4_bytes(int32_t batch, int32_t N, int32_t K, int32_t scales);
-dlm_status dlm_pack_mxfp4(int32_t batch, int32_t N, int32_t K, const void* codes, const void* scales,
-                          void* dst_codes, void* dst_scales, void* stream);
+ * dlm_pack_mx: codes device uint8 [batch, N, K * bits / 8], scales device uint8
+ * [batch, N, K / 32] (E8M0 codes, one per 32 elements of a row), both
+ * row-major, 16-byte aligned -> dst_codes, dst_scales (device, caller-
+ * allocated, dlm_packed_mx_bytes long, overlapping no input); enqueued on
+ * `stream`.  E_DTYPE unless dtype is DLM_MXFP4 or DLM_MXFP6; E_ARG for null,
+ * misaligned or overlapping pointers or batch / N / K < 1; E_SHAPE unless
+ * K % 128 == 0. */
+size_t dlm_packed_mx_bytes(int32_t dtype, int32_t batch, int32_t N, int32_t K, int32_t scales);
+dlm_status dlm_pack_mx(int32_t dtype, int32_t batch, int32_t N, int32_t K, const void* codes, const void* scales,
+                       void* dst_codes, void* dst_scales, void* stream);
 
 /* One request.  Host struct of non-owning device pointers.
  *   kv: KV cache, bf16 (fp32 for DLM_F32 models).
@@ -389,11 +395,12 @@ dlm_status dlm_op_gemm(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int3
 size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N, int32_t K, int32_t variant,
                              int32_t splits);
 
-/* Test hook: the MoE layer's grouped expert GEMM over MXFP4 weights.  E
+/* Test hook: the MoE layer's grouped expert GEMM over MX weights (dtype
+ * DLM_MXFP4 or DLM_MXFP6, else E_DTYPE).  E
  * experts, counts: HOST int32 [E], the rows of each (>= 0; M = their sum >= 1);
  * A: device bf16 [M, K], expert 0's rows first, then expert 1's, ...; B, S
  * (and B2, S2 for swiglu): the E experts' [N, K] matrices packed by
- * dlm_pack_mxfp4.  swiglu = 0: C fp32 [M, N] = A B^T per expert; swiglu = 1:
+ * dlm_pack_mx.  swiglu = 0: C fp32 [M, N] = A B^T per expert; swiglu = 1:
  * C bf16 [M, N] = silu(A B^T) * (A B2^T).  B is decoded exactly (code value x
  * block scale); fp32 accumulation.  ws: device, dlm_op_mx_gemm_workspace(E)
  * bytes (the experts' row offsets and tile starts, copied from the host on
@@ -401,9 +408,9 @@ size_t dlm_op_gemm_workspace(int32_t dtype, int32_t swiglu, int32_t M, int32_t N
  * dlm_op_gemm.  E_ARG for null pointers, E outside [1, 256], a negative count,
  * M < 1 or a variant outside 0..5; E_SHAPE unless K % 128 == 0 and N >= 1;
  * E_WORKSPACE if ws_bytes is too small. */
-dlm_status dlm_op_mx_gemm(int32_t swiglu, int32_t E, const int32_t* counts, int32_t N, int32_t K, const void* A,
-                          const void* B, const void* S, const void* B2, const void* S2, void* C, void* ws,
-                          size_t ws_bytes, int32_t variant, float* ms, void* stream);
+dlm_status dlm_op_mx_gemm(int32_t dtype, int32_t swiglu, int32_t E, const int32_t* counts, int32_t N, int32_t K,
+                          const void* A, const void* B, const void* S, const void* B2, const void* S2, void* C,
+                          void* ws, size_t ws_bytes, int32_t variant, float* ms, void* stream);
 size_t dlm_op_mx_gemm_workspace(int32_t E);
 
 /* Test hook: the MoE layer's sort of (row, slot) assignments by expert.

@@ -33,7 +33,7 @@ DLM_DEVERR_MASK_APPEND = 2
 DLM_MAX_SEQS = 64
 DLM_STATIC_SCRATCH_BYTES = 128 << 20
 
-DLM_F32, DLM_BF16, DLM_FP8, DLM_MXFP4 = 0, 1, 2, 3
+DLM_F32, DLM_BF16, DLM_FP8, DLM_MXFP4, DLM_MXFP6 = 0, 1, 2, 3, 4
 DLM_FFN_DENSE, DLM_FFN_MOE = 0, 1
 DLM_COMMIT_TOPK, DLM_COMMIT_THRESHOLD = 0, 1
 
@@ -55,7 +55,7 @@ EXPORTS = [
     "dlm_timing_enable", "dlm_timing_read", "dlm_kernel_name", "dlm_debug_router",
     "dlm_op_quant_rows", "dlm_op_gemm", "dlm_op_gemm_workspace", "dlm_packed_weight_bytes", "dlm_pack_weight",
     "dlm_op_route", "dlm_op_route_workspace", "dlm_op_router_topk", "dlm_denoise_step_noalloc",
-    "dlm_packed_mxfp4_bytes", "dlm_pack_mxfp4", "dlm_op_mx_gemm", "dlm_op_mx_gemm_workspace",
+    "dlm_packed_mx_bytes", "dlm_pack_mx", "dlm_op_mx_gemm", "dlm_op_mx_gemm_workspace",
 ]
 DLM_GEMM_B_TILED = 0x100
 
@@ -144,10 +144,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dlm_op_route": (c_int32, [P, c_int32, c_int32, c_int32, P, P, P, P, P, c_size_t, P]),
         "dlm_op_route_workspace": (c_size_t, [c_int32, c_int32]),
         "dlm_op_router_topk": (c_int32, [P, c_int32, c_int32, c_int32, P, P, P]),
-        "dlm_packed_mxfp4_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
-        "dlm_pack_mxfp4": (c_int32, [c_int32, c_int32, c_int32, P, P, P, P, P]),
-        "dlm_op_mx_gemm": (c_int32, [c_int32, c_int32, POINTER(c_int32), c_int32, c_int32, P, P, P, P, P, P, P,
-                                     c_size_t, c_int32, POINTER(c_float), P]),
+        "dlm_packed_mx_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+        "dlm_pack_mx": (c_int32, [c_int32, c_int32, c_int32, c_int32, P, P, P, P, P]),
+        "dlm_op_mx_gemm": (c_int32, [c_int32, c_int32, c_int32, POINTER(c_int32), c_int32, c_int32, P, P, P, P, P,
+                                     P, P, c_size_t, c_int32, POINTER(c_float), P]),
         "dlm_op_mx_gemm_workspace": (c_size_t, [c_int32]),
     }
     for name, (res, args) in sig.items():

@@ -260,17 +260,21 @@ dlm_status check_config(const dlm_config* c) {
             return fail(DLM_E_SHAPE, "top_k not in [1, min(16, n_experts)]");
         if (c->d_expert < 1) return fail(DLM_E_SHAPE, "d_expert < 1");
         if (c->expert_dtype != c->dtype) {
-            if (c->expert_dtype != DLM_MXFP4 || c->dtype != DLM_BF16)
-                return fail(DLM_E_DTYPE, "expert_dtype %d with dtype %d (experts: the model's dtype, or MXFP4 "
-                            "with bf16)", c->expert_dtype, c->dtype);
+            if ((c->expert_dtype != DLM_MXFP4 && c->expert_dtype != DLM_MXFP6) || c->dtype != DLM_BF16)
+                return fail(DLM_E_DTYPE, "expert_dtype %d with dtype %d (experts: the model's dtype, or MXFP4 / "
+                            "MXFP6 with bf16)", c->expert_dtype, c->dtype);
             if (c->d_model % 128 || c->d_expert % 128)
-                return fail(DLM_E_SHAPE, "MXFP4 experts need d_model and d_expert multiples of 128");
+                return fail(DLM_E_SHAPE, "MX experts need d_model and d_expert multiples of 128");
         }
     }
     return DLM_OK;
 }
 
-bool mx_experts(const dlm_config& c) { return c.ffn == DLM_FFN_MOE && c.expert_dtype == DLM_MXFP4; }
+// Element bits of the routed experts' MX weights, 0 when they are not MX.
+int mx_bits(const dlm_config& c) {
+    if (c.ffn != DLM_FFN_MOE) return 0;
+    return c.expert_dtype == DLM_MXFP4 ? 4 : c.expert_dtype == DLM_MXFP6 ? 6 : 0;
+}
 
 dlm_status check_weights(const dlm_config* c, const dlm_weights* w) {
     if (!w) return fail(DLM_E_ARG, "weights is NULL");
@@ -288,8 +292,8 @@ dlm_status check_weights(const dlm_config* c, const dlm_weights* w) {
                 return fail(DLM_E_ARG, "layer %d: NULL expert weight", l);
             if (fp8 && (!L.we_gate_s || !L.we_up_s || !L.we_down_s))
                 return fail(DLM_E_DTYPE, "layer %d: fp8 model needs expert scales", l);
-            if (mx_experts(*c) && (!L.we_gate_e8 || !L.we_up_e8 || !L.we_down_e8))
-                return fail(DLM_E_DTYPE, "layer %d: MXFP4 experts need their E8M0 scales", l);
+            if (mx_bits(*c) && (!L.we_gate_e8 || !L.we_up_e8 || !L.we_down_e8))
+                return fail(DLM_E_DTYPE, "layer %d: MX experts need their E8M0 scales", l);
         }
     }
     return DLM_OK;
@@ -371,7 +375,8 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
     const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
     const int nqkv = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
     const int gdt = c.dtype;                       // GEMM operand type
-    const bool mx = mx_experts(c);                 // MXFP4 routed experts
+    const int mxb = mx_bits(c);                    // MX routed experts: element bits (0: not MX)
+    const bool mx = mxb != 0;
     float* x = at<float>(ws, p.x);
     void* hA = at<void>(ws, p.hA);
     uint8_t* hq = fp8 ? at<uint8_t>(ws, p.hq) : nullptr;
@@ -517,13 +522,14 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
             void* ei = at<void>(ws, p.ei);
             float* y = at<float>(ws, p.y);
             if (mx) {
-                // MXFP4 experts: gate/up with the SwiGLU epilogue, then down,
-                // on the bf16 activations
+                // MX experts: gate/up with the SwiGLU epilogue, then down, on
+                // the bf16 activations
                 MxDesc g;
+                g.bits = mxb;
                 g.swiglu = true;
                 g.A = hA; g.lda = d; g.gather = sorted; g.gather_div = k;
                 g.B = L.we_gate; g.B2 = L.we_up; g.S = L.we_gate_e8; g.S2 = L.we_up_e8;
-                g.b_stride = mx_code_bytes(De, d); g.s_stride = mx_scale_bytes(De, d);
+                g.b_stride = mx_code_bytes(mxb, De, d); g.s_stride = mx_scale_bytes(De, d);
                 g.offs = offs; g.tile_start = tstart; g.E = E;
                 g.M = A; g.N = De; g.K = d; g.C = ei; g.ldc = De;
                 {
@@ -531,9 +537,10 @@ void forward(dlm_model* m, Mode mode, const SeqTab& seqs, const IdSource& ids, v
                     mx_grouped(g, st);
                 }
                 MxDesc h;
+                h.bits = mxb;
                 h.A = ei; h.lda = De;
                 h.B = L.we_down; h.S = L.we_down_e8;
-                h.b_stride = mx_code_bytes(d, De); h.s_stride = mx_scale_bytes(d, De);
+                h.b_stride = mx_code_bytes(mxb, d, De); h.s_stride = mx_scale_bytes(d, De);
                 h.offs = offs; h.tile_start = tstart; h.E = E;
                 h.M = A; h.N = d; h.K = De; h.C = y; h.ldc = d;
                 Timed t(m, DLM_K_EXPERT_DOWN, st);
@@ -870,36 +877,39 @@ dlm_status dlm_pack_weight(int32_t dtype, int32_t batch, int32_t N, int32_t K, c
     return hip_status("dlm_pack_weight");
 }
 
-static dlm_status mx_check(int32_t batch, int32_t N, int32_t K) {
+static int mx_dtype_bits(int32_t dtype) { return dtype == DLM_MXFP4 ? 4 : dtype == DLM_MXFP6 ? 6 : 0; }
+
+static dlm_status mx_check(int32_t dtype, int32_t batch, int32_t N, int32_t K) {
+    if (!mx_dtype_bits(dtype)) return fail(DLM_E_DTYPE, "dtype %d is not an MX format", dtype);
     if (batch < 1 || N < 1 || K < 1) return fail(DLM_E_ARG, "batch / N / K < 1");
     if (K % 128) return fail(DLM_E_SHAPE, "K %d is not a multiple of 128", K);
     return DLM_OK;
 }
 
-size_t dlm_packed_mxfp4_bytes(int32_t batch, int32_t N, int32_t K, int32_t scales) {
-    if (mx_check(batch, N, K)) return 0;
-    return (size_t)batch * (size_t)(scales ? mx_scale_bytes(N, K) : mx_code_bytes(N, K));
+size_t dlm_packed_mx_bytes(int32_t dtype, int32_t batch, int32_t N, int32_t K, int32_t scales) {
+    if (mx_check(dtype, batch, N, K)) return 0;
+    return (size_t)batch * (size_t)(scales ? mx_scale_bytes(N, K) : mx_code_bytes(mx_dtype_bits(dtype), N, K));
 }
 
-dlm_status dlm_pack_mxfp4(int32_t batch, int32_t N, int32_t K, const void* codes, const void* scales,
-                          void* dst_codes, void* dst_scales, void* stream) {
+dlm_status dlm_pack_mx(int32_t dtype, int32_t batch, int32_t N, int32_t K, const void* codes, const void* scales,
+                       void* dst_codes, void* dst_scales, void* stream) {
     g_err.clear();
-    dlm_status s = mx_check(batch, N, K);
+    dlm_status s = mx_check(dtype, batch, N, K);
     if (s) return s;
     if (!codes || !scales || !dst_codes || !dst_scales) return fail(DLM_E_ARG, "null pointer");
     if (((uintptr_t)codes | (uintptr_t)dst_codes) % 16) return fail(DLM_E_ARG, "codes not 16-byte aligned");
     struct Range { uintptr_t lo, hi; };
     const Range r[4] = {
-        {(uintptr_t)codes, (uintptr_t)codes + (size_t)batch * N * (K / 2)},
+        {(uintptr_t)codes, (uintptr_t)codes + (size_t)batch * N * ((size_t)K * mx_dtype_bits(dtype) / 8)},
         {(uintptr_t)scales, (uintptr_t)scales + (size_t)batch * N * (K / 32)},
-        {(uintptr_t)dst_codes, (uintptr_t)dst_codes + dlm_packed_mxfp4_bytes(batch, N, K, 0)},
-        {(uintptr_t)dst_scales, (uintptr_t)dst_scales + dlm_packed_mxfp4_bytes(batch, N, K, 1)}};
+        {(uintptr_t)dst_codes, (uintptr_t)dst_codes + dlm_packed_mx_bytes(dtype, batch, N, K, 0)},
+        {(uintptr_t)dst_scales, (uintptr_t)dst_scales + dlm_packed_mx_bytes(dtype, batch, N, K, 1)}};
     for (int i = 0; i < 4; ++i)
         for (int j = i + 1; j < 4; ++j)
             if ((i >= 2 || j >= 2) && r[i].lo < r[j].hi && r[j].lo < r[i].hi)
                 return fail(DLM_E_ARG, "packed output overlaps another buffer");
-    mx_pack(batch, N, K, codes, scales, dst_codes, dst_scales, (hipStream_t)stream);
-    return hip_status("dlm_pack_mxfp4");
+    mx_pack(mx_dtype_bits(dtype), batch, N, K, codes, scales, dst_codes, dst_scales, (hipStream_t)stream);
+    return hip_status("dlm_pack_mx");
 }
 
 size_t dlm_op_mx_gemm_workspace(int32_t E) {
@@ -907,10 +917,11 @@ size_t dlm_op_mx_gemm_workspace(int32_t E) {
     return 2 * align_up((size_t)(E + 1) * 4);
 }
 
-dlm_status dlm_op_mx_gemm(int32_t swiglu, int32_t E, const int32_t* counts, int32_t N, int32_t K, const void* A,
-                          const void* B, const void* S, const void* B2, const void* S2, void* C, void* ws,
-                          size_t ws_bytes, int32_t variant, float* ms, void* stream) {
+dlm_status dlm_op_mx_gemm(int32_t dtype, int32_t swiglu, int32_t E, const int32_t* counts, int32_t N, int32_t K,
+                          const void* A, const void* B, const void* S, const void* B2, const void* S2, void* C,
+                          void* ws, size_t ws_bytes, int32_t variant, float* ms, void* stream) {
     g_err.clear();
+    if (!mx_dtype_bits(dtype)) return fail(DLM_E_DTYPE, "dtype %d is not an MX format", dtype);
     if (!counts || !A || !B || !S || !C || !ws || (swiglu && (!B2 || !S2))) return fail(DLM_E_ARG, "null pointer");
     if (E < 1 || E > 256) return fail(DLM_E_ARG, "E %d not in [1, 256]", E);
     if (variant < 0 || variant > mx_variants()) return fail(DLM_E_ARG, "variant %d not in 0..%d", variant, mx_variants());
@@ -939,10 +950,11 @@ dlm_status dlm_op_mx_gemm(int32_t swiglu, int32_t E, const int32_t* counts, int3
     if (e == hipSuccess) e = hipStreamSynchronize(st);   // `host` dies with this call
     if (e != hipSuccess) return fail(DLM_E_HIP, "dlm_op_mx_gemm: %s", hipGetErrorString(e));
     MxDesc d;
+    d.bits = mx_dtype_bits(dtype);
     d.swiglu = swiglu != 0;
     d.A = A; d.lda = K;
     d.B = B; d.B2 = B2; d.S = S; d.S2 = S2;
-    d.b_stride = mx_code_bytes(N, K); d.s_stride = mx_scale_bytes(N, K);
+    d.b_stride = mx_code_bytes(d.bits, N, K); d.s_stride = mx_scale_bytes(N, K);
     d.offs = offs; d.tile_start = tstart; d.E = E;
     d.M = (int)M; d.N = N; d.K = K; d.C = C; d.ldc = N;
     d.variant = variant;

@@ -96,23 +96,25 @@ long gemm_splitk_floats(const GemmDesc& d);
 // the narrowest tile is used for M <= 64
 int lm_head_tile_n(int M);
 
-// MXFP4 expert weights (mxfp4.hip).  Packed layout of a [N, K] matrix (K a
-// multiple of 128, N padded to a multiple of 16): codes in blocks of 16 rows x
-// 64 bytes (128 E2M1 codes per row, the even element in the low nibble), block
-// (g, t) at byte (g * K / 128 + t) * 1024; E8M0 scales in blocks of 64 bytes,
-// block (g, t) at byte (g * K / 128 + t) * 64, byte r + 16 j = row 16 g + r,
-// elements 128 t + 32 j .. + 32.  Matrices of a batch follow one another.
-long mx_code_bytes(int N, int K);
+// MX expert weights (mx.hip): MXFP4 (E2M1, bits = 4) and MXFP6 (E2M3, bits =
+// 6).  Packed layout of a [N, K] matrix (K a multiple of 128, N padded to a
+// multiple of 16): codes in blocks of 16 rows x RB bytes (RB = 128 * bits / 8,
+// the row-major code bytes of 128 elements), block (g, t) at byte (g * K / 128
+// + t) * 16 RB; E8M0 scales in blocks of 64 bytes, block (g, t) at byte (g * K
+// / 128 + t) * 64, byte r + 16 j = row 16 g + r, elements 128 t + 32 j .. + 32.
+// Matrices of a batch follow one another.
+long mx_code_bytes(int bits, int N, int K);
 long mx_scale_bytes(int N, int K);
-// codes [batch, N, K / 2] and scales [batch, N, K / 32] row-major -> packed
-void mx_pack(int batch, int N, int K, const void* codes, const void* scales, void* dst_codes, void* dst_scales,
-             hipStream_t st);
-// m-tile rows of the MXFP4 grouped GEMM (the routing's tile height for it)
+// codes [batch, N, K * bits / 8] and scales [batch, N, K / 32] row-major -> packed
+void mx_pack(int bits, int batch, int N, int K, const void* codes, const void* scales, void* dst_codes,
+             void* dst_scales, hipStream_t st);
+// m-tile rows of the MX grouped GEMM (the routing's tile height for it)
 int mx_grouped_bm();
 // Grouped expert GEMM with bf16 A [M, K] (rows in expert order, or gathered as
-// in GemmDesc) and MXFP4 B: swiglu -> C bf16 = silu(A B^T) * (A B2^T), else
+// in GemmDesc) and MX B: swiglu -> C bf16 = silu(A B^T) * (A B2^T), else
 // C fp32 = A B^T.  offs / tile_start as for gemm_grouped with mx_grouped_bm().
 struct MxDesc {
+    int bits = 4;                                 // 4: MXFP4 (E2M1), 6: MXFP6 (E2M3)
     bool swiglu = false;
     const void* A = nullptr; long lda = 0;        // elements
     const int* gather = nullptr; int gather_div = 1;

@@ -1,32 +1,37 @@
-// MXFP4 expert weights (OCP Microscaling Formats v1.0, MXFP4: E2M1 elements
-// in blocks of 32 sharing one E8M0 power-of-two scale): the packed layout, its
-// packer, and the grouped expert GEMM that reads it.
+// MX expert weights (OCP Microscaling Formats v1.0: elements in blocks of 32
+// sharing one E8M0 power-of-two scale), in two element formats: MXFP4 (E2M1,
+// 4 bits) and MXFP6 (E2M3, 6 bits).  The packed layout, its packer, and the
+// grouped expert GEMM that reads it.
 //
-// Arithmetic: W4A16.  Each weight is its E2M1 value times its block's scale,
-// widened exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4: an E2M1
+// Arithmetic: weights-only quantisation.  Each weight is its element value
+// times its block's scale, widened exactly to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp4 / v_cvt_scalef32_pk32_bf16_fp6: an E2M1 or E2M3
 // value times a power of two is a bf16 value unless it leaves bf16's range),
 // multiplied with the bf16 activations on the bf16 MFMA, fp32 accumulation --
 // the same products and sums as a bf16 model whose expert weights are the
-// decoded MXFP4 values.  Only the bytes in HBM shrink: 4.25 bits per weight.
+// decoded MX values.  Only the bytes in HBM shrink: 4.25 or 6.25 bits a weight.
 //
 // Packed layout of one [N, K] matrix (K a multiple of 128, N padded to a
-// multiple of 16 with zero codes), nT = K / 128 super-steps of 128 elements:
-//   codes:  block (g, t) of 16 rows x 64 bytes at byte (g * nT + t) * 1024;
-//           row r of the block at +64 r holds elements [128 t, 128 t + 128)
-//           of row 16 g + r, two per byte, the even element in the low nibble
-//           (the row-major bytes, moved whole).
+// multiple of 16 with zero codes), nT = K / 128 super-steps of 128 elements,
+// RB = 128 * bits / 8 code bytes per row and super-step (64 or 96):
+//   codes:  block (g, t) of 16 rows x RB bytes at byte (g * nT + t) * 16 RB;
+//           row r of the block at +RB r holds elements [128 t, 128 t + 128)
+//           of row 16 g + r as in the row-major codes (MXFP4: two per byte,
+//           the even element in the low nibble; MXFP6: four per 3 bytes,
+//           element 4i + j at bits 6j of the little-endian 24-bit group i),
+//           moved whole.
 //   scales: block (g, t) of 64 bytes at byte (g * nT + t) * 64; byte r + 16 j
 //           is the E8M0 code of row 16 g + r, elements [128 t + 32 j, + 32).
-// Experts follow one another.  A wave loads one code block per super-step and
-// 16-row tile with one 16-byte load per lane (lane l: row l % 16, elements
-// 32 (l / 16) .. + 32, one scale block) and the 64 scale bytes with one byte
-// per lane, both contiguous.
+// Experts follow one another.  A wave reads one code block per super-step and
+// 16-row tile, lane l taking row l % 16, elements 32 (l / 16) .. + 32 -- one
+// scale block: 16 bytes (MXFP4, one load) or 24 (MXFP6, three 8-byte loads)
+// -- and the 64 scale bytes with one byte per lane, all contiguous.
 //
 // The MFMA's K order inside a super-step is permuted, identically for both
 // operands: MFMA k-step s (of 4) takes, on lane group q = l / 16, elements
-// 32 q + 8 s .. + 8 -- the lane's own dword s of codes -- so each lane widens
-// the codes it loaded without any exchange; the activation rows are read from
-// LDS at the same element offsets.
+// 32 q + 8 s .. + 8 of the lane's own codes, so each lane widens the codes it
+// loaded without any exchange; the activation rows are read from LDS at the
+// same element offsets.
 //
 // Data movement.  A workgroup is NW compute waves plus NPROD producer waves.
 // The producers copy the expert m-tile's activation rows (gathered through the
@@ -43,32 +48,32 @@
 namespace dlm {
 
 constexpr int MX_SUPER = 128;        // K elements per super-step
-constexpr int MX_CODE_BLOCK = 1024;  // code bytes per (16 rows, super-step)
 constexpr int MX_SCALE_BLOCK = 64;   // scale bytes per (16 rows, super-step)
 constexpr int MX_BM = 64;            // expert m-tile rows
 
 int mx_grouped_bm() { return MX_BM; }
 
-long mx_code_bytes(int N, int K) { return packed_rows(N) * (long)K / 2; }
+long mx_code_bytes(int bits, int N, int K) { return packed_rows(N) * (long)K * bits / 8; }
 long mx_scale_bytes(int N, int K) { return packed_rows(N) * (long)K / 32; }
 
 // ------------------------------------------------------------- packing --
 
-// One thread per 16 bytes of packed codes: block (b, g, t), 16-byte piece p of
-// the block = row p / 4, bytes 16 (p % 4) .. + 16 of the row's 64.
-__global__ __launch_bounds__(256) void mx_pack_codes_kernel(const uint8_t* src, uint8_t* dst, int N, int K,
+// One thread per 8 bytes of packed codes: block (b, g, t) of 16 rows x rb
+// bytes, 8-byte piece p of the block = row p / (rb / 8), bytes 8 (p % (rb /
+// 8)) .. + 8 of the row's rb.
+__global__ __launch_bounds__(256) void mx_pack_codes_kernel(const uint8_t* src, uint8_t* dst, int N, int K, int rb,
                                                             long per_matrix, long total) {
     const long c = (long)blockIdx.x * 256 + threadIdx.x;
     if (c >= total) return;
-    const int nT = K / MX_SUPER;
+    const int nT = K / MX_SUPER, ppr = rb / 8;
     const long b = c / per_matrix, i = c % per_matrix;
-    const long blk = i / 64;
-    const int p = (int)(i % 64);
+    const long blk = i / (16 * ppr);
+    const int p = (int)(i % (16 * ppr));
     const long g = blk / nT, t = blk % nT;
-    const long n = g * 16 + p / 4;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (n < N) v = *(const uint4*)(src + (b * N + n) * (long)(K / 2) + t * 64 + (p % 4) * 16);
-    *(uint4*)(dst + c * 16) = v;
+    const long n = g * 16 + p / ppr;
+    uint2 v = {0u, 0u};
+    if (n < N) v = *(const uint2*)(src + (b * N + n) * (long)nT * rb + t * rb + (p % ppr) * 8);
+    *(uint2*)(dst + c * 8) = v;
 }
 
 // One thread per packed scale byte: block (b, g, t), byte r + 16 j.  Rows past
@@ -86,12 +91,12 @@ __global__ __launch_bounds__(256) void mx_pack_scales_kernel(const uint8_t* src,
     dst[c] = n < N ? src[(b * N + n) * (long)(K / 32) + t * 4 + p / 16] : (uint8_t)127;
 }
 
-void mx_pack(int batch, int N, int K, const void* codes, const void* scales, void* dst_codes, void* dst_scales,
-             hipStream_t st) {
-    const long pc = mx_code_bytes(N, K) / 16, ps = mx_scale_bytes(N, K);
+void mx_pack(int bits, int batch, int N, int K, const void* codes, const void* scales, void* dst_codes,
+             void* dst_scales, hipStream_t st) {
+    const long pc = mx_code_bytes(bits, N, K) / 8, ps = mx_scale_bytes(N, K);
     if (pc * batch > 0)
         launch(mx_pack_codes_kernel, dim3((unsigned)((pc * batch + 255) / 256)), dim3(256), 0, st,
-               (const uint8_t*)codes, (uint8_t*)dst_codes, N, K, pc, pc * batch);
+               (const uint8_t*)codes, (uint8_t*)dst_codes, N, K, MX_SUPER * bits / 8, pc, pc * batch);
     if (ps * batch > 0)
         launch(mx_pack_scales_kernel, dim3((unsigned)((ps * batch + 255) / 256)), dim3(256), 0, st,
                (const uint8_t*)scales, (uint8_t*)dst_scales, N, K, ps, ps * batch);
@@ -100,6 +105,8 @@ void mx_pack(int batch, int N, int K, const void* codes, const void* scales, voi
 // ------------------------------------------------------- grouped GEMM --
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 
 // E8M0 code -> its scale 2^(e - 127) as fp32 (code 0 is 2^-127, an fp32
 // subnormal; 255 is NaN).  Branch-free: ldexp, then one select.
@@ -118,6 +125,22 @@ __device__ __forceinline__ bf16x8 widen_fp4x8(uint32_t w, float scale) {
     return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// A lane's codes of one super-step and tile (32 elements, one scale block).
+template <int BITS> struct MxCodes;
+template <> struct MxCodes<4> {
+    static constexpr int LOADS = 1;                          // global loads per super-step
+    u32x4 w;
+    __device__ __forceinline__ void load(const uint8_t* p) { w = *(const u32x4*)p; }
+};
+template <> struct MxCodes<6> {
+    static constexpr int LOADS = 3;
+    uint2 w[3];
+    __device__ __forceinline__ void load(const uint8_t* p) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) w[i] = *(const uint2*)(p + 8 * i);
+    }
+};
+
 struct MxArgs {
     const uint8_t* A; long lda;          // bf16 rows, lda in bytes
     const int* gather; int gather_div;   // A row of permuted row p = gather[p] / gather_div (nullable)
@@ -129,8 +152,12 @@ struct MxArgs {
     void* C; long ldc;                   // elements
 };
 
-template <bool DUAL, int NW, int TNW, int SPC, int P, int NBUF, int NPROD>
+template <int BITS, bool DUAL, int NW, int TNW, int SPC, int P, int NBUF, int NPROD>
 struct MxCfg {
+    static constexpr int FMT = BITS;                     // element bits: 4 (E2M1) or 6 (E2M3)
+    static constexpr int RB = MX_SUPER * BITS / 8;       // code bytes per row and super-step
+    static constexpr int CODE_BLOCK = 16 * RB;           // code bytes per (16 rows, super-step)
+    static constexpr int LPG = (MxCodes<BITS>::LOADS + 1) * TNW * (DUAL ? 2 : 1);   // loads per super-step
     static constexpr bool TWO = DUAL;
     static constexpr int NWAVES = NW, TN = TNW, CH = SPC, D = P * SPC, NA = NBUF, NP = NPROD;
     static constexpr int NB = TNW * (DUAL ? 2 : 1);      // weight tiles per wave
@@ -139,7 +166,7 @@ struct MxCfg {
     static constexpr int ABUF = MX_BM * RS;              // one LDS buffer
     static constexpr int THREADS = (NW + NPROD) * WAVE;
     static_assert(RS <= 1024 && 1024 % RS == 0, "a 1 KB DMA covers whole rows");
-    static_assert(2 * NB * (D - 1) < 64, "vmcnt");
+    static_assert(LPG * (D - 1) < 64, "vmcnt");
     static_assert(NBUF >= 2 && NBUF * ABUF <= 160 * 1024, "A ring fits LDS");
 };
 
@@ -199,8 +226,8 @@ __device__ __forceinline__ void mx_compute(const uint8_t* smem, const MxArgs& a,
         const int j = b % G::TN;
         const int g = min((colw + j * 16) / 16, gmax);      // tiles past N read the last (not stored)
         const bool second = G::TWO && b >= G::TN;
-        cb[b] = (second ? a.B2 : a.B) + (long)ex * a.b_stride + ((long)g * nT) * MX_CODE_BLOCK + (lane % 16) * 64 +
-                (lane / 16) * 16;
+        cb[b] = (second ? a.B2 : a.B) + (long)ex * a.b_stride + ((long)g * nT) * G::CODE_BLOCK + (lane % 16) * G::RB +
+                (lane / 16) * (G::RB / 4);
         sb[b] = (second ? a.S2 : a.S) + (long)ex * a.s_stride + ((long)g * nT) * MX_SCALE_BLOCK + lane;
     }
     f32x4 acc[TMA][NB];
@@ -209,12 +236,12 @@ __device__ __forceinline__ void mx_compute(const uint8_t* smem, const MxArgs& a,
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[i][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 code[D][NB];
+    MxCodes<G::FMT> code[D][NB];
     uint32_t sc[D][NB];
-    auto issue = [&](int t, u32x4 (&cd)[NB], uint32_t (&s)[NB]) {
+    auto issue = [&](int t, MxCodes<G::FMT> (&cd)[NB], uint32_t (&s)[NB]) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            cd[b] = *(const u32x4*)(cb[b] + (long)t * MX_CODE_BLOCK);
+            cd[b].load(cb[b] + (long)t * G::CODE_BLOCK);
             s[b] = sb[b][(long)t * MX_SCALE_BLOCK];
         }
     };
@@ -226,6 +253,17 @@ __device__ __forceinline__ void mx_compute(const uint8_t* smem, const MxArgs& a,
         float scale[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) scale[b] = e8m0_scale(sc[p][b]);
+        // MXFP6: the lane's 32 codes of each tile widened at once (elements 8 s
+        // .. + 8 feed k-step s)
+        bf16x32_t w6[G::FMT == 6 ? NB : 1];
+        if constexpr (G::FMT == 6) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint2* c = code[p][b].w;
+                w6[b] = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(u32x6{c[0].x, c[0].y, c[1].x, c[1].y, c[2].x, c[2].y},
+                                                                      scale[b]);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             bf16x8 af[TMA];
@@ -234,7 +272,14 @@ __device__ __forceinline__ void mx_compute(const uint8_t* smem, const MxArgs& a,
             for (int i = 0; i < TMA; ++i) af[i] = *(const bf16x8*)(abuf + (i * 16 + r) * G::RS + ((q ^ r) << 4));
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const bf16x8 bf = widen_fp4x8(code[p][b][s], scale[b]);
+                bf16x8 bf;
+                if constexpr (G::FMT == 4) {
+                    bf = widen_fp4x8(code[p][b].w[s], scale[b]);
+                } else {
+                    const bf16x32_t& v = w6[b];
+                    bf = bf16x8{v[8 * s], v[8 * s + 1], v[8 * s + 2], v[8 * s + 3], v[8 * s + 4], v[8 * s + 5],
+                                v[8 * s + 6], v[8 * s + 7]};
+                }
 #pragma unroll
                 for (int i = 0; i < TMA; ++i)
                     acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][b], 0, 0, 0);
@@ -251,7 +296,7 @@ __device__ __forceinline__ void mx_compute(const uint8_t* smem, const MxArgs& a,
 #pragma unroll
         for (int p = 0; p < D; ++p) {
             const int t = t0 + p;
-            wait_vm<2 * NB * (D - 1)>();
+            wait_vm<G::LPG * (D - 1)>();
             // no instruction of a later step is scheduled before this wait
             // (the compiler would wait for that step's loads here)
             __builtin_amdgcn_sched_barrier(0);
@@ -351,27 +396,28 @@ __global__ __launch_bounds__(G::THREADS) void mx_grouped_kernel(MxArgs a) {
 // matter most: one wave issuing every A copy was the bottleneck (a sweep on
 // the 26B-class canvas step's expert shapes, 2048 assignments over 58
 // experts: 69 -> 45 us for gate/up with four).
-template <bool DUAL, class F>
+template <int BITS, bool DUAL, class F>
 static bool mx_with_variant(int v, F f) {
     switch (v) {
-        case 0:
-            if constexpr (DUAL) f(MxCfg<DUAL, 4, 2, 2, 1, 2, 4>{});
-            else f(MxCfg<DUAL, 8, 2, 2, 1, 2, 4>{});
+        case 0:   // 6-bit codes hold 50% more registers in flight: the pair takes 8 waves x 1 tile
+            if constexpr (DUAL && BITS == 4) f(MxCfg<BITS, DUAL, 4, 2, 2, 1, 2, 4>{});
+            else if constexpr (DUAL) f(MxCfg<BITS, DUAL, 8, 1, 2, 1, 2, 4>{});
+            else f(MxCfg<BITS, DUAL, 8, 2, 2, 1, 2, 4>{});
             return true;
-        case 1: f(MxCfg<DUAL, 4, DUAL ? 2 : 4, 2, 1, 3, 4>{}); return true;
-        case 2: f(MxCfg<DUAL, 4, DUAL ? 2 : 4, 1, 3, 4, 4>{}); return true;
-        case 3: f(MxCfg<DUAL, 8, DUAL ? 1 : 2, 2, 2, 4, 4>{}); return true;
-        case 4: f(MxCfg<DUAL, 4, DUAL ? 2 : 4, 2, 1, 4, 1>{}); return true;
-        case 5: f(MxCfg<DUAL, 4, DUAL ? 2 : 4, 2, 1, 2, 2>{}); return true;
+        case 1: f(MxCfg<BITS, DUAL, 4, DUAL ? 2 : 4, 2, 1, 3, 4>{}); return true;
+        case 2: f(MxCfg<BITS, DUAL, 4, DUAL ? 2 : 4, 1, 3, 4, 4>{}); return true;
+        case 3: f(MxCfg<BITS, DUAL, 8, DUAL ? 1 : 2, 2, 2, 4, 4>{}); return true;
+        case 4: f(MxCfg<BITS, DUAL, 4, DUAL ? 2 : 4, 2, 1, 4, 1>{}); return true;
+        case 5: f(MxCfg<BITS, DUAL, 4, DUAL ? 2 : 4, 2, 1, 2, 2>{}); return true;
         default: return false;
     }
 }
 constexpr int MX_VARIANTS = 5;
 int mx_variants() { return MX_VARIANTS; }
 
-template <bool DUAL>
+template <int BITS, bool DUAL>
 static void mx_launch(const MxDesc& d, hipStream_t st) {
-    mx_with_variant<DUAL>(d.variant, [&](auto g) {
+    mx_with_variant<BITS, DUAL>(d.variant, [&](auto g) {
         using G = decltype(g);
         MxArgs a;
         a.A = (const uint8_t*)d.A; a.lda = d.lda * 2;
@@ -390,8 +436,13 @@ static void mx_launch(const MxDesc& d, hipStream_t st) {
 }
 
 void mx_grouped(const MxDesc& d, hipStream_t st) {
-    if (d.swiglu) mx_launch<true>(d, st);
-    else mx_launch<false>(d, st);
+    if (d.bits == 6) {
+        if (d.swiglu) mx_launch<6, true>(d, st);
+        else mx_launch<6, false>(d, st);
+    } else {
+        if (d.swiglu) mx_launch<4, true>(d, st);
+        else mx_launch<4, false>(d, st);
+    }
 }
 
 }  // namespace dlm

@@ -24,7 +24,10 @@ import torch
 from . import abi
 from .abi import check
 
-_DTYPES = {"f32": abi.DLM_F32, "bf16": abi.DLM_BF16, "fp8": abi.DLM_FP8, "mxfp4": abi.DLM_MXFP4}
+_DTYPES = {"f32": abi.DLM_F32, "bf16": abi.DLM_BF16, "fp8": abi.DLM_FP8, "mxfp4": abi.DLM_MXFP4,
+           "mxfp6": abi.DLM_MXFP6}
+# MX expert formats: (key suffix of the codes, element bits)
+_MX = {"mxfp4": (".q4", 4), "mxfp6": (".q6", 6)}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -194,21 +197,23 @@ class DLM:
         self._keep.append(dst)
         return dst
 
-    def _mx(self, weights, name):
-        """(packed codes pointer, packed scales pointer) of an MXFP4 expert
-        tensor: codes `name.q4` uint8 [E, N, K / 2] and E8M0 scales `name.e8`
-        uint8 [E, N, K / 32], rearranged by dlm_pack_mxfp4 (a kernel on the
-        current stream)."""
-        q = weights[name + ".q4"].to(self.device).contiguous()
+    def _mx(self, weights, name, fmt):
+        """(packed codes pointer, packed scales pointer) of an MX expert tensor:
+        codes `name.q4` (MXFP4) or `name.q6` (MXFP6) uint8 [E, N, K * bits /
+        8] and E8M0 scales `name.e8` uint8 [E, N, K / 32], rearranged by
+        dlm_pack_mx (a kernel on the current stream)."""
+        suffix, bits = _MX[fmt]
+        q = weights[name + suffix].to(self.device).contiguous()
         e = weights[name + ".e8"].to(self.device).contiguous()
-        E, N, K = q.shape[0], q.shape[1], q.shape[2] * 2
-        nc = self.lib.dlm_packed_mxfp4_bytes(E, N, K, 0)
-        ns = self.lib.dlm_packed_mxfp4_bytes(E, N, K, 1)
+        E, N, K = q.shape[0], q.shape[1], q.shape[2] * 8 // bits
+        dt = _DTYPES[fmt]
+        nc = self.lib.dlm_packed_mx_bytes(dt, E, N, K, 0)
+        ns = self.lib.dlm_packed_mx_bytes(dt, E, N, K, 1)
         if nc == 0 or ns == 0 or tuple(e.shape) != (E, N, K // 32):
-            raise ValueError(f"cannot pack MXFP4 {name}: codes {tuple(q.shape)}, scales {tuple(e.shape)}")
+            raise ValueError(f"cannot pack {fmt} {name}: codes {tuple(q.shape)}, scales {tuple(e.shape)}")
         dc = torch.empty(nc, dtype=torch.uint8, device=self.device)
         ds = torch.empty(ns, dtype=torch.uint8, device=self.device)
-        check(self.lib.dlm_pack_mxfp4(E, N, K, _ptr(q), _ptr(e), _ptr(dc), _ptr(ds), _stream()), "dlm_pack_mxfp4")
+        check(self.lib.dlm_pack_mx(dt, E, N, K, _ptr(q), _ptr(e), _ptr(dc), _ptr(ds), _stream()), "dlm_pack_mx")
         self._keep += [dc, ds]
         return _ptr(dc), _ptr(ds)
 
@@ -240,10 +245,11 @@ class DLM:
             L.w_down, L.w_down_s = self._proj(weights, p + "w_down")
             if cfg.ffn == "moe":
                 L.w_router = _ptr(self._dev(weights[p + "w_router"]))
-                if getattr(cfg, "expert_dtype", None) == "mxfp4":
-                    L.we_gate, L.we_gate_e8 = self._mx(weights, p + "we_gate")
-                    L.we_up, L.we_up_e8 = self._mx(weights, p + "we_up")
-                    L.we_down, L.we_down_e8 = self._mx(weights, p + "we_down")
+                fmt = getattr(cfg, "expert_dtype", None)
+                if fmt in _MX:
+                    L.we_gate, L.we_gate_e8 = self._mx(weights, p + "we_gate", fmt)
+                    L.we_up, L.we_up_e8 = self._mx(weights, p + "we_up", fmt)
+                    L.we_down, L.we_down_e8 = self._mx(weights, p + "we_down", fmt)
                 else:
                     L.we_gate, L.we_gate_s = self._proj(weights, p + "we_gate")
                     L.we_up, L.we_up_s = self._proj(weights, p + "we_up")

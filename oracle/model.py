@@ -39,7 +39,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-from .numerics import e4m3_decode, mxfp4_decode, quant_per_token_e4m3, round_bf16
+from .numerics import e4m3_decode, mxfp4_decode, mxfp6_decode, quant_per_token_e4m3, round_bf16
 
 NEG_INF = -np.inf
 
@@ -128,6 +128,15 @@ class OracleWeights:
                 packed = t.detach().cpu().numpy()
                 codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(*packed.shape[:-1], -1)
                 self.w[name[:-3]] = mxfp4_decode(codes, tensors[name[:-3] + ".e8"].detach().cpu().numpy())
+            elif name.endswith(".q6"):
+                # MXFP6 (E2M3): four 6-bit codes per 3 bytes (element 4i + j at bits
+                # 6j of the little-endian 24-bit group i), E8M0 block scales
+                b = t.detach().cpu().numpy().astype(np.uint32)
+                g = b.reshape(*b.shape[:-1], -1, 3)
+                bits = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+                codes = np.stack([(bits >> (6 * j)) & 63 for j in range(4)], axis=-1).reshape(*b.shape[:-1], -1)
+                self.w[name[:-3]] = mxfp6_decode(codes.astype(np.uint8),
+                                                 tensors[name[:-3] + ".e8"].detach().cpu().numpy())
             elif name.endswith(".e8"):
                 pass
             else:

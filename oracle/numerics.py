@@ -12,7 +12,10 @@ value (no intermediate fp32 rounding).
 Pins: round_bf16 against torch's fp32->bf16 conversion over fp32 bit patterns;
 e4m3_decode against the format's definition for all 256 codes and against
 torch.float8_e4m3fn; e4m3_encode against torch on in-range values, at every
-midpoint, and for saturation.
+midpoint, and for saturation.  The OCP Microscaling (MX v1.0) element formats
+E2M1 (MXFP4) and E2M3 (MXFP6): the value tables against the specification's,
+rounding by brute force over the representable values, the block quantisers'
+shared exponents, error bounds and round trips (tests/test_oracle_mxfp4.py).
 """
 from __future__ import annotations
 
@@ -193,5 +196,67 @@ def mxfp4_decode(codes, scales) -> np.ndarray:
     [..., K / 32]."""
     codes = np.asarray(codes, dtype=np.uint8)
     v = _E2M1_TABLE[codes]
+    s = e8m0_decode(scales)
+    return (v.reshape(*v.shape[:-1], -1, MX_BLOCK) * s[..., None]).reshape(v.shape)
+
+
+# ---- MXFP6 (OCP Microscaling v1.0, E2M3 elements) ------------------------------
+E2M3_MAX = 7.5
+E2M3_EMAX = 2          # exponent of the largest normal E2M3 value (7.5 = 1.875 * 2^2)
+
+
+def e2m3_decode_table() -> np.ndarray:
+    """Value of each of the 64 E2M3 codes: sign bit 5, exponent bits 4..3 with
+    bias 1, mantissa bits 2..0; exponent field 0 holds the subnormal m / 8; no
+    infinity or NaN."""
+    vals = np.empty(64, dtype=np.float64)
+    for code in range(64):
+        sgn = -1.0 if code & 32 else 1.0
+        e, m = (code >> 3) & 3, code & 7
+        vals[code] = sgn * (m / 8.0 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 1))
+    return vals
+
+
+_E2M3_TABLE = e2m3_decode_table()
+
+
+def e2m3_round(x) -> np.ndarray:
+    """Nearest E2M3 value, ties to the even mantissa, saturating at +-7.5.  The
+    magnitudes lie on a grid of spacing 1/8 below 2 (subnormals and exponent
+    1), 1/4 in [2, 4) and 1/2 in [4, 7.5]; on each grid the even multiples are
+    the codes with an even mantissa."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -E2M3_MAX, E2M3_MAX)
+    a = np.abs(x)
+    step = np.where(a < 2.0, 0.125, np.where(a < 4.0, 0.25, 0.5))
+    return np.copysign(np.round(a / step) * step, x)
+
+
+def e2m3_encode(x) -> np.ndarray:
+    """Codes of e2m3_round(x) (zero keeps the sign of x)."""
+    v = e2m3_round(x)
+    idx = np.searchsorted(_E2M3_TABLE[:32], np.abs(v))
+    return np.where(np.signbit(v), idx | 32, idx).astype(np.uint8)
+
+
+def mxfp6_quantize(w: np.ndarray):
+    """MXFP6 (E2M3) quantisation of the last axis (a multiple of 32): per block
+    of 32 the shared exponent is floor(log2(max |w|)) - 2, clamped to E8M0's
+    [-127, 127] (an all-zero block takes exponent 0), and each element is
+    e2m3_round(w / 2^exponent).  Returns (E2M3 codes uint8 with w's shape,
+    E8M0 scale codes uint8 [..., K / 32])."""
+    w = np.asarray(w, dtype=np.float64)
+    blocks = w.reshape(*w.shape[:-1], w.shape[-1] // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.clip(np.where(amax > 0, e - 1 - E2M3_EMAX, 0), -127, 127)
+    codes = e2m3_encode(blocks / np.ldexp(1.0, shared)[..., None])
+    return codes.reshape(w.shape), (shared + 127).astype(np.uint8)
+
+
+def mxfp6_decode(codes, scales) -> np.ndarray:
+    """Values of MXFP6 (E2M3) data: codes [..., K] times their blocks' E8M0
+    scales [..., K / 32]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    v = _E2M3_TABLE[codes]
     s = e8m0_decode(scales)
     return (v.reshape(*v.shape[:-1], -1, MX_BLOCK) * s[..., None]).reshape(v.shape)

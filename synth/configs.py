@@ -40,7 +40,7 @@ class ModelConfig:
     init_std: float = 0.02
     router_std: Optional[float] = None   # None -> d_model ** -0.5
     lm_head_std: Optional[float] = None  # None -> init_std; larger values give peaked confidences
-    expert_dtype: Optional[str] = None   # MoE experts' storage when it differs from dtype: "mxfp4"
+    expert_dtype: Optional[str] = None   # MoE experts' storage when it differs from dtype: "mxfp4", "mxfp6"
 
     @property
     def q_dim(self) -> int:
@@ -118,6 +118,9 @@ MOE_FP8 = replace(MOE_BF16, name="moe-26b-a3b-fp8", dtype="fp8")
 # the same model with its routed experts' weights in MXFP4 (4.25 bits per weight)
 MOE_MXFP4 = replace(MOE_BF16, name="moe-26b-a3b-mxfp4", expert_dtype="mxfp4")
 
+# ... and in MXFP6, E2M3 elements (6.25 bits per weight)
+MOE_MXFP6 = replace(MOE_BF16, name="moe-26b-a3b-mxfp6", expert_dtype="mxfp6")
+
 # Reduced models for oracle-speed parity: same structure, small dims, ragged
 # vocab (not a multiple of any tile) so tails are exercised.
 DENSE_BF16_MINI = ModelConfig(
@@ -132,6 +135,7 @@ MOE_BF16_MINI = ModelConfig(
 MOE_FP8_MINI = replace(MOE_BF16_MINI, name="moe-mini-fp8", dtype="fp8")
 
 MOE_MXFP4_MINI = replace(MOE_BF16_MINI, name="moe-mini-mxfp4", expert_dtype="mxfp4")
+MOE_MXFP6_MINI = replace(MOE_BF16_MINI, name="moe-mini-mxfp6", expert_dtype="mxfp6")
 
 DENSE_FP8_MINI = replace(DENSE_BF16_MINI, name="dense-mini-fp8", dtype="fp8")
 
@@ -159,6 +163,9 @@ RUNS = {
     # 3 with MXFP4 routed experts
     "moe-mxfp4": RunConfig("moe-mxfp4", MOE_MXFP4, canvas=256, n_requests=1,
                            prefix_len=(4096, 4096), n_canvases=4, rule="topk", n_steps=12),
+    # 3 with MXFP6 routed experts
+    "moe-mxfp6": RunConfig("moe-mxfp6", MOE_MXFP6, canvas=256, n_requests=1,
+                           prefix_len=(4096, 4096), n_canvases=4, rule="topk", n_steps=12),
     # 5: 32 independent requests, prefixes U[512, 4096], paged KV
     "moe-batch32": RunConfig("moe-batch32", MOE_BF16, canvas=256, n_requests=32,
                              prefix_len=(512, 4096), n_canvases=1, rule="topk",
@@ -184,6 +191,10 @@ RUNS = {
     "moe-mini-mxfp4": RunConfig("moe-mini-mxfp4", MOE_MXFP4_MINI, canvas=64, n_requests=1,
                                 prefix_len=(100, 100), n_canvases=2, rule="topk", n_steps=12),
     "moe-mini-mxfp4-batch": RunConfig("moe-mini-mxfp4-batch", MOE_MXFP4_MINI, canvas=64, n_requests=4,
+                                      prefix_len=(20, 150), n_canvases=1, rule="topk", n_steps=12),
+    "moe-mini-mxfp6": RunConfig("moe-mini-mxfp6", MOE_MXFP6_MINI, canvas=64, n_requests=1,
+                                prefix_len=(100, 100), n_canvases=2, rule="topk", n_steps=12),
+    "moe-mini-mxfp6-batch": RunConfig("moe-mini-mxfp6-batch", MOE_MXFP6_MINI, canvas=64, n_requests=4,
                                       prefix_len=(20, 150), n_canvases=1, rule="topk", n_steps=12),
     "moe-mini-batch": RunConfig("moe-mini-batch", MOE_BF16_MINI, canvas=64, n_requests=4,
                                 prefix_len=(20, 150), n_canvases=1, rule="topk",

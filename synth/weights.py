@@ -84,9 +84,43 @@ def quantize_mxfp4_rows(w: torch.Tensor):
     return packed.contiguous(), (shared + 127).to(torch.uint8).contiguous()
 
 
+E2M3_MAGNITUDES = tuple([m / 8 for m in range(8)] + [1 + m / 8 for m in range(8)] + [2 + m / 4 for m in range(8)]
+                        + [4 + m / 2 for m in range(8)])    # codes 0..31; bit 5 is the sign
+
+
+def quantize_mxfp6_rows(w: torch.Tensor):
+    """MXFP6 with E2M3 elements (OCP Microscaling v1.0) along the last axis, a
+    multiple of 32: each block of 32 shares the E8M0 exponent floor(log2
+    max|w|) - 2 (clamped to [-127, 127]; 0 for an all-zero block) and each
+    element is w / 2^exponent rounded to the nearest E2M3 value, ties to the
+    even mantissa, saturating at +-7.5.
+
+    Returns (codes uint8 [..., K * 3 / 4]: four 6-bit codes per 3 bytes,
+    element 4i + j at bits 6j .. 6j + 5 of the little-endian 24-bit group i;
+    scales uint8 [..., K / 32], the E8M0 codes exponent + 127)."""
+    blocks = w.float().reshape(*w.shape[:-1], w.shape[-1] // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, e = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    shared = torch.where(amax > 0, e - 3, torch.zeros_like(e)).clamp_(-127, 127)
+    x = torch.ldexp(blocks, -shared.unsqueeze(-1).float())
+    a = x.abs().clamp_(max=7.5)
+    step = torch.where(a < 2.0, 0.125, torch.where(a < 4.0, 0.25, 0.5))
+    r = torch.round(a / step) * step                                          # half to even on each grid
+    mags = torch.tensor(E2M3_MAGNITUDES, dtype=r.dtype, device=r.device)
+    codes = torch.bucketize(r, mags).to(torch.int32) | (torch.signbit(x).to(torch.int32) << 5)
+    g = codes.reshape(*w.shape[:-1], w.shape[-1] // 4, 4)
+    bits = g[..., 0] | (g[..., 1] << 6) | (g[..., 2] << 12) | (g[..., 3] << 18)
+    packed = torch.stack([bits & 255, (bits >> 8) & 255, (bits >> 16) & 255], dim=-1).to(torch.uint8)
+    return packed.reshape(*w.shape[:-1], w.shape[-1] * 3 // 4).contiguous(), (shared + 127).to(torch.uint8).contiguous()
+
+
 def _store(out: Dict[str, torch.Tensor], name: str, w: torch.Tensor, dtype: str,
            projection: bool):
-    if dtype == "mxfp4":
+    if dtype == "mxfp6":
+        q, e = quantize_mxfp6_rows(w)
+        out[name + ".q6"] = q
+        out[name + ".e8"] = e
+    elif dtype == "mxfp4":
         q, e = quantize_mxfp4_rows(w)
         out[name + ".q4"] = q
         out[name + ".e8"] = e

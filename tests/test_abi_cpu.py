@@ -69,7 +69,7 @@ def _cfg(**kw):
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=9, d_expert=64), abi.DLM_E_SHAPE),
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=64, top_k=17, d_expert=64), abi.DLM_E_SHAPE),
     (dict(n_layers=0), abi.DLM_E_SHAPE),
-    # MXFP4 experts: only for bf16 MoE models, d_model and d_expert multiples of 128
+    # MX experts: only for bf16 MoE models, d_model and d_expert multiples of 128
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=128, expert_dtype=abi.DLM_MXFP4), abi.DLM_E_DTYPE),
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=64, dtype=abi.DLM_BF16,
           expert_dtype=abi.DLM_MXFP4), abi.DLM_E_SHAPE),
@@ -77,6 +77,10 @@ def _cfg(**kw):
      abi.DLM_E_DTYPE),
     (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=128, dtype=abi.DLM_FP8,
           expert_dtype=abi.DLM_MXFP4), abi.DLM_E_DTYPE),
+    # MXFP6 experts: the same rules
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=128, expert_dtype=abi.DLM_MXFP6), abi.DLM_E_DTYPE),
+    (dict(ffn=abi.DLM_FFN_MOE, n_experts=8, top_k=2, d_expert=192, dtype=abi.DLM_BF16,
+          expert_dtype=abi.DLM_MXFP6), abi.DLM_E_SHAPE),
 ])
 def test_create_rejects_bad_config(kw, status):
     lib = _lib()
@@ -181,24 +185,35 @@ def test_op_router_topk_validates_on_the_host():
     assert lib.dlm_op_router_topk(f, 4, 32, 17, f, f, None) == abi.DLM_E_ARG
 
 
-def test_mxfp4_pack_and_gemm_validate_on_the_host():
-    """Packed MXFP4 sizes are host arithmetic (16-row padding; codes K / 2 and
-    scales K / 32 bytes per row); bad shapes and pointers are refused before
-    any HIP call."""
+def test_mx_pack_and_gemm_validate_on_the_host():
+    """Packed MX sizes are host arithmetic (16-row padding; codes K * bits / 8
+    and scales K / 32 bytes per row, bits 4 for MXFP4 and 6 for MXFP6); bad
+    dtypes, shapes and pointers are refused before any HIP call."""
     lib = _lib()
-    assert lib.dlm_packed_mxfp4_bytes(3, 40, 256, 0) == 3 * 48 * 128
-    assert lib.dlm_packed_mxfp4_bytes(3, 40, 256, 1) == 3 * 48 * 8
-    assert lib.dlm_packed_mxfp4_bytes(1, 16, 192, 0) == 0                   # K not a multiple of 128
-    assert lib.dlm_packed_mxfp4_bytes(0, 16, 128, 0) == 0
-    assert lib.dlm_pack_mxfp4(1, 16, 128, None, None, None, None, None) == abi.DLM_E_ARG
-    assert lib.dlm_pack_mxfp4(1, 16, 192, 0x1000, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_SHAPE
-    assert lib.dlm_pack_mxfp4(1, 16, 128, 0x1008, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_ARG   # misaligned
-    assert lib.dlm_pack_mxfp4(1, 16, 128, 0x1000, 0x2000, 0x1000, 0x20000, None) == abi.DLM_E_ARG   # overlap
+    f4, f6 = abi.DLM_MXFP4, abi.DLM_MXFP6
+    assert lib.dlm_packed_mx_bytes(f4, 3, 40, 256, 0) == 3 * 48 * 128
+    assert lib.dlm_packed_mx_bytes(f6, 3, 40, 256, 0) == 3 * 48 * 192
+    assert lib.dlm_packed_mx_bytes(f4, 3, 40, 256, 1) == 3 * 48 * 8
+    assert lib.dlm_packed_mx_bytes(f6, 3, 40, 256, 1) == 3 * 48 * 8
+    assert lib.dlm_packed_mx_bytes(abi.DLM_BF16, 1, 16, 128, 0) == 0       # not an MX format
+    assert lib.dlm_packed_mx_bytes(f6, 1, 16, 192, 0) == 0                  # K not a multiple of 128
+    assert lib.dlm_packed_mx_bytes(f4, 0, 16, 128, 0) == 0
+    assert lib.dlm_pack_mx(abi.DLM_FP8, 1, 16, 128, 0x1000, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_DTYPE
+    for f in (f4, f6):
+        assert lib.dlm_pack_mx(f, 1, 16, 128, None, None, None, None, None) == abi.DLM_E_ARG
+        assert lib.dlm_pack_mx(f, 1, 16, 192, 0x1000, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_SHAPE
+        assert lib.dlm_pack_mx(f, 1, 16, 128, 0x1008, 0x2000, 0x10000, 0x20000, None) == abi.DLM_E_ARG  # misaligned
+        assert lib.dlm_pack_mx(f, 1, 16, 128, 0x1000, 0x2000, 0x1000, 0x20000, None) == abi.DLM_E_ARG   # overlap
+    # MXFP6 codes of 16 rows x 128 elements are 1536 bytes: an output 1024
+    # bytes past them overlaps, one 2048 bytes past does not
+    assert lib.dlm_pack_mx(f6, 1, 16, 128, 0x10000, 0x2000, 0x10400, 0x20000, None) == abi.DLM_E_ARG
     cnt = (ctypes.c_int32 * 2)(3, 4)
     assert lib.dlm_op_mx_gemm_workspace(0) == 0
-    assert lib.dlm_op_mx_gemm(0, 2, cnt, 16, 128, None, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
+    assert lib.dlm_op_mx_gemm(abi.DLM_BF16, 0, 2, cnt, 16, 128, 0x1000, 0x1000, 0x1000, None, None, 0x1000,
+                              0x1000, 4096, 0, None, None) == abi.DLM_E_DTYPE
+    assert lib.dlm_op_mx_gemm(f4, 0, 2, cnt, 16, 128, None, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
                               None, None) == abi.DLM_E_ARG
-    assert lib.dlm_op_mx_gemm(0, 2, cnt, 16, 96, 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
+    assert lib.dlm_op_mx_gemm(f6, 0, 2, cnt, 16, 96, 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
                               None, None) == abi.DLM_E_SHAPE
-    assert lib.dlm_op_mx_gemm(1, 2, cnt, 16, 128, 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
+    assert lib.dlm_op_mx_gemm(f4, 1, 2, cnt, 16, 128, 0x1000, 0x1000, 0x1000, None, None, 0x1000, 0x1000, 4096, 0,
                               None, None) == abi.DLM_E_ARG                   # SwiGLU without B2 / S2

@@ -61,6 +61,12 @@ def test_fullsize_moe_mxfp4_two_layers():
              caps=BF16_CAPS)
 
 
+def test_fullsize_moe_mxfp6_two_layers():
+    """The same two layers with MXFP6 (E2M3) routed experts."""
+    lockstep(_layers(synth.get_run("moe-mxfp6"), 2), "moe-mxfp6 (full width, 2 layers)", max_steps=2,
+             caps=BF16_CAPS)
+
+
 def test_fullsize_moe_fp8_one_layer():
     lockstep(_layers(synth.get_run("moe-fp8"), 1), "moe-fp8 (full width, 1 layer)", max_steps=2, caps=FP8_CAPS)
 

@@ -15,7 +15,8 @@ from tests.lockstep import lockstep
 pytestmark = pytest.mark.gpu
 
 RUNS = ["tiny", "dense-mini", "dense-mini-ragged", "moe-mini", "dense-mini-fp8", "moe-mini-fp8",
-        "moe-mini-batch", "tiny-t2t", "moe-mini-mxfp4", "moe-mini-mxfp4-batch", "dense-mini-dh64", "dense-mini-dh32"]
+        "moe-mini-batch", "tiny-t2t", "moe-mini-mxfp4", "moe-mini-mxfp4-batch", "moe-mini-mxfp6",
+        "moe-mini-mxfp6-batch", "dense-mini-dh64", "dense-mini-dh32"]
 
 
 @pytest.mark.parametrize("name", RUNS)
