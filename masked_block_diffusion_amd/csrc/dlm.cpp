@@ -4,6 +4,7 @@
 // their sources are documented in include/dlm.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -214,7 +215,8 @@ Plan plan(const dlm_config& c, int rows, int max_kv) {
         p.eis = fp8 ? take(A * 4) : 0;
         p.y = take(A * d * 4);
     }
-    const size_t nt = (c.vocab + lm_head_tile_n(1) - 1) / lm_head_tile_n(1);   // the narrowest vocab tile
+    const int tn = std::min(lm_head_tile_n(1), lm_head_tile_n(1 << 20));         // the narrowest vocab slice
+    const size_t nt = (c.vocab + tn - 1) / tn;
     p.pmax = take(R * nt * 4);
     p.psum = take(R * nt * 4);
     p.pidx = take(R * nt * 4);

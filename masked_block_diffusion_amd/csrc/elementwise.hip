@@ -69,9 +69,14 @@ void embed(const IdSource& ids, int rows, const void* table, int dtype, int d, i
 
 constexpr int RN_T = 256;    // threads per row (4 waves)
 constexpr int MAXC = 4;       // float4 per thread: d <= 4 * RN_T * MAXC
+constexpr int RN_SG = 8;      // routed-expert rows loaded together (top-8 in one round trip)
 
+// MC: float4 chunks per thread (MAXC, or 3 when d <= 3072: fewer registers
+// for the slot rows in flight).
+template <int MC>
 __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, MoeGather moe, const float* g, int rows,
                                                         int d, float eps, float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
+    constexpr int MAXC = MC;
     __shared__ float red[RN_T / WAVE];
     const int lane = threadIdx.x;      // thread of the row (4 waves per row)
     const int r = blockIdx.x;
@@ -118,13 +123,13 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, M
                 if (c < nc) acc[k] = acc[k] * sa * *(const f32x4*)(res.b_scale + 4 * c);
             }
         }
-        // routed experts, slot by slot in selection order; the rows of four
-        // slots are loaded together (one round trip per four slots)
-        for (int s0 = 0; moe.y && s0 < moe.k; s0 += 4) {
-            f32x4 yv[4][MAXC];
-            float ws[4];
+        // routed experts, slot by slot in selection order; the rows of RN_SG
+        // slots are loaded together (one round trip per RN_SG slots)
+        for (int s0 = 0; moe.y && s0 < moe.k; s0 += RN_SG) {
+            f32x4 yv[RN_SG][MAXC];
+            float ws[RN_SG];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < RN_SG; ++j) {
                 if (s0 + j >= moe.k) break;
                 const long a = (long)r * moe.k + s0 + j;
                 ws[j] = moe.w[a];
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, M
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < RN_SG; ++j) {
                 if (s0 + j >= moe.k) break;
 #pragma unroll
                 for (int k = 0; k < MAXC; ++k) {
@@ -213,7 +218,10 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, M
 void rmsnorm(float* x, const Partials& res, const MoeGather& moe, const float* g, int rows, int d, float eps,
              float* hf, uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st) {
     if (rows <= 0) return;
-    launch(rmsnorm_kernel, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+    if (d <= 4 * RN_T * 3)
+        launch(rmsnorm_kernel<3>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+    else
+        launch(rmsnorm_kernel<MAXC>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
 }
 
 int rmsnorm_max_dim() { return 4 * RN_T * MAXC; }

@@ -332,7 +332,11 @@ __device__ __forceinline__ void epilogue(C& c, const EpiArgs& e, int m0, int n0,
     const int rbase = m0 + wm * (C::BM / C::WM) + 4 * (lane / 16);
     const int cbase = n0 + wn * (C::BN / C::WN) + lane % 16;
     if constexpr (EPI == EPI_LMHEAD) {
-        static_assert(C::WN == 1, "LM head epilogue needs whole-tile columns per wave");
+        // one partial per (row, column slice of a wave): slice ntile * WN + wn
+        // of width BN / WN; a slice wholly past N (a ragged last tile) has
+        // none
+        const int slice = ntile * C::WN + wn;
+        const bool sok = slice < e.n_tiles;
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -366,8 +370,8 @@ __device__ __forceinline__ void epilogue(C& c, const EpiArgs& e, int m0, int n0,
                 for (int j = 0; j < C::TN; ++j) s += (vals[j] == -INFINITY) ? 0.f : __expf(vals[j] - mx);
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
-                if (rok && lane % 16 == 0) {
-                    const long k = (long)row * e.n_tiles + ntile;
+                if (rok && sok && lane % 16 == 0) {
+                    const long k = (long)row * e.n_tiles + slice;
                     e.pmax[k] = mx;
                     e.psum[k] = s;
                     e.pidx[k] = ix;
@@ -635,6 +639,7 @@ static long part_floats(const GemmDesc& d) {
     return s == 1 ? 0 : (long)s * d.M * d.N * (DUAL ? 2 : 1);
 }
 
+// bn: the columns one LM-head partial covers (BN / WN of the tile)
 static EpiArgs make_epi(const GemmDesc& d, int bn) {
     EpiArgs e;
     e.C = d.C; e.ldc = d.ldc;
@@ -656,7 +661,7 @@ static int launch_dense(const GemmDesc& d, hipStream_t st) {
     if (a.splits > 1 && (!d.splitk || part_floats<C, T, DUAL, EPI>(d) > d.splitk_floats))
         a.splits = 1;   // no room: unsplit (correct, fewer workgroups)
     a.part = d.splitk;
-    a.e = make_epi(d, C::BN);
+    a.e = make_epi(d, C::BN / C::WN);
     const int grid = ((d.M + C::BM - 1) / C::BM) * ((d.N + C::BN - 1) / C::BN) * a.splits;
     if (grid == 0) return 1;
     launch((gemm_dense_kernel<C, T, EPI>), dim3(grid), dim3(C::THREADS), 0, st, a);
@@ -869,6 +874,8 @@ void pack_weight(int eb, int batch, int N, int K, const void* src, void* dst, hi
            (uint8_t*)dst, N, row_bytes, nkt, per, total);
 }
 
-int lm_head_tile_n(int M) { return M <= 64 ? CoreHs<bf16_t>::BN : CoreHw<bf16_t>::BN; }
+int lm_head_tile_n(int M) {
+    return M <= 64 ? CoreHs<bf16_t>::BN / CoreHs<bf16_t>::WN : CoreHw<bf16_t>::BN / CoreHw<bf16_t>::WN;
+}
 
 }  // namespace dlm
