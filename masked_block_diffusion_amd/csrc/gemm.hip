@@ -552,11 +552,12 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2 x 2 k-groups, 6 stages
 //     (SwiGLU pair: 128 x 64 x 2 weights, 2 k-groups, if N >= 4096, else 64 x 32 x 2)
 //   prefill M                                           128 x 128, waves 2x2 x 2 k-groups, 4 stages (3 SwiGLU);
+//                                                       single weight: 128 x 256 (3 stages) when that gives >= 256 tiles,
 //                                                       128 x 64 for a short-K residual add that 128 x 128 leaves the chip idle
 //   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128 (two k-groups), waves 4x1
 //   grouped (experts)                                   SwiGLU pair 64 x 64 x 2, else 64 x 128; waves 2x2, 3 stages
 //                                                       (fp8: 2 k-groups); >= 256 rows per expert on average:
-//                                                       128 x 128, 2 k-groups (BM = grouped_bm)
+//                                                       SwiGLU pair 128 x 128, else 128 x 256, 2 k-groups (BM = grouped_bm)
 // The canvas choices come from a sweep of every variant and split factor on
 // the workloads' projection shapes: small tiles give enough workgroups to keep
 // weight bytes in flight on every CU; the m-tiles sharing a weight tile are
@@ -567,6 +568,12 @@ template <typename T, bool DUAL> using CoreM = Core<T, 64, 64, 2, 2, DUAL, 4>;
 template <typename T, bool DUAL>
 using CoreW = std::conditional_t<DUAL, Core<T, 128, 64, 2, 2, true, 4>, Core<T, 256, 64, 4, 1, false, 3>>;
 template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>;
+// Wide single-weight tile for compute-bound shapes (prefill-sized M, many
+// rows per expert): each wave's 64 x 128 block reads 12 fragments per 32
+// MFMAs instead of 8 per 16 (a 128 x 128 tile's 64 x 64 blocks); measured on
+// the 32-request MoE step: expert down 20.1 -> 15.7 ms, the shared expert's
+// down 10.1 -> 6.9 ms per step.
+template <typename T> using CoreLW = Core<T, 128, 256, 2, 2, false, 3, 2>;
 template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
 template <typename T> using CoreHw = Core<T, 256, 128, 4, 1, false, 3, 2>;
 // Expert tiles: 64 rows (about what one expert gets from a 256-row canvas at
@@ -579,8 +586,10 @@ using CoreG = std::conditional_t<sizeof(T) == 1,
                                  std::conditional_t<DUAL, Core<T, 64, 64, 2, 2, true, 3, 2>, Core<T, 64, 128, 2, 2, false, 3, 2>>,
                                  std::conditional_t<DUAL, Core<T, 64, 64, 2, 2, true, 3>, Core<T, 64, 128, 2, 2, false, 3>>>;
 // Experts that average 256 rows or more (many requests' canvases, prompts)
-// are compute-bound: 128 x 128 tiles with two k-groups, as for prefill GEMMs.
-template <typename T, bool DUAL> using CoreGL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>;
+// are compute-bound: 128-row tiles with two k-groups, 128 x 128 for the
+// SwiGLU pair (wider pair tiles measured slower: more padding rows' work per
+// ragged expert) and the wide tile for the down projection.
+template <typename T, bool DUAL> using CoreGL = std::conditional_t<DUAL, Core<T, 128, 128, 2, 2, true, 3, 2>, CoreLW<T>>;
 static_assert(CoreG<float, true>::BM == CoreG<float, false>::BM && CoreG<bf16_t, true>::BM == CoreG<bf16_t, false>::BM &&
               CoreG<fp8_t, true>::BM == CoreG<fp8_t, false>::BM && CoreGL<bf16_t, true>::BM == CoreGL<bf16_t, false>::BM,
               "one expert m-tile height per operand type and tile family");
@@ -739,11 +748,18 @@ static void with_core(const GemmDesc& d, F f) {
                 f(Core<T, 64, 64, 2, 2, false, 6, 2>{});
             }
         } else {
-            // prefill-sized M: 128 x 128 tiles with two k-groups; a residual
-            // add whose 128 x 128 tiles would leave CUs idle and whose K is
-            // short (the O projection at a 1024-token prompt: 16.4 us against
-            // 24.5) takes 128 x 64 tiles instead
+            // prefill-sized M: 128 x 128 tiles with two k-groups, or the wide
+            // 128 x 256 tile when that still gives a workgroup per CU; a
+            // residual add whose 128 x 128 tiles would leave CUs idle and
+            // whose K is short (the O projection at a 1024-token prompt: 16.4
+            // us against 24.5) takes 128 x 64 tiles instead
             const long t128 = (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+            if constexpr (!DUAL) {
+                if ((long)((d.M + 127) / 128) * ((d.N + 255) / 256) >= SPLIT_TARGET_WG) {
+                    f(CoreLW<T>{});
+                    return;
+                }
+            }
             if constexpr (!DUAL && EPI == EPI_ADD_F32) {
                 if (t128 < SPLIT_TARGET_WG && d.K < 4L * d.N) {
                     f(Core<T, 128, 64, 2, 2, false, 4, 2>{});

@@ -45,22 +45,23 @@ PROMPT = 256
 
 
 class _MxExperts:
-    """The experts of one MXFP4 tensor (codes and E8M0 scales on the GPU),
-    each decoded by the oracle (OracleWeights) when first used."""
+    """The experts of one MX tensor (MXFP4 `.q4` or MXFP6 `.q6` codes and
+    E8M0 scales on the GPU), each decoded by the oracle (OracleWeights) when
+    first used."""
 
-    def __init__(self, cfg, name, q, e8):
-        self.cfg, self.name, self.q, self.e8, self.cache = cfg, name, q, e8, {}
+    def __init__(self, cfg, name, suffix, q, e8):
+        self.cfg, self.name, self.suffix, self.q, self.e8, self.cache = cfg, name, suffix, q, e8, {}
 
     def __getitem__(self, e):
         if e not in self.cache:
-            one = {self.name + ".q4": self.q[e:e + 1].cpu(), self.name + ".e8": self.e8[e:e + 1].cpu()}
+            one = {self.name + self.suffix: self.q[e:e + 1].cpu(), self.name + ".e8": self.e8[e:e + 1].cpu()}
             self.cache[e] = OracleWeights(self.cfg, one)[self.name][0]
         return self.cache[e]
 
 
 class StreamedWeights:
     """OracleWeights over GPU tensors, one layer at a time: `load(l)` copies
-    layer l's tensors to the host in float64 (MXFP4 experts: decoded one
+    layer l's tensors to the host in float64 (MX experts: decoded one
     expert at a time, when the oracle first uses it), `drop(l)` releases
     them.  The global tensors stay loaded (the embedding as float32, exact for
     its bf16 values)."""
@@ -78,8 +79,8 @@ class StreamedWeights:
         for k, v in self.gpu.items():
             if not k.startswith(f"{l}.") or k.endswith(".e8"):
                 continue
-            if k.endswith(".q4"):
-                self.w[k[:-3]] = _MxExperts(self.cfg, k[:-3], v, self.gpu[k[:-3] + ".e8"])
+            if k.endswith((".q4", ".q6")):
+                self.w[k[:-3]] = _MxExperts(self.cfg, k[:-3], k[-3:], v, self.gpu[k[:-3] + ".e8"])
             else:
                 self.w[k] = self._host(v)
 
@@ -105,7 +106,7 @@ def _conf_pred(lg):
     return 1.0 / np.exp(lg - m[:, None]).sum(axis=-1), np.argmax(lg, axis=-1).astype(np.int32)
 
 
-@pytest.mark.parametrize("name", ["moe", "moe-mxfp4"])
+@pytest.mark.parametrize("name", ["moe", "moe-mxfp4", "moe-mxfp6"])
 def test_moe_full_width_all_layers(name):
     from masked_block_diffusion_amd import DLM
     run = synth.get_run(name)

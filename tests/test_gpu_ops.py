@@ -127,6 +127,29 @@ def test_gemm_variants_match_fp64(variant, splits, M, N, K):
             assert torch.all((got - want).abs() <= tol), f"max excess {((got - want).abs() - tol).max()}"
 
 
+def test_gemm_wide_tile_matches_fp64():
+    """A prefill-sized single-weight GEMM that takes the wide 128 x 256 tile
+    (17 x 16 tiles, ragged in both M and N) against a float64 product of the
+    same bf16 values (fp32 accumulation: K * 2^-24 of sum |a||b|)."""
+    from masked_block_diffusion_amd import abi
+    lib = abi.load_library()
+    M, N, K = 2100, 4000, 256
+    g = torch.Generator().manual_seed(11)
+    A, B = _bf16_tensor((M, K), g), _bf16_tensor((N, K), g)
+    ref = A.double() @ B.double().T
+    bound = (A.double().abs() @ B.double().abs().T) * K * 2.0 ** -24 + 1e-30
+    st = torch.cuda.current_stream().cuda_stream
+    nws = lib.dlm_op_gemm_workspace(abi.DLM_BF16, 0, M, N, K, 0, 0)
+    ws = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    Ad, Bd = A.cuda(), B.cuda()
+    abi.check(lib.dlm_op_gemm(abi.DLM_BF16, 0, M, N, K, Ad.data_ptr(), Bd.data_ptr(), None, None, None, None,
+                              C.data_ptr(), ws.data_ptr(), ws.numel(), 0, 0, None, st), "gemm")
+    torch.cuda.synchronize()
+    got = C.double().cpu()
+    assert torch.all((got - ref).abs() <= bound), f"max excess {((got - ref).abs() - bound).max()}"
+
+
 def test_gemm_f32_matches_fp64():
     from masked_block_diffusion_amd import abi
     lib = abi.load_library()
