@@ -109,13 +109,14 @@ def kernel_model(name: str, cfg, rows: int, keys_per_req, experts_used=None):
     return None
 
 
-def traffic_record(kernel: str, workload: str):
-    """The committed PMC traffic record (profiles/*_traffic.md) of `kernel` on
-    `workload`, if the sources it was measured on are unchanged: the record
-    holds the SHA-256 of those files, recomputed here."""
+def traffic_record(kernel: str, workload: str, root: str = ROOT):
+    """The committed PMC traffic record (profiles/*_traffic.md under `root`)
+    of `kernel` on `workload`, if the sources it was measured on are unchanged:
+    the record holds the SHA-256 of those files, recomputed here (a source
+    that no longer exists makes the record stale)."""
     import glob
     import hashlib
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+    for path in sorted(glob.glob(os.path.join(root, "profiles", "*_traffic.md"))):
         for line in open(path):
             if not line.startswith("traffic-record: "):
                 continue
@@ -124,11 +125,15 @@ def traffic_record(kernel: str, workload: str):
                 continue
             h = hashlib.sha256()
             for f in rec["sources"]:
+                src = os.path.join(root, "masked_block_diffusion_amd", "csrc", f)
+                if not os.path.exists(src):        # a source renamed or removed since: stale
+                    h = None
+                    break
                 h.update(f.encode())
-                with open(os.path.join(ROOT, "masked_block_diffusion_amd", "csrc", f), "rb") as fh:
+                with open(src, "rb") as fh:
                     h.update(fh.read())
-            if h.hexdigest() == rec["sources_sha256"]:
-                rec["file"] = os.path.relpath(path, ROOT)
+            if h is not None and h.hexdigest() == rec["sources_sha256"]:
+                rec["file"] = os.path.relpath(path, root)
                 return rec
     return None
 

@@ -122,17 +122,26 @@ __global__ __launch_bounds__(RB) void route_hist_kernel(const int* ids, int n_as
     }
 }
 
-// One workgroup of 256 threads: thread e owns expert e.
+// One workgroup of 256 threads: thread e owns expert e.  An expert's block
+// counts lie E ints apart; each pass over them issues SCAN_CHUNK loads before
+// using any (a chain of one dependent load per block took 86-92 us for the
+// 128-256 blocks of a 4096-token prompt or a 32-request step).  Pass 1 sums them, then the expert totals and m-tile counts are
+// scanned, pass 2 writes each block's base: the expert's offset plus the
+// counts of the earlier blocks.
+constexpr int SCAN_CHUNK = 32;
+
 __global__ __launch_bounds__(256) void route_scan_kernel(int* hist, int nblocks, int E, int bm, int* offs,
                                                           int* tile_start) {
     __shared__ int tot[MAX_E], tiles[MAX_E];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int b = 0; b < nblocks; ++b) {
-            const int c = hist[(long)b * E + e];
-            hist[(long)b * E + e] = run;       // base of block b within expert e
-            run += c;
+        for (int b0 = 0; b0 < nblocks; b0 += SCAN_CHUNK) {
+            int c[SCAN_CHUNK];
+#pragma unroll
+            for (int i = 0; i < SCAN_CHUNK; ++i) c[i] = b0 + i < nblocks ? hist[(long)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < SCAN_CHUNK; ++i) run += c[i];
         }
     }
     tot[e] = e < E ? run : 0;
@@ -154,7 +163,17 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* hist, int nblocks,
     if (e < E) {
         offs[e] = tot[e];
         tile_start[e] = tiles[e];
-        for (int b = 0; b < nblocks; ++b) hist[(long)b * E + e] += tot[e];
+        int base = tot[e];
+        for (int b0 = 0; b0 < nblocks; b0 += SCAN_CHUNK) {
+            int c[SCAN_CHUNK];
+#pragma unroll
+            for (int i = 0; i < SCAN_CHUNK; ++i) c[i] = b0 + i < nblocks ? hist[(long)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < SCAN_CHUNK; ++i) {
+                if (b0 + i < nblocks) hist[(long)(b0 + i) * E + e] = base;   // base of block b0 + i within the sort
+                base += c[i];
+            }
+        }
     }
 }
 
