@@ -18,6 +18,8 @@
 
 namespace dlm {
 
+constexpr int LM_UNROLL = 8;
+
 __global__ __launch_bounds__(256) void lm_merge_kernel(const float* pmax, const float* psum, const int* pidx,
                                                         int rows, int n_tiles, float* conf, int* pred) {
     const int lane = threadIdx.x % WAVE;
@@ -26,12 +28,22 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const float* pmax, const 
     const float* pm = pmax + (long)r * n_tiles;
     const float* ps = psum + (long)r * n_tiles;
     const int* pi = pidx + (long)r * n_tiles;
+    // a lane takes tiles lane, lane + 64, ...; each pass loads LM_UNROLL of
+    // them before using any (one dependent round trip per tile otherwise)
     float m = -INFINITY;
     int ix = 0x7fffffff;
-    for (int t = lane; t < n_tiles; t += WAVE) {
-        const float v = pm[t];
-        const int i = pi[t];
-        if (v > m || (v == m && i < ix)) { m = v; ix = i; }
+    for (int t0 = lane; t0 < n_tiles; t0 += WAVE * LM_UNROLL) {
+        float v[LM_UNROLL];
+        int id[LM_UNROLL];
+#pragma unroll
+        for (int u = 0; u < LM_UNROLL; ++u) {
+            const int t = t0 + u * WAVE;
+            v[u] = t < n_tiles ? pm[t] : -INFINITY;
+            id[u] = t < n_tiles ? pi[t] : 0x7fffffff;
+        }
+#pragma unroll
+        for (int u = 0; u < LM_UNROLL; ++u)
+            if (v[u] > m || (v[u] == m && id[u] < ix)) { m = v[u]; ix = id[u]; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -40,9 +52,17 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const float* pmax, const 
         if (om > m || (om == m && oi < ix)) { m = om; ix = oi; }
     }
     float z = 0.f;
-    for (int t = lane; t < n_tiles; t += WAVE) {
-        const float v = pm[t];
-        if (v != -INFINITY) z += ps[t] * __expf(v - m);
+    for (int t0 = lane; t0 < n_tiles; t0 += WAVE * LM_UNROLL) {
+        float v[LM_UNROLL], w[LM_UNROLL];
+#pragma unroll
+        for (int u = 0; u < LM_UNROLL; ++u) {
+            const int t = t0 + u * WAVE;
+            v[u] = t < n_tiles ? pm[t] : -INFINITY;
+            w[u] = t < n_tiles ? ps[t] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < LM_UNROLL; ++u)
+            if (v[u] != -INFINITY) z += w[u] * __expf(v[u] - m);
     }
     z = wave_sum(z);
     if (lane == 0) {
