@@ -25,7 +25,12 @@ logit difference relative to max|logit| against the bar of tests/parity.py
 router flips only at near-ties, and every layer's new KV slots (prefill and
 append) within LOGIT_TOL of the largest oracle value of that layer and kind,
 with the cache-writing forwards' routing compared token by token (a token
-re-routed at a near-tie is left out above its flip, tests/lockstep.py)."""
+re-routed at a near-tie is left out above its flip, tests/lockstep.py).
+
+The 32-request batch (the 8192-row step whose GEMMs take the compute-bound
+tile family and the wide tile) runs the same depth check on its first
+denoising step: the GPU prefills all 32 short prompts and steps all 32
+canvases at once; the oracle follows the request with the longest prompt."""
 from dataclasses import replace
 
 import numpy as np
@@ -241,6 +246,105 @@ def test_moe_full_width_all_layers(name):
     for s in subs.values():
         if s is not gm:
             s.close()
+    gm.close()
+
+
+def test_moe_batch32_full_width_all_layers():
+    """The first denoising step of 32 requests (8192 canvas rows; prompts
+    U[64, 256], contiguous caches -- a truncated handle cannot read paged
+    ones, and paging changes no arithmetic) through all 32 layers, one
+    request followed by the oracle at depths 2 / 8 / 16 / 32."""
+    from masked_block_diffusion_amd import DLM
+    run = replace(synth.get_run("moe-batch32"), prefix_len=(64, 256), n_canvases=1)
+    cfg, C, L, n = run.model, run.canvas, run.model.n_layers, run.n_requests
+    prompts = synth.make_inputs(run)
+    r = int(np.argmax([len(p) for p in prompts]))          # the request the oracle follows
+    P = len(prompts[r])
+    print(f"[depth] moe-batch32 full width, {L} layers, {n} requests, prompts 64..256, following request {r} "
+          f"({P} tokens)", flush=True)
+    w = synth.make_weights(cfg, seed=run.seed, device="cuda")
+    gm = DLM(cfg, w, canvas=C)
+    subs = {k: gm.truncated(k) for k in DEPTHS if k < L}
+    subs[L] = gm
+    cap = run.capacity()
+    seqs = [gm.new_seq(cap) for _ in range(n)]
+    rows = n * C
+    ws = gm.workspace(rows, cap)
+    conf = torch.empty(rows, dtype=torch.float32, device="cuda")
+    pred = torch.empty(rows, dtype=torch.int32, device="cuda")
+    logits = torch.empty(rows * cfg.vocab, dtype=torch.float32, device="cuda")
+    rdbg = torch.empty(L * rows * cfg.top_k, dtype=torch.int32, device="cuda")
+    rlog = torch.empty(L * rows * cfg.n_experts, dtype=torch.float32, device="cuda")
+    gm.dlm_debug_router(rdbg, rlog, L * rows)
+    pre_route = None
+    for q in range(n):
+        gm.dlm_prefill(seqs[q], prompts[q].cuda(), ws)
+        if q == r:
+            torch.cuda.synchronize()
+            pre_route = (rdbg[:L * P * cfg.top_k].view(L, P, cfg.top_k).cpu().numpy(),
+                         rlog[:L * P * cfg.n_experts].view(L, P, cfg.n_experts).cpu().numpy().astype(np.float64))
+    for s_ in seqs:
+        s_.canvas.fill_(cfg.mask_id)
+    g = {}
+    for k in sorted(subs):                # the full model last: its routing stays in the debug buffers
+        subs[k].dlm_denoise_step(seqs, conf, pred, ws, logits)
+        torch.cuda.synchronize()
+        g[k] = logits.view(n, C, cfg.vocab)[r].cpu().numpy()
+        progress(f"[depth] batch step through {k} layers")
+    g["rsets"] = rdbg[:L * rows * cfg.top_k].view(L, n, C, cfg.top_k)[:, r].cpu().numpy()
+    g["rlog"] = rlog[:L * rows * cfg.n_experts].view(L, n, C, cfg.n_experts)[:, r].cpu().numpy().astype(np.float64)
+
+    W = StreamedWeights(cfg, w)
+    om = OracleModel(cfg, W)
+    shape = (cfg.n_kv_heads, cap, cfg.head_dim)
+    st = {s: SeqState([np.zeros(shape) for _ in range(L)], [np.zeros(shape) for _ in range(L)], 0)
+          for s in ("exact", "noisy")}
+    xs = {s: W["embed"][prompts[r].numpy().astype(np.int64)].astype(np.float64) for s in st}
+    ys = {s: W["embed"][np.full(C, cfg.mask_id, dtype=np.int64)].astype(np.float64) for s in st}
+    dbg = {s: StepDebug() for s in st}
+    pre_dbg = StepDebug()
+    o = {}
+    for l in range(L):
+        W.load(l)
+        for s in st:
+            ctx = perturbed(om, seed=1 + l) if s == "noisy" else _null()
+            with ctx:
+                st[s].T = 0
+                xs[s] = om.layer(l, xs[s], st[s], True, pre_dbg if s == "exact" else None)
+                st[s].T = P
+                ys[s] = om.layer(l, ys[s], st[s], False, dbg[s])
+        W.drop(l)
+        progress(f"[depth] oracle layer {l + 1} of {L} (exact, noisy)")
+        if l + 1 in DEPTHS:
+            res = {}
+            for s in st:
+                with (perturbed(om, seed=101 + l) if s == "noisy" else _null()):
+                    lg = _logits(om, ys[s], cfg.mask_id)
+                c_, p_ = _conf_pred(lg)
+                res[s] = (c_, p_, StepDebug(lg, list(dbg[s].router_sets), list(dbg[s].router_gap),
+                                            list(dbg[s].router_logits)))
+            o[l + 1] = res
+    bands_of = {k: oracle_bands(cfg.mask_id, np.ones(C, dtype=bool), o[k]["exact"], [o[k]["noisy"]], cfg.dtype)
+                for k in DEPTHS}
+    skip = cache_routing_flips(*pre_route, pre_dbg, bands_of[L], cfg.dtype, "prefill routing")
+    kv_worst = kv_check(seqs[r], st["exact"], 0, P, cfg.dtype, "prefill", skip)
+    worst = {}
+    for k in DEPTHS:
+        ex_, bands = o[k]["exact"], bands_of[k]
+        rep = StepReport()
+        ex_rows = router_exemptions(g["rsets"][:k], g["rlog"][:k], ex_[2], bands, cfg.dtype, rep)
+        compare_logits(g[k], ex_[2].logits, cfg.mask_id, cfg.dtype, rep, ex_rows, bands)
+        progress(f"[depth] batch request {r} depth {k}: max rel logit err {rep.logit_err / rep.logit_scale:.4g} "
+                 f"(oracle's own move {bands.delta_logit_rel:.4g}, bar {logit_bar(cfg.dtype, bands):.3g}), "
+                 f"router-exempt rows {len(ex_rows)}/{C}, decisive router flips {rep.router_flips_decisive}")
+        assert not rep.problems, f"batch depth {k}: {rep.problems}"
+        worst[k] = rep.logit_err / rep.logit_scale
+    assert gm.dlm_check_device_status() == 0
+    progress(f"[depth] moe-batch32: max rel logit err by depth {worst}; KV max|d| / bound {kv_worst:.3g} "
+             f"({len(skip)} cached tokens re-routed at near-ties)")
+    for s_ in subs.values():
+        if s_ is not gm:
+            s_.close()
     gm.close()
 
 
