@@ -30,7 +30,8 @@ from tests.progress import progress
 pytestmark = pytest.mark.gpu
 
 CASES = [("tiny", False), ("tiny", True), ("dense-mini-ragged", True), ("moe-mini", False),
-         ("moe-mini-batch", True), ("dense-mini-fp8", False), ("moe-mini-mxfp4", True), ("dense-full", True)]
+         ("moe-mini-batch", True), ("dense-mini-fp8", False), ("moe-mini-mxfp4", True), ("moe-mini-mxfp6", False),
+         ("dense-full", True)]
 
 
 def _run(name):
