@@ -36,7 +36,8 @@ def _prefill(gm, seqs, prefixes, ws):
         s.canvas.fill_(gm.cfg.mask_id)
 
 
-@pytest.mark.parametrize("name,paged", [("dense-mini", False), ("moe-mini-batch", True), ("tiny", False)])
+@pytest.mark.parametrize("name,paged", [("dense-mini", False), ("moe-mini-batch", True), ("tiny", False),
+                                        ("moe-mini-mxfp4-batch", True), ("moe-mini-mxfp6", False)])
 def test_step_graph_replays_match_direct_calls(name, paged):
     from masked_block_diffusion_amd import CanvasSteps
     run, gm, seqs, prefixes, ws, rule = _setup(name, paged)
