@@ -39,7 +39,7 @@ def _outputs(run, cfg, n):
             torch.full((n * C * cfg.vocab,), -1.0, device="cuda"))
 
 
-@pytest.mark.parametrize("name", ["moe-mini-batch", "dense-mini-ragged", "tiny"])
+@pytest.mark.parametrize("name", ["moe-mini-batch", "dense-mini-ragged", "tiny", "moe-mini-mxfp4-batch"])
 def test_noalloc_matches_workspace_entry_point(name):
     run, cfg, gm, seqs, ws = _setup(name)
     for call, group in enumerate((seqs, seqs[:1])):       # the second call is smaller
