@@ -36,11 +36,12 @@ enum Epi { EPI_F32 = 0, EPI_BF16, EPI_ADD_F32, EPI_SWIGLU_BF16, EPI_SWIGLU_F32, 
 
 constexpr int BKB = 128;             // K bytes per stage row
 
-// KW_ k-groups: 4 * KW_ waves share the tile and the LDS ring; k-group g
+// A k-group is WM x WN = 4 or 8 waves, each owning a (BM / WM) x (BN / WN)
+// block of the tile.  KW_ k-groups share the tile and the LDS ring; k-group g
 // computes k-steps g, g + KW, ... of every stage, and the groups' accumulators
-// are added through LDS before the epilogue.  Two k-groups put two waves on
-// each SIMD, which doubles the LDS fragment bandwidth a SIMD can draw (one
-// wave reads at most ~27 B per clock from LDS).
+// are added through LDS before the epilogue.  Two k-groups (or an 8-wave
+// group) put two waves on each SIMD, which doubles the LDS fragment bandwidth
+// a SIMD can draw (one wave reads at most ~27 B per clock from LDS).
 template <typename T, int BM_, int BN_, int WM_, int WN_, bool DUAL, int NS, int KW_ = 1>
 struct Core {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -53,16 +54,17 @@ struct Core {
     static constexpr int STAGE = ROWS * BKB;
     static constexpr int LDS_BYTES = NS * STAGE;
     static constexpr int KW = KW_;
-    static constexpr int NWAVES = 4 * KW;
+    static constexpr int NPOS = WM * WN;                            // waves per k-group
+    static constexpr int NWAVES = NPOS * KW;
     static constexpr int THREADS = WAVE * NWAVES;
-    static constexpr int LPW = ROWS / 32 / KW;                      // 1-KB loads per wave per stage
+    static constexpr int LPW = ROWS / 8 / NWAVES;                   // 1-KB loads per wave per stage
     static constexpr int KS = BKB / KSB;                            // MFMA k-steps per stage
     static constexpr int KSW = KS / KW;                             // ... per k-group
     static constexpr int PART = TM * TN * 4;
     typedef typename Mfma<T>::frag frag;
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile");
-    static_assert(WM * WN == 4, "4 waves per k-group");
-    static_assert(ROWS % (32 * KW) == 0 && KS % KW == 0, "stage rows / k-steps");
+    static_assert(NPOS == 4 || NPOS == 8, "4 or 8 waves per k-group");
+    static_assert(ROWS % (8 * NWAVES) == 0 && KS % KW == 0, "stage rows / k-steps");
     static_assert((NS - 2) * LPW < 64, "vmcnt");
 
     const uint8_t* src[LPW];     // this lane's source (row + swizzled chunk) per load
@@ -81,8 +83,8 @@ struct Core {
     template <class F>
     __device__ __forceinline__ void init(F rowptr) {
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-        pos = wave % 4;
-        kg = wave / 4;
+        pos = wave % NPOS;
+        kg = wave / NPOS;
         const int lane = threadIdx.x % WAVE;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
@@ -123,8 +125,8 @@ struct Core {
     static constexpr int FRAG_REGS = KSW * (TM + TN * (DUAL ? 2 : 1)) * 4;
     static constexpr int ACC_REGS = TM * TN * 4 * (DUAL ? 2 : 1);
     static constexpr bool DB =
-        2 * FRAG_REGS + (sizeof(T) == 1 ? 2 * FRAG_REGS : 0) + ACC_REGS <= (KW == 1 ? 400 : 190);
-    static_assert(KW == 1 || WAVE * 4 * ACC_REGS * 4 <= LDS_BYTES, "k-group exchange fits the LDS ring");
+        2 * FRAG_REGS + (sizeof(T) == 1 ? 2 * FRAG_REGS : 0) + ACC_REGS <= (NWAVES == 4 ? 400 : 190);
+    static_assert(KW == 1 || WAVE * NPOS * ACC_REGS * 4 <= LDS_BYTES, "k-group exchange fits the LDS ring");
 
     __device__ __forceinline__ void read(Frags& f, const uint8_t* stage) const {
         const int lane = threadIdx.x % WAVE;
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   prefill M                                           128 x 128, waves 2x2 x 2 k-groups, 4 stages (3 SwiGLU);
 //                                                       single weight: 128 x 256 (3 stages) when that gives >= 256 tiles,
 //                                                       128 x 64 for a short-K residual add that 128 x 128 leaves the chip idle
-//   LM head (whole-tile columns per wave)               64 x 64 / 256 x 128 (two k-groups), waves 4x1
+//   LM head (one partial per wave column slice)         64 x 64 (waves 4x1) / 256 x 256 (waves 4x2; fp8: 256 x 128, 4x1 x 2 k-groups)
 //   grouped (experts)                                   SwiGLU pair 64 x 64 x 2, else 64 x 128; waves 2x2, 3 stages
 //                                                       (fp8: 2 k-groups); >= 256 rows per expert on average:
 //                                                       SwiGLU pair 128 x 128, else 128 x 256, 2 k-groups (BM = grouped_bm)
@@ -575,7 +577,14 @@ template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUA
 // down 10.1 -> 6.9 ms per step.
 template <typename T> using CoreLW = Core<T, 128, 256, 2, 2, false, 3, 2>;
 template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
-template <typename T> using CoreHw = Core<T, 256, 128, 4, 1, false, 3, 2>;
+// LM head at canvas M: a 256 x 256 tile of 8 waves (64 x 128 each), two
+// stages -- each activation K-slice in LDS feeds twice the vocabulary of a
+// 256 x 128 tile (measured on the 256 x 262144 x 2560 head: 438-452 us ->
+// 345-349).  fp8 keeps 256 x 128 with two k-groups (its widened fragments
+// would spill at 256 x 256).
+template <typename T>
+using CoreHw = std::conditional_t<sizeof(T) == 1, Core<T, 256, 128, 4, 1, false, 3, 2>,
+                                  Core<T, 256, 256, 4, 2, false, 2, 1>>;
 // Expert tiles: 64 rows (about what one expert gets from a 256-row canvas at
 // top-8 of 128) and 3 stages, from a sweep over routings that touch 32 to 69
 // experts; wider weight tiles for the narrow-K down projection.  fp8 tiles run
