@@ -553,13 +553,16 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   small M (<= 64; the tiny model, short canvases)     32 x 64,  waves 1x4, 4 stages
 //   canvas M (<= 256; one request's canvas)             64 x 64,  waves 2x2 x 2 k-groups, 6 stages
 //     (SwiGLU pair: 128 x 64 x 2 weights, 2 k-groups, if N >= 4096, else 64 x 32 x 2)
-//   prefill M                                           128 x 128, waves 2x2 x 2 k-groups, 4 stages (3 SwiGLU);
-//                                                       single weight: 128 x 256 (3 stages) when that gives >= 256 tiles,
+//   prefill M                                           128 x 128, waves 2x2 x 2 k-groups, 4 stages; SwiGLU pair
+//                                                       256 x 128 x 2, waves 4x2, 2 stages (fp8: 128 x 128 x 2, 2 k-groups);
+//                                                       single weight: 256 x 256, waves 4x2, 2 stages (fp8: 128 x 256)
+//                                                       when 128 x 256 tiles number >= 256,
 //                                                       128 x 64 for a short-K residual add that 128 x 128 leaves the chip idle
 //   LM head (one partial per wave column slice)         64 x 64 (waves 4x1) / 256 x 256 (waves 4x2; fp8: 256 x 128, 4x1 x 2 k-groups)
 //   grouped (experts)                                   SwiGLU pair 64 x 64 x 2, else 64 x 128; waves 2x2, 3 stages
 //                                                       (fp8: 2 k-groups); >= 256 rows per expert on average:
-//                                                       SwiGLU pair 128 x 128, else 128 x 256, 2 k-groups (BM = grouped_bm)
+//                                                       SwiGLU pair 128 x 128 (2 k-groups), else 128 x 256 (waves 2x4)
+//                                                       (BM = grouped_bm)
 // The canvas choices come from a sweep of every variant and split factor on
 // the workloads' projection shapes: small tiles give enough workgroups to keep
 // weight bytes in flight on every CU; the m-tiles sharing a weight tile are
@@ -569,13 +572,24 @@ template <typename T, bool DUAL> using CoreS = Core<T, 32, 64, 1, 4, DUAL, 4>;
 template <typename T, bool DUAL> using CoreM = Core<T, 64, 64, 2, 2, DUAL, 4>;
 template <typename T, bool DUAL>
 using CoreW = std::conditional_t<DUAL, Core<T, 128, 64, 2, 2, true, 4>, Core<T, 256, 64, 4, 1, false, 3>>;
-template <typename T, bool DUAL> using CoreL = Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>;
-// Wide single-weight tile for compute-bound shapes (prefill-sized M, many
-// rows per expert): each wave's 64 x 128 block reads 12 fragments per 32
-// MFMAs instead of 8 per 16 (a 128 x 128 tile's 64 x 64 blocks); measured on
-// the 32-request MoE step: expert down 20.1 -> 15.7 ms, the shared expert's
-// down 10.1 -> 6.9 ms per step.
+// Prefill SwiGLU pair: 256 x 128 x 2 weights over 8 waves of 64 x 64 x 2
+// (one k-group, 2 stages) -- twice the rows per weight tile of 128 x 128;
+// measured on the 32-request MoE step (8192 canvas rows): shared expert's
+// gate/up 7.8 -> 5.9 ms per step.  fp8 keeps 128 x 128 x 2 with two k-groups
+// (its widened fragments spill at 256 rows).
+template <typename T, bool DUAL>
+using CoreL = std::conditional_t<DUAL && sizeof(T) != 1, Core<T, 256, 128, 4, 2, true, 2, 1>,
+                                 Core<T, 128, 128, 2, 2, DUAL, DUAL ? 3 : 4, 2>>;
+// Wide single-weight tile (fp8 prefill-sized M): each wave's 64 x 128 block
+// reads 12 fragments per 32 MFMAs instead of 8 per 16 (a 128 x 128 tile's
+// 64 x 64 blocks).
 template <typename T> using CoreLW = Core<T, 128, 256, 2, 2, false, 3, 2>;
+// Dense prefill single-weight tile: 256 x 256 over 8 waves of 64 x 128, one
+// k-group and 2 stages (twice the rows per weight tile of CoreLW; shared
+// expert's down projection on the 32-request step: 11.6 -> 8.7 ms).  fp8
+// stays on CoreLW: its widened fragments spill at 256 x 256.
+template <typename T>
+using CoreLD = std::conditional_t<sizeof(T) == 1, CoreLW<T>, Core<T, 256, 256, 4, 2, false, 2, 1>>;
 template <typename T> using CoreHs = Core<T, 64, 64, 4, 1, false, 4>;
 // LM head at canvas M: a 256 x 256 tile of 8 waves (64 x 128 each), two
 // stages -- each activation K-slice in LDS feeds twice the vocabulary of a
@@ -595,10 +609,13 @@ using CoreG = std::conditional_t<sizeof(T) == 1,
                                  std::conditional_t<DUAL, Core<T, 64, 64, 2, 2, true, 3, 2>, Core<T, 64, 128, 2, 2, false, 3, 2>>,
                                  std::conditional_t<DUAL, Core<T, 64, 64, 2, 2, true, 3>, Core<T, 64, 128, 2, 2, false, 3>>>;
 // Experts that average 256 rows or more (many requests' canvases, prompts)
-// are compute-bound: 128-row tiles with two k-groups, 128 x 128 for the
+// are compute-bound: 128-row tiles, 128 x 128 with two k-groups for the
 // SwiGLU pair (wider pair tiles measured slower: more padding rows' work per
-// ragged expert) and the wide tile for the down projection.
-template <typename T, bool DUAL> using CoreGL = std::conditional_t<DUAL, Core<T, 128, 128, 2, 2, true, 3, 2>, CoreLW<T>>;
+// ragged expert; so did 8 waves of 64 x 32 x 2) and, for the down
+// projection, 128 x 256 over 8 waves of 64 x 64 with one k-group (expert
+// down on the 32-request step: 15.7 -> 14.0 ms against the 4-wave wide tile).
+template <typename T, bool DUAL>
+using CoreGL = std::conditional_t<DUAL, Core<T, 128, 128, 2, 2, true, 3, 2>, Core<T, 128, 256, 2, 4, false, 3, 1>>;
 static_assert(CoreG<float, true>::BM == CoreG<float, false>::BM && CoreG<bf16_t, true>::BM == CoreG<bf16_t, false>::BM &&
               CoreG<fp8_t, true>::BM == CoreG<fp8_t, false>::BM && CoreGL<bf16_t, true>::BM == CoreGL<bf16_t, false>::BM,
               "one expert m-tile height per operand type and tile family");
@@ -757,15 +774,16 @@ static void with_core(const GemmDesc& d, F f) {
                 f(Core<T, 64, 64, 2, 2, false, 6, 2>{});
             }
         } else {
-            // prefill-sized M: 128 x 128 tiles with two k-groups, or the wide
-            // 128 x 256 tile when that still gives a workgroup per CU; a
+            // prefill-sized M: 128 x 128 tiles with two k-groups (SwiGLU
+            // pair: 256 x 128 x 2), or the 256 x 256 tile when 128 x 256
+            // tiles would still give a workgroup per CU; a
             // residual add whose 128 x 128 tiles would leave CUs idle and
             // whose K is short (the O projection at a 1024-token prompt: 16.4
             // us against 24.5) takes 128 x 64 tiles instead
             const long t128 = (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
             if constexpr (!DUAL) {
                 if ((long)((d.M + 127) / 128) * ((d.N + 255) / 256) >= SPLIT_TARGET_WG) {
-                    f(CoreLW<T>{});
+                    f(CoreLD<T>{});
                     return;
                 }
             }
