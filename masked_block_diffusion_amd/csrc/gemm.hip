@@ -561,7 +561,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_grouped_kernel(GroupedArgs a)
 //   LM head (one partial per wave column slice)         64 x 64 (waves 4x1) / 256 x 256 (waves 4x2; fp8: 256 x 128, 4x1 x 2 k-groups)
 //   grouped (experts)                                   SwiGLU pair 64 x 64 x 2, else 64 x 128; waves 2x2, 3 stages
 //                                                       (fp8: 2 k-groups); >= 256 rows per expert on average:
-//                                                       SwiGLU pair 128 x 128 (2 k-groups), else 128 x 256 (waves 2x4)
+//                                                       SwiGLU pair 128 x 128 (2 k-groups), else 128 x 256 (waves 2x4);
+//                                                       bf16, >= 512 rows per expert: 256 x 128 x 2 / 256 x 256 (waves 4x2)
 //                                                       (BM = grouped_bm)
 // The canvas choices come from a sweep of every variant and split factor on
 // the workloads' projection shapes: small tiles give enough workgroups to keep
@@ -616,13 +617,26 @@ using CoreG = std::conditional_t<sizeof(T) == 1,
 // down on the 32-request step: 15.7 -> 14.0 ms against the 4-wave wide tile).
 template <typename T, bool DUAL>
 using CoreGL = std::conditional_t<DUAL, Core<T, 128, 128, 2, 2, true, 3, 2>, Core<T, 128, 256, 2, 4, false, 3, 1>>;
+// bf16 experts averaging 512 rows or more (the 32-request step: 65536
+// assignments over 128 experts) take 256-row m-tiles over 8 wave positions:
+// 256 x 128 x 2 for the SwiGLU pair, 256 x 256 for the down projection (one
+// k-group, 2 stages) -- twice the rows per weight tile outweighs the longer
+// padding of ragged experts there: expert gate/up 22.0 -> 20.1 ms, down 13.6
+// -> 12.4 ms per step.  At ~256 rows per expert (a 4096-token prompt) the
+// padding would cost more than it saves.
+template <typename T, bool DUAL>
+using CoreGX = std::conditional_t<DUAL, Core<T, 256, 128, 4, 2, true, 2, 1>, Core<T, 256, 256, 4, 2, false, 2, 1>>;
 static_assert(CoreG<float, true>::BM == CoreG<float, false>::BM && CoreG<bf16_t, true>::BM == CoreG<bf16_t, false>::BM &&
-              CoreG<fp8_t, true>::BM == CoreG<fp8_t, false>::BM && CoreGL<bf16_t, true>::BM == CoreGL<bf16_t, false>::BM,
+              CoreG<fp8_t, true>::BM == CoreG<fp8_t, false>::BM && CoreGL<bf16_t, true>::BM == CoreGL<bf16_t, false>::BM &&
+              CoreGL<fp8_t, true>::BM == CoreGL<bf16_t, true>::BM && CoreGL<float, true>::BM == CoreGL<bf16_t, true>::BM &&
+              CoreGX<bf16_t, true>::BM == CoreGX<bf16_t, false>::BM,
               "one expert m-tile height per operand type and tile family");
 
 static bool grouped_large(int n_assign, int E) { return (long)n_assign >= 256L * E; }
+static bool grouped_huge(int dtype, int n_assign, int E) { return dtype == DT_BF16 && (long)n_assign >= 512L * E; }
 
 int grouped_bm(int dtype, int n_assign, int E) {
+    if (grouped_huge(dtype, n_assign, E)) return CoreGX<bf16_t, true>::BM;
     if (grouped_large(n_assign, E)) return CoreGL<bf16_t, true>::BM;
     switch (dtype) {
         case DT_F32: return CoreG<float, true>::BM;
@@ -853,6 +867,12 @@ static void grouped_with(const GemmDesc& d, hipStream_t st) {
 // (grouped_bm with the same assignment count).
 template <typename T>
 static void grouped_t(const GemmDesc& d, hipStream_t st) {
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        if (grouped_huge(d.dtype, d.M, d.E)) {
+            grouped_with<T, CoreGX>(d, st);
+            return;
+        }
+    }
     if (grouped_large(d.M, d.E)) grouped_with<T, CoreGL>(d, st);
     else grouped_with<T, CoreG>(d, st);
 }
