@@ -72,8 +72,9 @@ constexpr int MAXC = 4;       // float4 per thread: d <= 4 * RN_T * MAXC
 constexpr int RN_SG = 8;      // routed-expert rows loaded together (top-8 in one round trip)
 
 // MC: float4 chunks per thread (MAXC, or 3 when d <= 3072: fewer registers
-// for the slot rows in flight).
-template <int MC>
+// for the slot rows in flight).  YB: the routed experts' rows are bf16 (held
+// as raw 8-byte groups until use, half the registers of fp32 rows).
+template <int MC, bool YB>
 __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, MoeGather moe, const float* g, int rows,
                                                         int d, float eps, float* hf, bf16_t* hb, fp8_t* hq, float* hs) {
     constexpr int MAXC = MC;
@@ -126,18 +127,22 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, M
         // routed experts, slot by slot in selection order; the rows of RN_SG
         // slots are loaded together (one round trip per RN_SG slots)
         for (int s0 = 0; moe.y && s0 < moe.k; s0 += RN_SG) {
-            f32x4 yv[RN_SG][MAXC];
+            typedef std::conditional_t<YB, uint2, f32x4> yrow_t;
+            yrow_t yv[RN_SG][MAXC];
             float ws[RN_SG];
 #pragma unroll
             for (int j = 0; j < RN_SG; ++j) {
                 if (s0 + j >= moe.k) break;
                 const long a = (long)r * moe.k + s0 + j;
                 ws[j] = moe.w[a];
-                const float* yr = moe.y + (long)moe.inv[a] * d;
+                const long yo = (long)moe.inv[a] * d;
 #pragma unroll
                 for (int k = 0; k < MAXC; ++k) {
                     const int c = lane + RN_T * k;
-                    if (c < nc) yv[j][k] = *(const f32x4*)(yr + 4 * c);
+                    if (c < nc) {
+                        if constexpr (YB) yv[j][k] = *(const uint2*)((const bf16_t*)moe.y + yo + 4 * c);
+                        else yv[j][k] = *(const f32x4*)((const float*)moe.y + yo + 4 * c);
+                    }
                 }
             }
 #pragma unroll
@@ -146,7 +151,16 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, M
 #pragma unroll
                 for (int k = 0; k < MAXC; ++k) {
                     const int c = lane + RN_T * k;
-                    if (c < nc) acc[k] += ws[j] * yv[j][k];
+                    if (c < nc) {
+                        if constexpr (YB) {
+                            const uint2 u = yv[j][k];
+                            const f32x4 y = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+                            acc[k] += ws[j] * y;
+                        } else {
+                            acc[k] += ws[j] * yv[j][k];
+                        }
+                    }
                 }
             }
         }
@@ -218,10 +232,14 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(float* x, Partials res, M
 void rmsnorm(float* x, const Partials& res, const MoeGather& moe, const float* g, int rows, int d, float eps,
              float* hf, uint16_t* hb, uint8_t* hq, float* hs, hipStream_t st) {
     if (rows <= 0) return;
-    if (d <= 4 * RN_T * 3)
-        launch(rmsnorm_kernel<3>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
-    else
-        launch(rmsnorm_kernel<MAXC>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+    const bool yb = moe.y && moe.y_bf16;
+    if (d <= 4 * RN_T * 3) {
+        if (yb) launch(rmsnorm_kernel<3, true>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+        else launch(rmsnorm_kernel<3, false>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+    } else {
+        if (yb) launch(rmsnorm_kernel<MAXC, true>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+        else launch(rmsnorm_kernel<MAXC, false>, dim3(rows), dim3(RN_T), 0, st, x, res, moe, g, rows, d, eps, hf, hb, hq, hs);
+    }
 }
 
 int rmsnorm_max_dim() { return 4 * RN_T * MAXC; }

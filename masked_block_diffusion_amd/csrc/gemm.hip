@@ -635,6 +635,8 @@ static_assert(CoreG<float, true>::BM == CoreG<float, false>::BM && CoreG<bf16_t,
 static bool grouped_large(int n_assign, int E) { return (long)n_assign >= 256L * E; }
 static bool grouped_huge(int dtype, int n_assign, int E) { return dtype == DT_BF16 && (long)n_assign >= 512L * E; }
 
+bool grouped_compute_bound(int n_assign, int E) { return grouped_large(n_assign, E); }
+
 int grouped_bm(int dtype, int n_assign, int E) {
     if (grouped_huge(dtype, n_assign, E)) return CoreGX<bf16_t, true>::BM;
     if (grouped_large(n_assign, E)) return CoreGL<bf16_t, true>::BM;
@@ -859,6 +861,7 @@ static void grouped_with(const GemmDesc& d, hipStream_t st) {
             else launch_grouped<G<T, true>, T, EPI_SWIGLU_BF16>(d, st);
             break;
         case GEMM_STORE_F32: launch_grouped<G<T, false>, T, EPI_F32>(d, st); break;
+        case GEMM_STORE_BF16: launch_grouped<G<T, false>, T, EPI_BF16>(d, st); break;
         default: break;
     }
 }

@@ -39,6 +39,9 @@ constexpr int MAX_SEQS = 64;
 // n_assign (row, expert) assignments over E experts (the GEMM's M and E); the
 // routing scan computes each expert's first m-tile for this tile height.
 int grouped_bm(int dtype, int n_assign, int E);
+// True when the experts average 256 rows or more (the compute-bound tile
+// family): many requests' canvases, prompts.
+bool grouped_compute_bound(int n_assign, int E);
 
 // C[M, N] (op)= A[M, K] * B[N, K]^T.  Leading dimensions in elements.
 struct GemmDesc {
@@ -169,12 +172,14 @@ struct Partials {
 
 // The routed experts' part of an MoE layer's output, for row r:
 // sum over slots s (in selection order) of w[r * k + s] * y[inv[r * k + s]]
-// (y fp32 [assignments, d] in sorted order).  Unset when y is null.
+// (y [assignments, d] in sorted order: bf16 when y_bf16, else fp32).  Unset
+// when y is null.
 struct MoeGather {
-    const float* y = nullptr;
+    const void* y = nullptr;
     const int* inv = nullptr;
     const float* w = nullptr;
     int k = 0;
+    bool y_bf16 = false;
 };
 
 // x += res + moe (the residual update of a split O / down projection when
