@@ -199,6 +199,10 @@ RUNS = {
     "moe-mini-batch": RunConfig("moe-mini-batch", MOE_BF16_MINI, canvas=64, n_requests=4,
                                 prefix_len=(20, 150), n_canvases=1, rule="topk",
                                 n_steps=12),
+    # a long prompt on the reduced MoE: its prefill routes 8400 assignments over
+    # 16 experts (>= 512 per expert), the compute-bound expert tiles' regime
+    "moe-mini-longprompt": RunConfig("moe-mini-longprompt", MOE_BF16_MINI, canvas=64, n_requests=1,
+                                     prefix_len=(2100, 2100), n_canvases=1, rule="topk", n_steps=12),
     # token editing on the tiny model: the threshold sits inside the spread of its
     # confidences (~1/V), so some earlier tokens are rewritten and some are not
     "tiny-t2t": RunConfig("tiny-t2t", TINY_DENSE_F32, canvas=32, n_requests=1,
