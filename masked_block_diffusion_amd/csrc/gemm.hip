@@ -651,7 +651,8 @@ constexpr int SPLIT_TARGET_WG = 256;
 
 // Split-K factor: enough workgroups for the chip when the output tiles alone
 // are too few; every split keeps at least 4 K-stages; equalised so that no
-// split is empty.  LM-head and prefill-sized GEMMs are never split.
+// split is empty.  LM-head GEMMs are never split; prefill-sized ones only as a
+// residual add with a long K and too few tiles (in two).
 template <class C, typename T, int EPI>
 static int splits_for(const GemmDesc& d) {
     if constexpr (EPI == EPI_LMHEAD) return 1;
