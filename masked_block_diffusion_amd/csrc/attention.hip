@@ -42,6 +42,8 @@
 //     would poison the sum).
 // fp32 kernel (fp32 models): one thread per (query, head), online softmax,
 // fp32 throughout.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "kvcache.h"
@@ -58,6 +60,7 @@ struct AttnArgs {
     int layer, hq, hkv, group;
     int causal;
     int n_qblocks;               // per (request, kv head)
+    uint8_t order[MAX_SEQS];     // requests in dispatch order: longest key range first
     int n_splits;
     int tiles_per_split;
     float scale_log2;            // dh^-1/2 * log2(e)
@@ -66,6 +69,7 @@ struct AttnArgs {
     float* ml_part;              // [n_splits, rows, hq, 2]
     int rows;
 };
+static_assert(MAX_SEQS <= 256, "request indices fit AttnArgs::order");
 
 template <int DH>
 struct AttnShape {
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(AttnShape<DH>::NW * WAVE) void attn_bf16_kernel(Att
     const int split = b % a.n_splits; b /= a.n_splits;
     const int qblk = b % a.n_qblocks; b /= a.n_qblocks;
     const int kvh = b % a.hkv; b /= a.hkv;
-    const int sq = b;
+    const int sq = a.order[b];
     const int tid = threadIdx.x, lane = tid % WAVE;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int g = lane / 16, li = lane % 16;
@@ -479,6 +483,12 @@ static void launch_attn_bf16(AttnArgs& a, int n_seqs, int max_keys, bool causal,
     using S = AttnShape<DH>;
     constexpr int per_cu = (160 * 1024) / (S::NSTAGE * S::STAGE) >= 2 ? 2 : 1;
     a.n_qblocks = (a.seqs.per_seq * a.group + S::QB - 1) / S::QB;
+    // Requests' workgroups are dispatched longest key range first (ties by
+    // index), so the short ones fill the tail: 32 requests with prompts of
+    // 512 to 4096 tokens, attention 16.2 -> 15.2 ms per step.  Each
+    // workgroup's work is unchanged, so are the results.
+    for (int i = 0; i < n_seqs; ++i) a.order[i] = (uint8_t)i;
+    std::stable_sort(a.order, a.order + n_seqs, [&](uint8_t x, uint8_t y) { return a.seqs.T[x] > a.seqs.T[y]; });
     const int ntiles = (max_keys + KT - 1) / KT;
     const int base = n_seqs * a.hkv * a.n_qblocks;
     // causal (prefill) ranges split too: a query block's keys end at its last
